@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE layer forward tokens/s on one MI355X, with roofline fractions.
+
+One step = one moe_layer_forward (route, dispatch/permute, wave-scheduled
+linear1 + SwiGLU + linear2, combine) over one batch of synthetic inputs that
+are already resident in HBM.  The headline workload is the long-tail decode
+batch (T=128, H=4096, I=2048, E=256, top-8); the prefill batch (T=8192) is
+reported alongside.  Weights are random FP4 E2M1 with power-of-two sub-block
+scales and fp32 128x128 block scales (seed 0).
+
+Roofline of the dominant kernel (the expert-FFN kernel), timed with HIP events
+that the library records around it on its own stream in every timed step:
+  decode:  algorithmic bytes = active experts x (FP4 codes + E8M0 sub-block
+           scales + fp32 block scales) = 13,375,488 B each, against 8 TB/s;
+  prefill: algorithmic FLOP = 2*T*k*3*H*I against the dense FP8 peak 5.0 PFLOP/s.
+The CPU baseline is the C oracle (test infrastructure) timed on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "MoE layer tokens/s; %HBM peak at T=128, %FP8 MFMA peak at T=8192"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix
+
+
+def weight_bytes_per_expert(H: int, I: int) -> int:
+    """FP4 codes + E8M0 sub-block scales + fp32 block scales of gate, up and down."""
+    return 3 * (H * I // 2) + 3 * (H * I // 32) + 3 * (H // 128) * (I // 128) * 4
+
+
+def ffn_flops(T: int, k: int, H: int, I: int) -> int:
+    """Two grouped GEMMs: gate and up (2*H*I each) plus down (2*H*I) per token-expert pair."""
+    return 2 * T * k * 3 * H * I
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run_gpu(name, steps, warmup, layer_cache):
+    import torch
+    from fp4_weight_grouped_amd import inputs, v4moe
+
+    inp = inputs.make(name)
+    d = inp.dims
+    dev = "cuda:0"
+    key = (d.H, d.I, d.E, d.topk)
+    if key not in layer_cache:
+        t0 = time.time()
+        dims = v4moe.dims(d.T, d.H, d.I, d.E, d.topk)
+        ex = v4moe.upload_experts(inp.experts, dims, dev)
+        layer_cache[key] = v4moe.MoELayer(d.H, d.I, d.E, d.topk, ex,
+                                          torch.from_numpy(inp.w_router).to(dev), dev)
+        log(f"[bench] uploaded + prepacked weights in {time.time() - t0:.1f}s")
+    layer = layer_cache[key]
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
+    tid = None if inp.token_ids is None else torch.from_numpy(inp.token_ids).to(dev)
+    out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
+
+    for _ in range(warmup):
+        layer.forward(x, bias, inp.mode, tid, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        v4moe.moe_time_next_ffn(*ev[i])
+        _, ids, _, off = layer.forward(x, bias, inp.mode, tid, out=out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    counts = np.diff(off.cpu().numpy())
+    n_active = int((counts > 0).sum())
+    wbytes = n_active * weight_bytes_per_expert(d.H, d.I)
+    flops = ffn_flops(d.T, d.topk, d.H, d.I)
+    r = dict(workload=name, T=d.T, H=d.H, I=d.I, E=d.E, topk=d.topk, ms_per_step=ms_step,
+             tokens_per_s=d.T / (ms_step / 1e3), ffn_ms=ffn_ms, active_experts=n_active,
+             load_max_over_mean=float(counts.max() / counts.mean()), idle_experts=int((counts == 0).sum()),
+             weight_bytes=wbytes, ffn_hbm_gbs=wbytes / (ffn_ms / 1e3) / 1e9,
+             ffn_tflops=flops / (ffn_ms / 1e3) / 1e12)
+    log(f"[bench] {name}: {ms_step:.3f} ms/step, ffn {ffn_ms:.3f} ms, "
+        f"{r['ffn_hbm_gbs']:.0f} GB/s, {r['ffn_tflops']:.0f} TFLOP/s, active {n_active}")
+    return r, inp
+
+
+def cpu_baseline(inp, max_tokens=128):
+    import oracle
+    T = inp.dims.T
+    sub = None if T <= max_tokens else np.arange(max_tokens, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.layer_forward(inp, subset=sub)
+    dt = time.perf_counter() - t0
+    n = T if sub is None else len(sub)
+    return dict(value=n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                seconds=dt,
+                sample=(f"whole layer forward of all {T} tokens of the workload" if sub is None else
+                        f"routing/quantisation/permutation of all {T} tokens, expert FFN + combine "
+                        f"of the first {n} tokens; rate = those tokens / wall time"))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill side report")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cache = {}
+    head, inp = run_gpu(args.workload, args.steps, args.warmup, cache)
+    side = None
+    if not args.no_prefill and args.workload != "prefill":
+        side, _ = run_gpu("prefill", max(5, args.steps // 2), max(2, args.warmup // 2), cache)
+
+    if head["T"] <= 1024:
+        roof = dict(bound="hbm", achieved=head["ffn_hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=head["ffn_hbm_gbs"] / HBM_PEAK_GBS, traffic=None)
+    else:
+        roof = dict(bound="mfma", achieved=head["ffn_tflops"], peak=FP8_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=head["ffn_tflops"] / FP8_DENSE_PEAK_TFLOPS, traffic=None)
+    roof["kernel"] = "k_ffn_persistent (expert FFN, both grouped GEMMs)"
+    roof["kernel_ms"] = head["ffn_ms"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(inp)
+
+    rec = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "T": head["T"], "H": head["H"], "I": head["I"],
+                   "E": head["E"], "topk": head["topk"], "weights": "fp4-e2m1/e8m0-32/fp32-128x128",
+                   "parallelism": "none (one GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": head,
+    }
+    if side is not None:
+        rec["prefill"] = dict(side, roofline=dict(
+            bound="mfma", achieved=side["ffn_tflops"], peak=FP8_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
+            frac=side["ffn_tflops"] / FP8_DENSE_PEAK_TFLOPS, traffic=None))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

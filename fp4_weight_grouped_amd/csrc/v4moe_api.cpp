@@ -1,0 +1,368 @@
+// v4moe_api.cpp -- the C ABI of libv4moe (declared in include/v4moe.h).
+//
+// Host side only: argument checks (plain integer and pointer tests, no
+// runtime queries on the hot path; the host-launcher checks that P1 §2.1 moves
+// out of Python), workspace carving, and kernel launches on the caller's
+// stream.  Nothing here allocates, frees or synchronises, except the offline
+// moe_prepack_weights.
+//
+//   P1 = "DeepSeek-V4揭秘：细粒度专家并行隐藏通信时延，FP4量化与TileLang协同优化百万Token上下文"
+#include "v4moe.h"
+#include "v4moe_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+using namespace v4moe;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    std::once_flag once;
+    int ok = 0;          // 1: gfx950
+    int cus = 0;
+    int persist_per_cu[9] = {0};
+};
+DeviceInfo g_dev[kMaxDevices];
+
+// One-time probe of the current device (architecture and CU count).
+DeviceInfo* device_info()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    DeviceInfo* di = &g_dev[dev];
+    std::call_once(di->once, [di, dev]() {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+        di->ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        di->cus = prop.multiProcessorCount;
+        for (int mt : {1, 2, 4, 8}) di->persist_per_cu[mt] = persistent_blocks_per_cu(mt);
+    });
+    return di->ok ? di : nullptr;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool dims_ok(const v4moe_dims* d)
+{
+    if (!d) return false;
+    if (d->T < 0 || d->T > (1 << 24)) return false;
+    if (d->H < 256 || d->H > 16384 || d->H % 256) return false;
+    if (d->I < 128 || d->I > 16384 || d->I % 128) return false;
+    if (d->E < 1 || d->E > 1024) return false;
+    if (d->topk < 1 || d->topk > 16 || d->topk > d->E) return false;
+    if ((int64_t)d->T * d->topk > (1ll << 24)) return false;
+    return true;
+}
+
+// Workspace carving (offsets in bytes, each 256-aligned).
+struct Layout {
+    size_t xq, xs, sorted_pair, pair_pos, hist, mt_expert, mt_row0, ctrl, done1, queue, hq, hs, y;
+    size_t total;
+    int MT, n_mt_bound, nblk;
+};
+
+Layout layout(const v4moe_dims* d)
+{
+    Layout L{};
+    const size_t T = d->T, H = d->H, I = d->I, E = d->E, P = (size_t)d->T * d->topk;
+    L.MT = choose_mt(d->T, d->topk, d->E);
+    const size_t M = 16 * (size_t)L.MT;
+    L.n_mt_bound = (int)(P / M + (P < E ? P : E) + 1);
+    L.nblk = (int)((P + kPermChunk - 1) / kPermChunk);
+    const size_t NB1 = I / 128, NB2 = H / 256;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
+    L.xq = take(T * H);
+    L.xs = take(T * (H / 128) * 4);
+    L.sorted_pair = take(P * 4);
+    L.pair_pos = take(P * 4);
+    L.hist = take((size_t)(L.nblk > 0 ? L.nblk : 1) * E * 4);
+    L.mt_expert = take((size_t)L.n_mt_bound * 4);
+    L.mt_row0 = take((size_t)L.n_mt_bound * 4);
+    L.ctrl = take(16 * 4);
+    L.done1 = take((size_t)L.n_mt_bound * 4);
+    L.queue = take((size_t)L.n_mt_bound * (NB1 + NB2) * 4);
+    L.hq = take(P * I);
+    L.hs = take(P * (I / 128) * 4);
+    L.y = take(P * H * 2);
+    L.total = o;
+    return L;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool mat_ok(const v4moe_mat& m)
+{
+    return m.fp4 && m.e8m0 && m.blk && aligned16(m.fp4) && aligned16(m.e8m0) && aligned16(m.blk);
+}
+
+FfnArgs ffn_args(const v4moe_dims* d, const Layout& L, uint8_t* ws, const uint8_t* xq, const float* xs,
+                 const int32_t* offsets, const int32_t* sorted_pair, const v4moe_experts* w,
+                 uint16_t* y)
+{
+    FfnArgs a{};
+    a.T = d->T; a.H = d->H; a.I = d->I; a.E = d->E; a.topk = d->topk;
+    a.n_mt_bound = L.n_mt_bound;
+    a.xq = xq; a.xs = xs; a.offsets = offsets; a.sorted_pair = sorted_pair;
+    auto mp = [](const v4moe_mat& m) {
+        return MatPtr{static_cast<const uint8_t*>(m.fp4), static_cast<const uint8_t*>(m.e8m0), m.blk};
+    };
+    a.gate = mp(w->gate); a.up = mp(w->up); a.down = mp(w->down);
+    a.hq = ws + L.hq;
+    a.hs = reinterpret_cast<float*>(ws + L.hs);
+    a.y = y;
+    a.mt_expert = reinterpret_cast<int32_t*>(ws + L.mt_expert);
+    a.mt_row0 = reinterpret_cast<int32_t*>(ws + L.mt_row0);
+    a.ctrl = reinterpret_cast<int32_t*>(ws + L.ctrl);
+    a.done1 = reinterpret_cast<int32_t*>(ws + L.done1);
+    a.queue = reinterpret_cast<uint32_t*>(ws + L.queue);
+    return a;
+}
+
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws, bool persistent,
+            DeviceInfo* di, hipStream_t s)
+{
+    const int NB1 = d->I / 128, NB2 = d->H / 256;
+    hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return V4MOE_ELAUNCH;
+    if (launch_build_tiles(d->E, L.MT, NB1, NB2, persistent ? 1 : 0, a,
+                           reinterpret_cast<int32_t*>(ws + L.mt_expert),
+                           reinterpret_cast<int32_t*>(ws + L.mt_row0),
+                           reinterpret_cast<uint32_t*>(ws + L.queue), s) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    if (persistent) {
+        int per = di->persist_per_cu[L.MT];
+        int grid = di->cus * (per > 0 ? per : 1);
+        const int max_items = L.n_mt_bound * (NB1 + NB2);
+        if (grid > max_items) grid = max_items;
+        if (launch_ffn_persistent(L.MT, a, grid, s) != hipSuccess) return V4MOE_ELAUNCH;
+    } else {
+        if (launch_ffn(1, L.MT, a, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_ffn(2, L.MT, a, s) != hipSuccess) return V4MOE_ELAUNCH;
+    }
+    if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) size_t moe_workspace_bytes(const v4moe_dims* d)
+{
+    if (!dims_ok(d)) return 0;
+    return layout(d).total;
+}
+
+__attribute__((visibility("default"))) void moe_time_next_ffn(void* start_event, void* stop_event)
+{
+    t_ev_start = static_cast<hipEvent_t>(start_event);
+    t_ev_stop = static_cast<hipEvent_t>(stop_event);
+}
+
+__attribute__((visibility("default"))) const char* moe_strerror(int code)
+{
+    switch (code) {
+    case V4MOE_OK: return "ok";
+    case V4MOE_ENULL: return "a required pointer is NULL";
+    case V4MOE_EDIMS: return "unsupported or inconsistent dimensions";
+    case V4MOE_EALIGN: return "a pointer is not 16-byte aligned";
+    case V4MOE_EWORKSPACE: return "workspace too small";
+    case V4MOE_ELAUNCH: return "HIP launch or runtime call failed";
+    case V4MOE_ESCALE: return "sub-block scale outside the lossless window [-8, 6]";
+    case V4MOE_EDEVICE: return "current device is not gfx950";
+    default: return "unknown error";
+    }
+}
+
+__attribute__((visibility("default"))) int moe_route(const v4moe_dims* d, const uint16_t* x,
+                                                     const float* w_router, const float* bias,
+                                                     int32_t mode, const int64_t* token_ids,
+                                                     int32_t* topk_ids, float* topk_w, void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (mode != V4MOE_ROUTE_LEARNED && mode != V4MOE_ROUTE_HASH) return V4MOE_EDIMS;
+    if (d->T == 0) return V4MOE_OK;
+    if (!topk_ids || !topk_w) return V4MOE_ENULL;
+    if (mode == V4MOE_ROUTE_LEARNED && (!x || !w_router)) return V4MOE_ENULL;
+    if (mode == V4MOE_ROUTE_LEARNED && (!aligned16(x) || !aligned16(w_router))) return V4MOE_EALIGN;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w,
+                     as_stream(stream)) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+__attribute__((visibility("default"))) int moe_permute(const v4moe_dims* d, const uint16_t* x,
+                                                       const int32_t* topk_ids, int32_t* expert_offsets,
+                                                       int32_t* sorted_pair, int32_t* pair_pos,
+                                                       uint8_t* xq, float* xs, void* workspace,
+                                                       size_t ws_bytes, void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (!expert_offsets) return V4MOE_ENULL;
+    if (d->T == 0) {
+        // an empty batch: only the offsets (E+1 zeros) are written
+        if (!device_info()) return V4MOE_EDEVICE;
+        return launch_fill_i32(expert_offsets, 0, d->E + 1, as_stream(stream)) == hipSuccess ? V4MOE_OK
+                                                                                           : V4MOE_ELAUNCH;
+    }
+    if (!x || !topk_ids || !sorted_pair || !pair_pos || !xq || !xs || !workspace) return V4MOE_ENULL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(workspace)) return V4MOE_EALIGN;
+    const Layout L = layout(d);
+    if (ws_bytes < L.total) return V4MOE_EWORKSPACE;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    hipStream_t s = as_stream(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (launch_quant_x(d->T, d->H, x, xq, xs, s) != hipSuccess) return V4MOE_ELAUNCH;
+    if (launch_permute(d->T, d->topk, d->E, topk_ids, expert_offsets, sorted_pair, pair_pos,
+                       reinterpret_cast<int32_t*>(ws + L.hist), s) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+__attribute__((visibility("default"))) int moe_expert_ffn(const v4moe_dims* d, const uint8_t* xq,
+                                                          const float* xs, const int32_t* expert_offsets,
+                                                          const int32_t* sorted_pair, const v4moe_experts* w,
+                                                          uint16_t* y, void* workspace, size_t ws_bytes,
+                                                          void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (d->T == 0) return V4MOE_OK;
+    if (!xq || !xs || !expert_offsets || !sorted_pair || !w || !y || !workspace) return V4MOE_ENULL;
+    if (!mat_ok(w->gate) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
+    if (!aligned16(xq) || !aligned16(y) || !aligned16(workspace)) return V4MOE_EALIGN;
+    const Layout L = layout(d);
+    if (ws_bytes < L.total) return V4MOE_EWORKSPACE;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const FfnArgs a = ffn_args(d, L, ws, xq, xs, expert_offsets, sorted_pair, w, y);
+    return run_ffn(d, L, a, ws, false, di, as_stream(stream));
+}
+
+__attribute__((visibility("default"))) int moe_combine(const v4moe_dims* d, const uint16_t* y,
+                                                       const float* topk_w, uint16_t* out, void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (d->T == 0) return V4MOE_OK;
+    if (!y || !topk_w || !out) return V4MOE_ENULL;
+    if (!aligned16(y) || !aligned16(out)) return V4MOE_EALIGN;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    if (launch_combine(d->T, d->H, d->topk, y, topk_w, out, as_stream(stream)) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+__attribute__((visibility("default"))) int moe_layer_forward(
+    const v4moe_dims* d, const uint16_t* x, const float* w_router, const float* bias, int32_t mode,
+    const int64_t* token_ids, const v4moe_experts* w, int32_t* topk_ids, float* topk_w,
+    int32_t* expert_offsets, uint16_t* out, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (mode != V4MOE_ROUTE_LEARNED && mode != V4MOE_ROUTE_HASH) return V4MOE_EDIMS;
+    if (!expert_offsets) return V4MOE_ENULL;
+    if (d->T == 0) {
+        // an empty batch: only the offsets (E+1 zeros) are written
+        if (!device_info()) return V4MOE_EDEVICE;
+        return launch_fill_i32(expert_offsets, 0, d->E + 1, as_stream(stream)) == hipSuccess ? V4MOE_OK
+                                                                                           : V4MOE_ELAUNCH;
+    }
+    if (!x || !w || !topk_ids || !topk_w || !out || !workspace) return V4MOE_ENULL;
+    if (mode == V4MOE_ROUTE_LEARNED && !w_router) return V4MOE_ENULL;
+    if (!mat_ok(w->gate) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return V4MOE_EALIGN;
+    if (mode == V4MOE_ROUTE_LEARNED && !aligned16(w_router)) return V4MOE_EALIGN;
+    const Layout L = layout(d);
+    if (ws_bytes < L.total) return V4MOE_EWORKSPACE;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    hipStream_t s = as_stream(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* xq = ws + L.xq;
+    float* xs = reinterpret_cast<float*>(ws + L.xs);
+    int32_t* sp = reinterpret_cast<int32_t*>(ws + L.sorted_pair);
+    int32_t* pp = reinterpret_cast<int32_t*>(ws + L.pair_pos);
+    uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+    if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w, s) !=
+        hipSuccess)
+        return V4MOE_ELAUNCH;
+    if (launch_quant_x(d->T, d->H, x, xq, xs, s) != hipSuccess) return V4MOE_ELAUNCH;
+    if (launch_permute(d->T, d->topk, d->E, topk_ids, expert_offsets, sp, pp,
+                       reinterpret_cast<int32_t*>(ws + L.hist), s) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    const FfnArgs a = ffn_args(d, L, ws, xq, xs, expert_offsets, sp, w, y);
+    int rc = run_ffn(d, L, a, ws, true, di, s);
+    if (rc) return rc;
+    if (launch_combine(d->T, d->H, d->topk, y, topk_w, out, s) != hipSuccess) return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+__attribute__((visibility("default"))) int moe_prepack_weights(const v4moe_dims* d,
+                                                               const v4moe_experts* canonical,
+                                                               const v4moe_experts* packed,
+                                                               void* workspace, size_t ws_bytes,
+                                                               void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (!canonical || !packed || !workspace) return V4MOE_ENULL;
+    if (!mat_ok(canonical->gate) || !mat_ok(canonical->up) || !mat_ok(canonical->down) ||
+        !mat_ok(packed->gate) || !mat_ok(packed->up) || !mat_ok(packed->down))
+        return V4MOE_ENULL;
+    if (!aligned16(workspace)) return V4MOE_EALIGN;
+    if (ws_bytes < 256) return V4MOE_EWORKSPACE;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    hipStream_t s = as_stream(stream);
+    int32_t* bad = static_cast<int32_t*>(workspace);
+    if (launch_fill_i32(bad, 0, 1, s) != hipSuccess) return V4MOE_ELAUNCH;
+    const v4moe_mat* in[3] = {&canonical->gate, &canonical->up, &canonical->down};
+    const v4moe_mat* out[3] = {&packed->gate, &packed->up, &packed->down};
+    const int N[3] = {d->I, d->I, d->H}, K[3] = {d->H, d->H, d->I};
+    for (int i = 0; i < 3; i++) {
+        if (launch_prepack(d->E, N[i], K[i], static_cast<const uint8_t*>(in[i]->fp4),
+                           static_cast<const uint8_t*>(in[i]->e8m0),
+                           static_cast<uint8_t*>(const_cast<void*>(out[i]->fp4)),
+                           static_cast<uint8_t*>(const_cast<void*>(out[i]->e8m0)), bad, s) != hipSuccess)
+            return V4MOE_ELAUNCH;
+        if (out[i]->blk != in[i]->blk &&
+            hipMemcpyAsync(const_cast<float*>(out[i]->blk), in[i]->blk,
+                           (size_t)d->E * (N[i] / 128) * (K[i] / 128) * 4, hipMemcpyDeviceToDevice,
+                           s) != hipSuccess)
+            return V4MOE_ELAUNCH;
+    }
+    int32_t flag = 0;
+    if (hipMemcpyAsync(&flag, bad, 4, hipMemcpyDeviceToHost, s) != hipSuccess) return V4MOE_ELAUNCH;
+    if (hipStreamSynchronize(s) != hipSuccess) return V4MOE_ELAUNCH;
+    return flag ? V4MOE_ESCALE : V4MOE_OK;
+}
+
+__attribute__((visibility("default"))) int moe_dequant_fp8(const v4moe_mat* m, int32_t N, int32_t K,
+                                                           int32_t expert, uint8_t* out, void* stream)
+{
+    if (!m || !out) return V4MOE_ENULL;
+    if (!mat_ok(*m)) return V4MOE_ENULL;
+    if (N < 16 || N % 16 || K < 128 || K % 128 || expert < 0) return V4MOE_EDIMS;
+    if (!aligned16(out)) return V4MOE_EALIGN;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    if (launch_dequant_export(N, K, expert, static_cast<const uint8_t*>(m->fp4),
+                              static_cast<const uint8_t*>(m->e8m0), out, as_stream(stream)) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// v4moe_internal.h -- launchers shared by the kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace v4moe {
+
+// Pairs handled by one block of the permutation passes.
+constexpr int kPermChunk = 256;
+// Experts per scheduling wave of the persistent kernel (P1 §1.2: experts are
+// split into waves of a few experts each).
+constexpr int kWaveExperts = 8;
+
+struct MatPtr {
+    const uint8_t* fp4;   // packed [E][N/16][K/128][64][16]
+    const uint8_t* e8m0;  // packed [E][N/16][K/128][64]
+    const float* blk;     // [E][N/128][K/128]
+};
+
+// Everything an expert-FFN tile needs.
+struct FfnArgs {
+    int T, H, I, E, topk;
+    int n_mt_bound;            // capacity of the m-tile list
+    const uint8_t* xq;         // [T][H]   E4M3
+    const float* xs;           // [T][H/128]
+    const int32_t* offsets;    // [E+1]
+    const int32_t* sorted_pair;// [T*topk]
+    MatPtr gate, up, down;
+    uint8_t* hq;               // [T*topk][I] E4M3, rows in expert-sorted order
+    float* hs;                 // [T*topk][I/128]
+    uint16_t* y;               // [T*topk][H] bf16, row = pair id
+    const int32_t* mt_expert;  // [n_mt_bound] expert of each m-tile
+    const int32_t* mt_row0;    // [n_mt_bound] first sorted row of each m-tile
+    int32_t* ctrl;             // [0] number of m-tiles, [1] queue head, [2] queue length
+    int32_t* done1;            // [n_mt_bound] finished linear1 tiles per m-tile
+    const uint32_t* queue;     // persistent schedule
+};
+
+hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
+                        const float* bias, int mode, const int64_t* token_ids,
+                        int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_quant_x(int T, int H, const uint16_t* x, uint8_t* xq, float* xs, hipStream_t s);
+hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, int32_t* hist, hipStream_t s);
+hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue,
+                              const FfnArgs& a, int32_t* mt_expert, int32_t* mt_row0,
+                              uint32_t* queue, hipStream_t s);
+hipError_t launch_ffn(int phase, int MT, const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_persistent(int MT, const FfnArgs& a, int grid, hipStream_t s);
+int persistent_blocks_per_cu(int MT);
+hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* w, uint16_t* out,
+                          hipStream_t s);
+hipError_t launch_prepack(int E, int N, int K, const uint8_t* fp4_in, const uint8_t* e8_in,
+                          uint8_t* fp4_out, uint8_t* e8_out, int32_t* bad, hipStream_t s);
+hipError_t launch_dequant_export(int N, int K, int expert, const uint8_t* fp4, const uint8_t* e8,
+                                 uint8_t* out, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
+
+// Rows per m-tile (16 * MT) used for given dimensions.
+int choose_mt(int T, int k, int E);
+
+}  // namespace v4moe

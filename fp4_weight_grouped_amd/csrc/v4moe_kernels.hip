@@ -1,0 +1,955 @@
+// v4moe_kernels.hip -- HIP kernels of the MoE layer forward for gfx950.
+//
+// Sources (cited by short tag and section):
+//   P1 = "DeepSeek-V4揭秘：细粒度专家并行隐藏通信时延，FP4量化与TileLang协同优化百万Token上下文"
+//   P2 = "DeepSeek V4架构学习笔记"
+//
+// Kernels, in the order a layer forward runs them:
+//   k_route_learned / k_route_hash   routing (P2, DeepSeekMoE notes)
+//   k_quant_x                        FP8 dispatch payload (P1 §1.4)
+//   k_perm_pass<count> + k_perm_scan expert histogram, offsets, stable positions
+//   k_build_tiles                    m-tile list and the wave-ordered work queue
+//   k_ffn<1,MT>, k_ffn<2,MT>         linear1+SwiGLU+requant, linear2+scatter (unfused)
+//   k_ffn_persistent<MT>             the same tiles, wave-scheduled in one launch
+//   k_combine                        fixed-order weighted un-permute
+// plus the offline k_prepack and the test export k_dequant_export.
+//
+// Every tile of linear1/linear2 runs the same per-element arithmetic whatever
+// the tile height MT or the schedule: one 16x16x128 FP8 MFMA per 128-wide K
+// chunk, then acc = fma(xs*blk, P, acc) with chunks in increasing order.  A
+// row's result therefore does not depend on which rows share its tile (P1
+// §3.1, batch invariance; no split-K) and never on timing (P1 §3.2: no atomic
+// accumulation anywhere).
+#include "v4moe_device.h"
+#include "v4moe_internal.h"
+
+#include <limits.h>
+
+namespace v4moe {
+
+// ---------------------------------------------------------------------------
+// Routing
+// ---------------------------------------------------------------------------
+
+// Logits for TW tokens per block, every expert: thread = expert (E > 256 loops),
+// each thread runs TW independent fp32 fma chains over h ascending.  The x
+// values are block-uniform (scalar loads); W_r rows are read coalesced along e.
+// Then one wave per token selects the top k (logit descending, lower id on
+// ties), and lanes 0..k-1 compute sqrt(softplus(z)) and the normalised weights.
+template <int TW>
+__global__ __launch_bounds__(256) void k_route_learned(int T, int H, int E, int k,
+                                                       const uint16_t* __restrict__ x,
+                                                       const float* __restrict__ wr,
+                                                       const float* __restrict__ bias,
+                                                       int32_t* __restrict__ ids,
+                                                       float* __restrict__ wts)
+{
+    extern __shared__ float zs[];  // [TW][E]
+    const int t0 = blockIdx.x * TW;
+    const int tid = threadIdx.x;
+
+    for (int e0 = 0; e0 < E; e0 += 256) {
+        const int e = e0 + tid;
+        const bool ok = e < E;
+        const float* w = wr + (ok ? e : 0);
+        const uint32_t* xr[TW];
+#pragma unroll
+        for (int i = 0; i < TW; i++) {
+            int tok = min(t0 + i, T - 1);
+            xr[i] = reinterpret_cast<const uint32_t*>(x + (size_t)tok * H);
+        }
+        float acc[TW];
+#pragma unroll
+        for (int i = 0; i < TW; i++) acc[i] = 0.0f;
+        for (int h = 0; h < H; h += 8) {
+            float wv[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) wv[u] = w[(size_t)(h + u) * E];
+#pragma unroll
+            for (int i = 0; i < TW; i++) {
+                uint4 xx = *reinterpret_cast<const uint4*>(xr[i] + h / 2);
+                uint32_t q[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    acc[i] = __builtin_fmaf(bf16_to_f32(q[u] & 0xFFFFu), wv[2 * u], acc[i]);
+                    acc[i] = __builtin_fmaf(bf16_to_f32(q[u] >> 16), wv[2 * u + 1], acc[i]);
+                }
+            }
+        }
+        if (ok) {
+#pragma unroll
+            for (int i = 0; i < TW; i++) {
+                float z = acc[i];
+                if (bias) z = z + bias[e];
+                zs[i * E + e] = z;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    for (int i = wv; i < TW; i += 4) {
+        const int t = t0 + i;
+        if (t >= T) break;
+        const float* z = zs + i * E;
+        uint32_t taken = 0;  // bit q: expert lane + 64q already picked
+        float my_z = 0.0f;
+        int my_e = 0;
+        for (int j = 0; j < k; j++) {
+            float bv = 0.0f;
+            int be = INT_MAX;
+            for (int q = 0; q * 64 < E; q++) {
+                int e = lane + 64 * q;
+                if (e < E && !((taken >> q) & 1u)) {
+                    float v = z[e];
+                    if (be == INT_MAX || v > bv) { bv = v; be = e; }
+                }
+            }
+            for (int off = 32; off >= 1; off >>= 1) {
+                float ov = __shfl_xor(bv, off);
+                int oe = __shfl_xor(be, off);
+                bool better = oe != INT_MAX &&
+                              (be == INT_MAX || ov > bv || (ov == bv && oe < be));
+                if (better) { bv = ov; be = oe; }
+            }
+            if ((be & 63) == lane) taken |= 1u << (be >> 6);
+            if (lane == j) { my_z = bv; my_e = be; }
+        }
+        // affinity sqrt(softplus(z)), softplus(z) = max(z,0) + log1p(exp(-|z|))
+        float a = sqrtf(fmaxf(my_z, 0.0f) + log1pf(expf(-fabsf(my_z))));
+        float sum = 0.0f;
+        for (int j = 0; j < k; j++) sum += __shfl(a, j);
+        if (lane < k) {
+            ids[(size_t)t * k + lane] = my_e;
+            wts[(size_t)t * k + lane] = sum > 0.0f ? a / sum : 1.0f / (float)k;
+        }
+    }
+}
+
+// Hash routing: expert_j = splitmix64(id*k + j) mod E, +1 mod E past repeats.
+__global__ __launch_bounds__(256) void k_route_hash(int T, int E, int k,
+                                                    const int64_t* __restrict__ tids,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ wts)
+{
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    const uint64_t id = tids ? (uint64_t)tids[t] : (uint64_t)t;
+    int32_t* o = ids + (size_t)t * k;
+    for (int j = 0; j < k; j++) {
+        int c = (int)(splitmix64(id * (uint64_t)k + (uint64_t)j) % (uint64_t)E);
+        for (;;) {
+            bool dup = false;
+            for (int i = 0; i < j; i++) dup |= (o[i] == c);
+            if (!dup) break;
+            c = (c + 1 == E) ? 0 : c + 1;
+        }
+        o[j] = c;
+        wts[(size_t)t * k + j] = 1.0f / (float)k;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 dispatch payload: x -> (xq, xs) per token and 128-channel group.
+// 16 consecutive threads own one group (8 channels each, one 16-byte load).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quant_x(int T, int H, const uint16_t* __restrict__ x,
+                                                 uint8_t* __restrict__ xq, float* __restrict__ xs)
+{
+    const size_t total = (size_t)T * H / 8;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const bool ok = idx < total;
+    float f[8];
+    float amax = 0.0f;
+    if (ok) {
+        uint4 v = *reinterpret_cast<const uint4*>(x + idx * 8);
+        uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            f[2 * u] = bf16_to_f32(q[u] & 0xFFFFu);
+            f[2 * u + 1] = bf16_to_f32(q[u] >> 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++) amax = fmaxf(amax, fabsf(f[u]));
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (!ok) return;
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        lo |= e4m3_rne_sat(f[u] / s) << (8 * u);
+        hi |= e4m3_rne_sat(f[u + 4] / s) << (8 * u);
+    }
+    *reinterpret_cast<uint2*>(xq + idx * 8) = make_uint2(lo, hi);
+    if ((idx & 15) == 0) xs[idx / 16] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Expert-sorted permutation (stable counting sort of pair ids by expert).
+// Each 64-thread block owns kPermChunk consecutive pairs.  Within a wave the
+// lanes holding the same expert find each other with one ballot per id bit;
+// a lane's rank among them is a popcount of the lower lanes, so positions
+// follow pair order exactly.  Pass <true> writes per-block counts; the scan
+// turns them into per-block bases; pass <false> writes the positions.
+// ---------------------------------------------------------------------------
+template <bool kCount>
+__global__ __launch_bounds__(64) void k_perm_pass(int P, int E, const int32_t* __restrict__ ids,
+                                                  int32_t* __restrict__ hist,
+                                                  int32_t* __restrict__ sorted_pair,
+                                                  int32_t* __restrict__ pair_pos)
+{
+    extern __shared__ int32_t cnt[];  // [E]
+    const int lane = threadIdx.x;
+    const int b = blockIdx.x;
+    int32_t* row = hist + (size_t)b * E;
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+    __syncthreads();
+    const int p0 = b * kPermChunk;
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int it = 0; it < kPermChunk; it += 64) {
+        const int p = p0 + it + lane;
+        const bool valid = p < P;
+        const int e = valid ? ids[p] : 0;
+        const uint32_t key = valid ? (uint32_t)e : 0x7FFu;
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int bit = 0; bit < 11; bit++) {
+            const bool bb = (key >> bit) & 1u;
+            const uint64_t m = __ballot(bb);
+            peers &= bb ? m : ~m;
+        }
+        const int rank = __popcll(peers & lower);
+        const int tot = __popcll(peers);
+        const int base = valid ? cnt[e] : 0;
+        if (!kCount && valid) {
+            const int pos = row[e] + base + rank;
+            sorted_pair[pos] = p;
+            pair_pos[p] = pos;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (valid && rank == tot - 1) cnt[e] = base + tot;
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (kCount) {
+        __syncthreads();
+        for (int e = lane; e < E; e += 64) row[e] = cnt[e];
+    }
+}
+
+// One block: expert totals, exclusive scan -> offsets[E+1], and per-block bases
+// (offsets[e] + counts of earlier blocks) written back over the counts.
+__global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __restrict__ hist,
+                                                    int32_t* __restrict__ offsets)
+{
+    __shared__ int32_t tot[1024];
+    const int e = threadIdx.x;
+    int s = 0;
+    if (e < E)
+        for (int b = 0; b < nblk; b++) s += hist[(size_t)b * E + e];
+    tot[e] = s;
+    __syncthreads();
+    if (e == 0) {
+        int run = 0;
+        for (int i = 0; i < E; i++) {
+            int c = tot[i];
+            tot[i] = run;
+            run += c;
+        }
+        offsets[E] = run;
+    }
+    __syncthreads();
+    if (e < E) {
+        int run = tot[e];
+        offsets[e] = run;
+        for (int b = 0; b < nblk; b++) {
+            int c = hist[(size_t)b * E + e];
+            hist[(size_t)b * E + e] = run;
+            run += c;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// m-tile list and persistent work queue.
+// m-tile = up to M = 16*MT consecutive sorted rows of one expert.  The queue
+// is ordered by scheduling waves of kWaveExperts experts (P1 §1.2, Fig. 5):
+// linear1 of wave 0, linear1 of wave 1, linear2 of wave 0, linear1 of wave 2,
+// linear2 of wave 1, ..., linear2 of the last wave.  Entry = phase<<31 |
+// mtile<<8 | n-block.  Also clears the counters used by the persistent kernel.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int NB2, int build_queue,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ mt_expert,
+                                                      int32_t* __restrict__ mt_row0,
+                                                      int32_t* __restrict__ ctrl,
+                                                      int32_t* __restrict__ done1,
+                                                      uint32_t* __restrict__ queue)
+{
+    __shared__ int32_t base[1025];
+    __shared__ int32_t segpos[2 * 129];
+    const int tid = threadIdx.x;
+    int n = 0;
+    if (tid < E) n = (offsets[tid + 1] - offsets[tid] + M - 1) / M;
+    base[tid] = n;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < E; i++) {
+            int c = base[i];
+            base[i] = run;
+            run += c;
+        }
+        base[E] = run;
+    }
+    __syncthreads();
+    const int total = base[E];
+    if (tid < E) {
+        for (int m = 0; m < n; m++) {
+            mt_expert[base[tid] + m] = tid;
+            mt_row0[base[tid] + m] = offsets[tid] + m * M;
+        }
+    }
+    for (int i = tid; i < total; i += 1024) done1[i] = 0;
+    if (tid == 0) {
+        ctrl[0] = total;
+        ctrl[1] = 0;
+        ctrl[2] = build_queue ? total * (NB1 + NB2) : 0;
+    }
+    if (!build_queue) return;
+    const int W = (E + kWaveExperts - 1) / kWaveExperts;
+    if (tid == 0) {
+        // segment order: F1(0), [F1(w), F2(w-1)] for w = 1..W-1, F2(W-1)
+        int pos = 0;
+        for (int s = 0; s <= W; s++) {
+            if (s < W) {
+                int a = base[min(E, (s + 1) * kWaveExperts)] - base[s * kWaveExperts];
+                segpos[2 * s] = pos;
+                pos += a * NB1;
+            }
+            if (s >= 1) {
+                int w = s - 1;
+                int a = base[min(E, (w + 1) * kWaveExperts)] - base[w * kWaveExperts];
+                segpos[2 * w + 1] = pos;
+                pos += a * NB2;
+            }
+        }
+    }
+    __syncthreads();
+    for (int w = 0; w < W; w++) {
+        const int lo = base[w * kWaveExperts];
+        const int a = base[min(E, (w + 1) * kWaveExperts)] - lo;
+        for (int ph = 0; ph < 2; ph++) {
+            const int NB = ph ? NB2 : NB1;
+            const int pos = segpos[2 * w + ph];
+            for (int i = tid; i < a * NB; i += 1024) {
+                const int mt = lo + i / NB;
+                const int nb = i % NB;
+                queue[pos + i] = ((uint32_t)ph << 31) | ((uint32_t)mt << 8) | (uint32_t)nb;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Expert FFN tiles.
+//
+// Tile (phase 1) = one m-tile of M rows x 128 columns of h (128 gate + 128 up
+// output columns), K = H.  Tile (phase 2) = M rows x 256 output columns, K = I.
+// 4 waves; wave w owns 4 16-column n-tiles (phase 1: gate and up columns
+// 32w..32w+31 of the block, so SwiGLU pairs sit in the same lane; phase 2:
+// columns 64w..64w+63) and all M rows.
+//
+// Per 128-wide K chunk:
+//   A (activation E4M3 rows, gathered through sorted_pair in phase 1, the
+//     contiguous sorted rows of hq in phase 2) is staged in LDS, double
+//     buffered, row stride 144 B so that the 16 rows of an MFMA operand read
+//     spread over all banks; its per-row scales ride along.
+//   B (weights) goes HBM -> registers with one 16-byte load per lane per
+//     n-tile (the packed layout makes a wave's load one contiguous 1 KiB),
+//     kPrefetch chunks ahead; it is dequantised FP4 -> E4M3 in registers
+//     with the per-block LDS table and fed to the matrix cores directly.
+//     No wave shares a B fragment with another, so B never visits LDS.
+//   Each 16x16 output tile: P = MFMA over the chunk, acc = fma(xs*blk, P, acc).
+// ---------------------------------------------------------------------------
+constexpr int kPrefetch = 2;
+constexpr int kAStride = 144;
+constexpr int kLutBytes = 256 * 8;
+
+template <int PHASE, int MT>
+struct TileLayout {
+    static constexpr int M = 16 * MT;
+    static constexpr int A_BYTES = 2 * M * kAStride;
+    static constexpr int STAGE = PHASE == 1 ? M * 128 : 16 * 256 * 2;
+    static constexpr int A_REGION = ((A_BYTES > STAGE ? A_BYTES : STAGE) + 15) / 16 * 16;
+    static constexpr int XS_OFF = A_REGION;           // [2][M] float
+    static constexpr int RED_OFF = XS_OFF + 2 * M * 4; // [4][M] float
+    static constexpr int ROW_OFF = RED_OFF + 4 * M * 4; // [M] int
+    static constexpr int BYTES = ROW_OFF + M * 4;
+};
+
+template <int PHASE, int MT>
+__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8_t* smem,
+                                         const uint2* lut)
+{
+    using TL = TileLayout<PHASE, MT>;
+    constexpr int M = TL::M;
+    constexpr int ASEG = (M * 8 + 255) / 256;  // A 16-byte segments per thread per chunk
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int e = a.mt_expert[mt];
+    const int row0 = a.mt_row0[mt];
+    const int rows = min(M, a.offsets[e + 1] - row0);
+    const int K = PHASE == 1 ? a.H : a.I;
+    const int N = PHASE == 1 ? a.I : a.H;
+    const int C = K / 128;
+
+    float* xsb = reinterpret_cast<float*>(smem + TL::XS_OFF);
+    float* red = reinterpret_cast<float*>(smem + TL::RED_OFF);
+    int32_t* rowinfo = reinterpret_cast<int32_t*>(smem + TL::ROW_OFF);
+
+    // phase 1: token of each row (for the gather); phase 2: pair id (for the scatter)
+    for (int r = tid; r < M; r += 256) {
+        int v = -1;
+        if (r < rows) {
+            int p = a.sorted_pair[row0 + r];
+            v = PHASE == 1 ? p / a.topk : p;
+        }
+        rowinfo[r] = v;
+    }
+    __syncthreads();
+
+    // A staging: thread owns segments s = tid + 256*j (row s/8, 16-byte column s%8).
+    const uint8_t* asrc[ASEG];
+    const float* xsrc[ASEG];
+#pragma unroll
+    for (int j = 0; j < ASEG; j++) {
+        const int s = tid + 256 * j;
+        const int r = s >> 3;
+        asrc[j] = nullptr;
+        xsrc[j] = nullptr;
+        if (s < M * 8 && r < rows) {
+            if (PHASE == 1) {
+                const int t = rowinfo[r];
+                asrc[j] = a.xq + (size_t)t * a.H + (s & 7) * 16;
+                xsrc[j] = a.xs + (size_t)t * (a.H / 128);
+            } else {
+                const size_t R = (size_t)(row0 + r);
+                asrc[j] = a.hq + R * a.I + (s & 7) * 16;
+                xsrc[j] = a.hs + R * (a.I / 128);
+            }
+        }
+    }
+
+    // B sources: 4 n-tiles of this wave, pointing at chunk 0 of lane's slot.
+    const uint8_t* bsrc[4];
+    const uint8_t* ssrc[4];
+    const float* blk0;
+    const float* blk1;
+    {
+        const int NT16 = N / 16;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const MatPtr& m = PHASE == 1 ? (j < 2 ? a.gate : a.up) : a.down;
+            const int tile = PHASE == 1 ? nb * 8 + 2 * w + (j & 1) : nb * 16 + 4 * w + j;
+            const size_t rec = ((size_t)e * NT16 + tile) * C;
+            bsrc[j] = m.fp4 + rec * 1024 + lane * 16;
+            ssrc[j] = m.e8m0 + rec * 64 + lane;
+        }
+        if (PHASE == 1) {
+            blk0 = a.gate.blk + ((size_t)e * (a.I / 128) + nb) * C;
+            blk1 = a.up.blk + ((size_t)e * (a.I / 128) + nb) * C;
+        } else {
+            blk0 = a.down.blk + ((size_t)e * (a.H / 128) + nb * 2 + (w >> 1)) * C;
+            blk1 = blk0;
+        }
+    }
+
+    v4f acc[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    uint4 bq[kPrefetch][4];
+    uint32_t bs[kPrefetch][4];
+#pragma unroll
+    for (int u = 0; u < kPrefetch; u++)
+        if (u < C)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                bq[u][j] = *reinterpret_cast<const uint4*>(bsrc[j] + (size_t)u * 1024);
+                bs[u][j] = ssrc[j][(size_t)u * 64];
+            }
+
+    uint4 areg[ASEG];
+    float xreg[ASEG];
+    auto load_a = [&](int c) {
+#pragma unroll
+        for (int j = 0; j < ASEG; j++) {
+            if (asrc[j]) {
+                areg[j] = *reinterpret_cast<const uint4*>(asrc[j] + (size_t)c * 128);
+                xreg[j] = xsrc[j][c];
+            } else {
+                areg[j] = make_uint4(0, 0, 0, 0);
+                xreg[j] = 0.0f;
+            }
+        }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < ASEG; j++) {
+            const int s = tid + 256 * j;
+            if (s < M * 8) {
+                const int r = s >> 3;
+                *reinterpret_cast<uint4*>(smem + buf * M * kAStride + r * kAStride + (s & 7) * 16) = areg[j];
+                if ((s & 7) == 0) xsb[buf * M + r] = xreg[j];
+            }
+        }
+    };
+
+    load_a(0);
+    store_a(0);
+    __syncthreads();
+
+    for (int c0 = 0; c0 < C; c0 += kPrefetch) {
+#pragma unroll
+        for (int u = 0; u < kPrefetch; u++) {
+            const int c = c0 + u;
+            if (c < C) {
+                const int buf = c & 1;
+                if (c + 1 < C) load_a(c + 1);
+                v8i bf[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) bf[j] = dequant_slot(bq[u][j], lut[bs[u][j] & 0xFFu]);
+                if (c + kPrefetch < C) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        bq[u][j] = *reinterpret_cast<const uint4*>(bsrc[j] + (size_t)(c + kPrefetch) * 1024);
+                        bs[u][j] = ssrc[j][(size_t)(c + kPrefetch) * 64];
+                    }
+                }
+                const float sb0 = blk0[c];
+                const float sb1 = blk1[c];
+                const uint8_t* Ab = smem + buf * M * kAStride;
+                const float* Xb = xsb + buf * M;
+#pragma unroll
+                for (int i = 0; i < MT; i++) {
+                    if (i * 16 < rows) {
+                        const uint8_t* ap = Ab + (i * 16 + (lane & 15)) * kAStride + (lane >> 4) * 32;
+                        const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
+                        const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
+                        v8i af;
+                        af[0] = (int)a0.x; af[1] = (int)a0.y; af[2] = (int)a0.z; af[3] = (int)a0.w;
+                        af[4] = (int)a1.x; af[5] = (int)a1.y; af[6] = (int)a1.z; af[7] = (int)a1.w;
+                        const float4 x4 = *reinterpret_cast<const float4*>(Xb + i * 16 + (lane >> 4) * 4);
+                        const float s0[4] = {x4.x * sb0, x4.y * sb0, x4.z * sb0, x4.w * sb0};
+                        const float s1[4] = {x4.x * sb1, x4.y * sb1, x4.z * sb1, x4.w * sb1};
+#pragma unroll
+                        for (int j = 0; j < 4; j++) {
+                            const v4f P = mfma_chunk(af, bf[j]);
+                            const float* sc = (PHASE == 1 && j >= 2) ? s1 : s0;
+#pragma unroll
+                            for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(sc[q], P[q], acc[i][j][q]);
+                        }
+                    }
+                }
+                if (c + 1 < C) store_a((c + 1) & 1);
+                __syncthreads();
+            }
+        }
+    }
+
+    if (PHASE == 1) {
+        // h = SiLU(g) * u, then E4M3 per (row, 128 columns of h): the amax of a
+        // row is reduced over the 16 lanes of a row group, then over the 4 waves.
+        uint8_t* stage = smem;  // [M][128]
+        float hv[MT][2][4];
+#pragma unroll
+        for (int i = 0; i < MT; i++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                float mx = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const float g = acc[i][j][q];
+                    const float u = acc[i][2 + j][q];
+                    const float h = (g / (1.0f + expf(-g))) * u;
+                    hv[i][j][q] = h;
+                    mx = fmaxf(mx, fabsf(h));
+                }
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+                if ((lane & 15) == 0) red[w * M + i * 16 + (lane >> 4) * 4 + q] = mx;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < MT; i++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int r = i * 16 + (lane >> 4) * 4 + q;
+                const float amax = fmaxf(fmaxf(red[r], red[M + r]), fmaxf(red[2 * M + r], red[3 * M + r]));
+                const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    stage[r * 128 + 32 * w + 16 * j + (lane & 15)] = (uint8_t)e4m3_rne_sat(hv[i][j][q] / s);
+                if (w == 0 && (lane & 15) == 0 && r < rows)
+                    a.hs[(size_t)(row0 + r) * (a.I / 128) + nb] = s;
+            }
+        __syncthreads();
+        for (int s = tid; s < M * 8; s += 256) {
+            const int r = s >> 3;
+            if (r < rows)
+                *reinterpret_cast<uint4*>(a.hq + (size_t)(row0 + r) * a.I + nb * 128 + (s & 7) * 16) =
+                    *reinterpret_cast<const uint4*>(stage + r * 128 + (s & 7) * 16);
+        }
+        __syncthreads();
+    } else {
+        // bf16 rows scattered back to their pair slot p = t*topk + j.
+        uint16_t* stage = reinterpret_cast<uint16_t*>(smem);  // [16][256]
+#pragma unroll
+        for (int i = 0; i < MT; i++) {
+            if (i * 16 < rows) {
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        stage[((lane >> 4) * 4 + q) * 256 + 64 * w + 16 * j + (lane & 15)] =
+                            (uint16_t)f32_to_bf16(acc[i][j][q]);
+                __syncthreads();
+                for (int s = tid; s < 16 * 32; s += 256) {
+                    const int r = i * 16 + (s >> 5);
+                    if (r < rows) {
+                        const int p = rowinfo[r];
+                        *reinterpret_cast<uint4*>(a.y + (size_t)p * a.H + nb * 256 + (s & 31) * 8) =
+                            *reinterpret_cast<const uint4*>(stage + (s >> 5) * 256 + (s & 31) * 8);
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+}
+
+template <int PHASE, int MT>
+__global__ __launch_bounds__(256) void k_ffn(FfnArgs a, int NB)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int mt = blockIdx.x / NB;
+    const int nb = blockIdx.x % NB;
+    if (mt >= a.ctrl[0]) return;
+    uint2* lut = reinterpret_cast<uint2*>(smem);
+    lut[threadIdx.x] = dequant_lut_entry(threadIdx.x);
+    __syncthreads();
+    ffn_tile<PHASE, MT>(a, mt, nb, smem + kLutBytes, lut);
+}
+
+// Persistent, wave-scheduled: blocks take queue entries in order.  A linear2
+// tile waits until all linear1 tiles of its m-tile are done; those entries sit
+// earlier in the queue, were taken by running blocks and never wait, so every
+// wait ends.  Counters only signal readiness; no data is accumulated through
+// them, so the numerics are those of the unfused kernels.
+template <int MT>
+__global__ __launch_bounds__(256) void k_ffn_persistent(FfnArgs a)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ uint32_t item;
+    uint2* lut = reinterpret_cast<uint2*>(smem);
+    lut[threadIdx.x] = dequant_lut_entry(threadIdx.x);
+    const int NB1 = a.I / 128;
+    const int total = a.ctrl[2];
+    for (;;) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int q = atomicAdd(&a.ctrl[1], 1);
+            item = q < total ? a.queue[q] : 0xFFFFFFFFu;
+        }
+        __syncthreads();
+        const uint32_t it = item;
+        if (it == 0xFFFFFFFFu) break;
+        const int mt = (int)((it >> 8) & 0x7FFFFFu);
+        const int nb = (int)(it & 0xFFu);
+        if ((it >> 31) == 0) {
+            ffn_tile<1, MT>(a, mt, nb, smem + kLutBytes, lut);
+            __threadfence();
+            __syncthreads();
+            if (threadIdx.x == 0) atomicAdd(&a.done1[mt], 1);
+        } else {
+            if (threadIdx.x == 0)
+                while (__hip_atomic_load(&a.done1[mt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < NB1)
+                    __builtin_amdgcn_s_sleep(2);
+            __syncthreads();
+            (void)__hip_atomic_load(&a.done1[mt], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+            ffn_tile<2, MT>(a, mt, nb, smem + kLutBytes, lut);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: out[t] = bf16(sum_j w[t][j] * y[t*k+j]) in fp32, j ascending.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const uint16_t* __restrict__ y,
+                                                 const float* __restrict__ w, uint16_t* __restrict__ out)
+{
+    const size_t total = (size_t)T * H / 8;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const size_t t = idx / (H / 8);
+    const size_t c = idx % (H / 8);
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < k; j++) {
+        const float wj = w[t * k + j];
+        const uint4 v = *reinterpret_cast<const uint4*>(y + (t * k + j) * H + c * 8);
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            acc[2 * u] = __builtin_fmaf(wj, bf16_to_f32(q[u] & 0xFFFFu), acc[2 * u]);
+            acc[2 * u + 1] = __builtin_fmaf(wj, bf16_to_f32(q[u] >> 16), acc[2 * u + 1]);
+        }
+    }
+    uint4 o;
+    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+    o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+    o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + t * H + c * 8) = o;
+}
+
+// ---------------------------------------------------------------------------
+// Offline prepack (canonical -> packed) and the dequant test export.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_prepack(int E, int N, int K, const uint8_t* __restrict__ fin,
+                                                 const uint8_t* __restrict__ ein,
+                                                 uint8_t* __restrict__ fout, uint8_t* __restrict__ eout,
+                                                 int32_t* __restrict__ bad)
+{
+    const int C = K / 128;
+    const size_t total = (size_t)E * (N / 16) * C * 64;
+    const size_t slot = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (slot >= total) return;
+    const int lane = (int)(slot & 63);
+    const size_t rec = slot >> 6;
+    const int c = (int)(rec % C);
+    const int tile = (int)((rec / C) % (N / 16));
+    const size_t e = rec / C / (N / 16);
+    const int n = tile * 16 + (lane & 15);
+    const int k0 = c * 128 + (lane >> 4) * 32;
+    const uint4 v = *reinterpret_cast<const uint4*>(fin + (e * N + n) * (size_t)(K / 2) + k0 / 2);
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t code[32];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const uint32_t byte = (in[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        code[2 * i] = byte & 15u;
+        code[2 * i + 1] = byte >> 4;
+    }
+    uint32_t outw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int el = 8 * (j >> 2) + (j & 3);
+        outw[j >> 2] |= (code[el] | (code[el + 4] << 4)) << (8 * (j & 3));
+    }
+    *reinterpret_cast<uint4*>(fout + slot * 16) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    const uint8_t s = ein[(e * N + n) * (size_t)(K / 32) + k0 / 32];
+    eout[slot] = s;
+    if (s < 127 - 8 || s > 127 + 6) atomicOr(bad, 1);
+}
+
+__global__ __launch_bounds__(256) void k_dequant_export(int N, int K, int expert,
+                                                        const uint8_t* __restrict__ fp4,
+                                                        const uint8_t* __restrict__ e8,
+                                                        uint8_t* __restrict__ out)
+{
+    __shared__ uint2 lut[256];
+    lut[threadIdx.x] = dequant_lut_entry(threadIdx.x);
+    __syncthreads();
+    const int C = K / 128;
+    const size_t total = (size_t)(N / 16) * C * 64;
+    const size_t slot = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (slot >= total) return;
+    const int lane = (int)(slot & 63);
+    const size_t rec = slot >> 6;
+    const int c = (int)(rec % C);
+    const int tile = (int)(rec / C);
+    const size_t g = (size_t)expert * (N / 16) * C * 64 + slot;
+    const v8i o = dequant_slot(*reinterpret_cast<const uint4*>(fp4 + g * 16), lut[e8[g]]);
+    const int n = tile * 16 + (lane & 15);
+    const int k0 = c * 128 + (lane >> 4) * 32;
+    uint4* dst = reinterpret_cast<uint4*>(out + (size_t)n * K + k0);
+    dst[0] = make_uint4((uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]);
+    dst[1] = make_uint4((uint32_t)o[4], (uint32_t)o[5], (uint32_t)o[6], (uint32_t)o[7]);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static inline unsigned blocks_for(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
+                        const float* bias, int mode, const int64_t* token_ids,
+                        int32_t* ids, float* w, hipStream_t s)
+{
+    if (mode == 1) {
+        hipLaunchKernelGGL(k_route_hash, dim3(blocks_for(T, 256)), dim3(256), 0, s, T, E, k,
+                           token_ids, ids, w);
+    } else if (T <= 1024) {
+        hipLaunchKernelGGL(k_route_learned<1>, dim3(T), dim3(256), (size_t)E * 4, s, T, H, E, k,
+                           x, wr, bias, ids, w);
+    } else if (T <= 4096) {
+        hipLaunchKernelGGL(k_route_learned<4>, dim3(blocks_for(T, 4)), dim3(256), (size_t)4 * E * 4, s,
+                           T, H, E, k, x, wr, bias, ids, w);
+    } else {
+        hipLaunchKernelGGL(k_route_learned<16>, dim3(blocks_for(T, 16)), dim3(256), (size_t)16 * E * 4,
+                           s, T, H, E, k, x, wr, bias, ids, w);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_x(int T, int H, const uint16_t* x, uint8_t* xq, float* xs, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_quant_x, dim3(blocks_for((size_t)T * H / 8, 256)), dim3(256), 0, s, T, H, x,
+                       xq, xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, int32_t* hist, hipStream_t s)
+{
+    const int P = T * k;
+    const int nblk = (P + kPermChunk - 1) / kPermChunk;
+    hipLaunchKernelGGL(k_perm_pass<true>, dim3(nblk), dim3(64), (size_t)E * 4, s, P, E, ids, hist,
+                       sorted_pair, pair_pos);
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, E, nblk, hist, offsets);
+    hipLaunchKernelGGL(k_perm_pass<false>, dim3(nblk), dim3(64), (size_t)E * 4, s, P, E, ids, hist,
+                       sorted_pair, pair_pos);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue, const FfnArgs& a,
+                              int32_t* mt_expert, int32_t* mt_row0, uint32_t* queue, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, E, 16 * MT, NB1, NB2, build_queue,
+                       a.offsets, mt_expert, mt_row0, a.ctrl, a.done1, queue);
+    return hipGetLastError();
+}
+
+template <int PHASE, int MT>
+static hipError_t launch_ffn_t(const FfnArgs& a, hipStream_t s)
+{
+    const int NB = PHASE == 1 ? a.I / 128 : a.H / 256;
+    const size_t lds = kLutBytes + TileLayout<PHASE, MT>::BYTES;
+    hipLaunchKernelGGL((k_ffn<PHASE, MT>), dim3((unsigned)a.n_mt_bound * NB), dim3(256), lds, s, a, NB);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn(int phase, int MT, const FfnArgs& a, hipStream_t s)
+{
+    switch (MT * 2 + (phase - 1)) {
+    case 2: return launch_ffn_t<1, 1>(a, s);
+    case 3: return launch_ffn_t<2, 1>(a, s);
+    case 4: return launch_ffn_t<1, 2>(a, s);
+    case 5: return launch_ffn_t<2, 2>(a, s);
+    case 8: return launch_ffn_t<1, 4>(a, s);
+    case 9: return launch_ffn_t<2, 4>(a, s);
+    case 16: return launch_ffn_t<1, 8>(a, s);
+    case 17: return launch_ffn_t<2, 8>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int MT>
+static size_t persistent_lds()
+{
+    const size_t b1 = TileLayout<1, MT>::BYTES, b2 = TileLayout<2, MT>::BYTES;
+    return kLutBytes + (b1 > b2 ? b1 : b2);
+}
+
+template <int MT>
+static int persistent_occupancy()
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_ffn_persistent<MT>, 256, persistent_lds<MT>()) !=
+        hipSuccess)
+        n = 1;
+    return n < 1 ? 1 : n;
+}
+
+int persistent_blocks_per_cu(int MT)
+{
+    switch (MT) {
+    case 1: return persistent_occupancy<1>();
+    case 2: return persistent_occupancy<2>();
+    case 4: return persistent_occupancy<4>();
+    default: return persistent_occupancy<8>();
+    }
+}
+
+template <int MT>
+static hipError_t launch_persistent_t(const FfnArgs& a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_ffn_persistent<MT>, dim3(grid), dim3(256), persistent_lds<MT>(), s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_persistent(int MT, const FfnArgs& a, int grid, hipStream_t s)
+{
+    switch (MT) {
+    case 1: return launch_persistent_t<1>(a, grid, s);
+    case 2: return launch_persistent_t<2>(a, grid, s);
+    case 4: return launch_persistent_t<4>(a, grid, s);
+    case 8: return launch_persistent_t<8>(a, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* w, uint16_t* out,
+                          hipStream_t s)
+{
+    hipLaunchKernelGGL(k_combine, dim3(blocks_for((size_t)T * H / 8, 256)), dim3(256), 0, s, T, H, k, y,
+                       w, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_prepack(int E, int N, int K, const uint8_t* fp4_in, const uint8_t* e8_in,
+                          uint8_t* fp4_out, uint8_t* e8_out, int32_t* bad, hipStream_t s)
+{
+    const size_t total = (size_t)E * (N / 16) * (K / 128) * 64;
+    hipLaunchKernelGGL(k_prepack, dim3(blocks_for(total, 256)), dim3(256), 0, s, E, N, K, fp4_in, e8_in,
+                       fp4_out, e8_out, bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_export(int N, int K, int expert, const uint8_t* fp4, const uint8_t* e8,
+                                 uint8_t* out, hipStream_t s)
+{
+    const size_t total = (size_t)(N / 16) * (K / 128) * 64;
+    hipLaunchKernelGGL(k_dequant_export, dim3(blocks_for(total, 256)), dim3(256), 0, s, N, K, expert, fp4,
+                       e8, out);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ p, int32_t v, size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(n, 256)), dim3(256), 0, s, p, v, n);
+    return hipGetLastError();
+}
+
+int choose_mt(int T, int k, int E)
+{
+    const double avg = (double)T * k / (E > 0 ? E : 1);
+    if (avg <= 16.0) return 1;
+    if (avg <= 40.0) return 2;
+    if (avg <= 96.0) return 4;
+    return 8;
+}
+
+}  // namespace v4moe

@@ -26,14 +26,16 @@ gate and up have N=I, K=H; down has N=H, K=I.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import functools
+import os
 from typing import Optional
 
 import numpy as np
 
-# One random stream per tensor, keyed by a fixed tag, so that every tensor of a
-# workload is reproducible on its own.
+# One random stream per tensor (per expert for the weights), keyed by a fixed
+# tag, so that every tensor of a workload is reproducible on its own.
 _TAG = {
     "x": 1, "w_router": 2,
     "gate": 3, "up": 4, "down": 5,
@@ -107,11 +109,23 @@ class Experts:
 
 def gen_matrix(seed: int, tag: str, E: int, N: int, K: int,
                b_range=(-4, 0), blk_range=(0.01, 0.05)) -> Matrix:
-    r = _rng(seed, tag)
-    fp4 = np.frombuffer(r.bytes(E * N * K // 2), dtype=np.uint8).reshape(E, N, K // 2)
-    b = r.integers(b_range[0], b_range[1] + 1, size=(E, N, K // 32), dtype=np.int16)
-    e8m0 = (b + 127).astype(np.uint8)
-    blk = r.uniform(blk_range[0], blk_range[1], size=(E, N // 128, K // 128)).astype(np.float32)
+    """One random stream per (matrix, expert); experts are drawn in parallel
+    threads, which does not change the values."""
+    fp4 = np.empty((E, N, K // 2), np.uint8)
+    e8m0 = np.empty((E, N, K // 32), np.uint8)
+    blk = np.empty((E, N // 128, K // 128), np.float32)
+
+    def one(e):
+        r = np.random.default_rng(np.random.SeedSequence([seed, _TAG[tag], e]))
+        n = N * K // 2
+        # uniform FP4 codes: raw 64-bit generator output viewed as bytes (two codes per byte)
+        fp4[e] = r.bit_generator.random_raw((n + 7) // 8).view(np.uint8)[:n].reshape(N, K // 2)
+        b = r.integers(b_range[0], b_range[1] + 1, size=(N, K // 32), dtype=np.int16)
+        e8m0[e] = (b + 127).astype(np.uint8)
+        blk[e] = r.uniform(blk_range[0], blk_range[1], size=(N // 128, K // 128))
+
+    with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(one, range(E)))
     return Matrix(fp4=fp4, e8m0=e8m0, blk=blk)
 
 

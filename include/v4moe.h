@@ -1,0 +1,203 @@
+/*
+ * v4moe.h -- C ABI of libv4moe: the DeepSeek-V4-style MoE layer forward on one
+ * MI355X (gfx950), with FP4 (MXFP4) expert weights dequantised losslessly to
+ * FP8 E4M3 for FP8 matrix-core contractions.
+ *
+ * Sources (cited by short tag and section):
+ *   P1 = "DeepSeek-V4揭秘：细粒度专家并行隐藏通信时延，FP4量化与TileLang协同优化百万Token上下文"
+ *        (itsolotime.com/archives/32374)
+ *   P2 = "DeepSeek V4架构学习笔记" (67808.cn/a/484462.html)
+ *   P4 = "DeepSeek-V4 的暗线之二：训练一台不会失控的万亿参数机器"
+ *        (blog.xieydd.top/deepseek-v4-control-part2)
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Outputs are fully overwritten.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *     is the default stream) and never synchronise the host, except
+ *     moe_prepack_weights, which is an offline step and synchronises.
+ *   - bf16 values travel as uint16_t bit patterns; E4M3 and FP4 as bytes.
+ *   - Return value: 0 on success, a negative V4MOE_E* code otherwise (no
+ *     exceptions cross the ABI).  A code is returned before anything is
+ *     enqueued.  Device faults surface at the caller's next synchronisation.
+ *   - T = 0 is a valid no-op: only expert_offsets (E+1 zeros) is written, by
+ *     moe_permute and moe_layer_forward; pointers to empty arrays may be NULL.
+ *   - Results are deterministic and batch-invariant: a token's outputs do not
+ *     depend on the other tokens of the batch nor on run-to-run scheduling
+ *     (P1 §3.1 batch invariance, §3.2 determinism).  No atomics accumulate
+ *     data; atomics only hand out work and signal readiness.
+ *   - Not thread-safe per workspace: concurrent calls must use distinct
+ *     workspaces.
+ */
+#ifndef V4MOE_H
+#define V4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+#define V4MOE_OK               0
+#define V4MOE_ENULL           -1   /* a required pointer is NULL                       */
+#define V4MOE_EDIMS           -2   /* unsupported or inconsistent dimensions            */
+#define V4MOE_EALIGN          -3   /* a pointer is not 16-byte aligned                  */
+#define V4MOE_EWORKSPACE      -4   /* workspace too small (see moe_workspace_bytes)     */
+#define V4MOE_ELAUNCH         -5   /* a HIP launch or runtime call failed               */
+#define V4MOE_ESCALE          -6   /* sub-block scale outside the lossless window       */
+#define V4MOE_EDEVICE         -7   /* current device is not a gfx950                    */
+
+/* Layer dimensions.  Requirements: 0 <= T; T*topk <= 2^24; H a multiple of
+ * 256 with 256 <= H <= 16384; I a multiple of 128 with 128 <= I <= 16384;
+ * 1 <= E <= 1024; 1 <= topk <= min(E, 16). */
+typedef struct {
+    int32_t T;      /* tokens in the batch                          */
+    int32_t H;      /* hidden size (linear1 K, linear2 N)           */
+    int32_t I;      /* expert intermediate size (linear1 N, linear2 K) */
+    int32_t E;      /* routed experts                               */
+    int32_t topk;   /* experts per token                            */
+} v4moe_dims;
+
+/* One expert weight matrix for all E experts: N output rows, K inputs.
+ * P1 §4 (FP4 quantisation-aware training): FP4 E2M1 elements with a scale per
+ * 1x32 sub-block, nested in 128x128 FP8 quantisation blocks.
+ *
+ * CANONICAL layout (what a checkpoint holds; input of moe_prepack_weights):
+ *   fp4  uint8 [E][N][K/2]     K contiguous; element k in the low nibble when k is even
+ *   e8m0 uint8 [E][N][K/32]    sub-block scale 2^b stored as the byte 127+b
+ *   blk  fp32  [E][N/128][K/128]  scale of each 128x128 block
+ * PACKED layout (output of moe_prepack_weights; what every compute entry
+ * point reads).  Same byte counts; blk is unchanged.  For each expert, each
+ * 16-row group n16 and each 128-wide K chunk c, a 1 KiB record holds 64
+ * slots of 16 bytes; slot s covers row n16*16 + (s%16) and the 32 elements
+ * k = c*128 + (s/16)*32 + [0,32); byte j of a slot holds element 8*(j/4)+j%4
+ * of those 32 in its low nibble and element 8*(j/4)+j%4+4 in its high nibble.
+ *   fp4  uint8 [E][N/16][K/128][64][16]
+ *   e8m0 uint8 [E][N/16][K/128][64]   (the scale byte of slot s)
+ *   blk  fp32  [E][N/128][K/128]
+ */
+typedef struct {
+    const void*  fp4;
+    const void*  e8m0;
+    const float* blk;
+} v4moe_mat;
+
+/* The SwiGLU expert weights (P1 §1.4: gate, up and down projections).
+ * gate, up: N = I, K = H.  down: N = H, K = I. */
+typedef struct {
+    v4moe_mat gate;
+    v4moe_mat up;
+    v4moe_mat down;
+} v4moe_experts;
+
+#define V4MOE_ROUTE_LEARNED 0
+#define V4MOE_ROUTE_HASH    1
+
+/* Workspace bytes needed by moe_permute, moe_expert_ffn and
+ * moe_layer_forward for these dimensions (host-only, pure).  Returns 0 for
+ * invalid dims. */
+size_t moe_workspace_bytes(const v4moe_dims* d);
+
+/* Routing (P2, DeepSeekMoE notes: the affinity is sqrt(softplus(.)) in place
+ * of V3's sigmoid; the early layers use hash routing).
+ *   x         bf16 [T][H]
+ *   w_router  fp32 [H][E]
+ *   bias      fp32 [E] or NULL: added to the logits (selection and weights)
+ *   mode      V4MOE_ROUTE_LEARNED: logits z[t][e] = fp32 fused multiply-add
+ *             chain over h ascending from +0 (+ bias as one fp32 add); the
+ *             topk largest z are taken, ties to the lower expert id, slot j
+ *             = j-th pick; a = sqrt(softplus(z)); topk_w = a / sum(a) over
+ *             the picks.
+ *             V4MOE_ROUTE_HASH: expert_j = splitmix64(id*topk + j) mod E,
+ *             stepping +1 mod E past experts already picked; topk_w = 1/topk.
+ *   token_ids int64 [T] or NULL (NULL: id = t); hash mode only.
+ *   topk_ids  int32 [T][topk]   (out)
+ *   topk_w    fp32  [T][topk]   (out)
+ * x, w_router: 16-byte aligned. */
+int moe_route(const v4moe_dims* d, const uint16_t* x, const float* w_router,
+              const float* bias, int32_t mode, const int64_t* token_ids,
+              int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Dispatch on one GPU (P1 §1.1-1.2: the FP8 dispatch stage becomes a local
+ * expert-sorted permutation; P1 §1.4: FP8 dispatch payload).
+ *   x              bf16 [T][H]
+ *   topk_ids       int32 [T][topk] (as produced by moe_route; ids must be in [0,E))
+ *   expert_offsets int32 [E+1]  (out) exclusive scan of per-expert pair counts
+ *   sorted_pair    int32 [T*topk] (out) pair ids p = t*topk+j, stably sorted by expert
+ *   pair_pos       int32 [T*topk] (out) inverse of sorted_pair
+ *   xq             uint8 [T][H]  (out) E4M3 codes of x: per token and 128-channel
+ *                  group g, s = fp32(amax/448) (1 if the group is zero) and
+ *                  q = E4M3(fp32(x/s)), round to nearest even, saturating
+ *   xs             fp32 [T][H/128] (out) the scales s
+ * The FP8 rows are gathered by the expert FFN on load: they are never
+ * materialised in expert order.  x, xq: 16-byte aligned. */
+int moe_permute(const v4moe_dims* d, const uint16_t* x, const int32_t* topk_ids,
+                int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                uint8_t* xq, float* xs, void* workspace, size_t ws_bytes, void* stream);
+
+/* Expert FFN over all experts, unfused schedule (linear1 + SwiGLU for every
+ * expert, then linear2 for every expert; P1 §1.1 stage model).
+ * For each pair p routed to expert e (rows of e in sorted order):
+ *   G, U = per-128-K-chunk FP8 products of xq[t] with the dequantised gate/up
+ *          rows, each chunk scaled by xs[t][c] * blk[n/128][c], fp32 accumulation;
+ *   h    = SiLU(G) * U  (fp32), requantised to E4M3 per 128 channels like x;
+ *   y[p] = bf16 of the same chunked product of h with the down rows.
+ *   y    bf16 [T*topk][H] (out), row p = t*topk + j.
+ * w: PACKED weights.  xq, y and all weight arrays: 16-byte aligned. */
+int moe_expert_ffn(const v4moe_dims* d, const uint8_t* xq, const float* xs,
+                   const int32_t* expert_offsets, const int32_t* sorted_pair,
+                   const v4moe_experts* w, uint16_t* y,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Combine as a weighted un-permute (P1 §1.4: BF16 combine payload; P1 §3.2:
+ * no atomics):  out[t] = bf16( sum_{j=0..topk-1} topk_w[t][j] * y[t*topk+j] ),
+ * summed in fp32 in increasing j.  y, out: 16-byte aligned. */
+int moe_combine(const v4moe_dims* d, const uint16_t* y, const float* topk_w,
+                uint16_t* out, void* stream);
+
+/* The whole layer: route, dispatch, then one persistent kernel that runs the
+ * experts in waves of 8 (P1 §1.2 and Fig. 5: the compute of wave w overlaps
+ * the gather of wave w+1 and the scatter-back of finished experts), then the
+ * combine.  Same arithmetic as the four calls above, so the output is
+ * bit-identical to moe_route + moe_permute + moe_expert_ffn + moe_combine.
+ *   topk_ids, topk_w, expert_offsets: outputs exported for checking.
+ *   out bf16 [T][H]. */
+int moe_layer_forward(const v4moe_dims* d, const uint16_t* x, const float* w_router,
+                      const float* bias, int32_t mode, const int64_t* token_ids,
+                      const v4moe_experts* w, int32_t* topk_ids, float* topk_w,
+                      int32_t* expert_offsets, uint16_t* out,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Offline: canonical -> packed weight layout (both device buffers of equal
+ * size; blk pointers of `packed` may alias those of `canonical`).  Checks that
+ * every sub-block exponent b lies in the lossless window [-8, 6] (P1 §4: the
+ * FP4->FP8 conversion is exact while the sub-block scales of a block stay
+ * within a bounded ratio; with E4M3 subnormals that window is b in [-8, 6]).
+ * Needs a workspace of at least 256 bytes; synchronises `stream`. */
+int moe_prepack_weights(const v4moe_dims* d, const v4moe_experts* canonical,
+                        const v4moe_experts* packed, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/* Test export of the dequantisation used inside the matrix kernels:
+ * expert `expert` of the PACKED matrix m (N rows, K inputs) -> E4M3 bytes
+ * [N][K] in canonical row-major order. */
+int moe_dequant_fp8(const v4moe_mat* m, int32_t N, int32_t K, int32_t expert,
+                    uint8_t* out, void* stream);
+
+/* Profiling hook (no effect on results).  start/stop are hipEvent_t handles
+ * created by the caller (or NULL to clear).  The next moe_expert_ffn or
+ * moe_layer_forward call made by this host thread records `start` on its
+ * stream just before its expert-FFN kernels and `stop` just after them, then
+ * forgets both; elapsed time between them is the expert FFN's device time. */
+void moe_time_next_ffn(void* start_event, void* stop_event);
+
+/* Text for an error code. */
+const char* moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* V4MOE_H */

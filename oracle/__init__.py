@@ -54,6 +54,8 @@ def lib():
         if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
             build()
         L = ctypes.CDLL(_SO)
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = ci
         L.orc_e2m1_value.argtypes = [ci]; L.orc_e2m1_value.restype = ctypes.c_double
         L.orc_e4m3_value.argtypes = [ci]; L.orc_e4m3_value.restype = ctypes.c_double
         L.orc_e4m3_encode.argtypes = [ctypes.c_double]; L.orc_e4m3_encode.restype = ci
@@ -84,6 +86,10 @@ def lib():
 
 def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
 
 
 # ---- scalar format helpers ----------------------------------------------------------

@@ -30,8 +30,21 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define EXPORT __attribute__((visibility("default")))
+
+/* Threads the OpenMP loops below use (1 without OpenMP). */
+EXPORT int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */
@@ -156,12 +169,17 @@ EXPORT int orc_dequant_bitmap(int code, int b)
  * e8m0 [N][K/32] (byte = 127 + b)  ->  E4M3 bytes [N][K]. */
 EXPORT void orc_dequant_matrix(int N, int K, const uint8_t* fp4, const uint8_t* e8m0, uint8_t* out)
 {
+    /* memoised orc_dequant_code: one entry per (code, e8m0 byte) */
+    uint8_t lut[16][256];
+    for (int c = 0; c < 16; c++)
+        for (int s = 0; s < 256; s++)
+            lut[c][s] = (uint8_t)orc_dequant_code(c, s - 127);
+#pragma omp parallel for schedule(static)
     for (int n = 0; n < N; n++)
         for (int k = 0; k < K; k++) {
             uint8_t byte = fp4[(size_t)n * (K / 2) + k / 2];
             int code = (k & 1) ? (byte >> 4) : (byte & 15);
-            int b = (int)e8m0[(size_t)n * (K / 32) + k / 32] - 127;
-            out[(size_t)n * K + k] = (uint8_t)orc_dequant_code(code, b);
+            out[(size_t)n * K + k] = lut[code][e8m0[(size_t)n * (K / 32) + k / 32]];
         }
 }
 

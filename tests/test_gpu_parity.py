@@ -1,0 +1,273 @@
+"""GPU parity of libv4moe against the CPU oracle (needs an MI355X).
+
+Bar (per the method's acceptance): routing ids, permutation, expert offsets,
+dequantised E4M3 bytes and the FP8 dispatch payload are bit-exact; routing
+weights within 1e-6 relative; the bf16 output within relative L2 <= 2e-3 and
+max|d| <= 1e-2 * max|ref|.  Outputs are also checked to be bit-identical
+between the unfused and the wave-scheduled paths, across repeated runs, and
+between a request run alone and inside a larger batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_weight_grouped_amd import inputs, v4moe
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REL_L2 = 2e-3
+MAX_REL = 1e-2
+
+
+def bf16_f64(bits):
+    a = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return a.view(np.float32).astype(np.float64)
+
+
+def check_out(got_bits, ref_bits, what=""):
+    g, r = bf16_f64(got_bits), bf16_f64(ref_bits)
+    rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    mx = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
+    print(f"  {what} rel_l2={rel:.3e} max_rel={mx:.3e} exact={np.mean(g == r):.4f}", flush=True)
+    assert rel <= REL_L2, (what, rel)
+    assert mx <= MAX_REL, (what, mx)
+
+
+_layers = {}
+
+
+def layer_for(inp):
+    d = inp.dims
+    key = (d.H, d.I, d.E, d.topk, id(inp.experts))
+    if key not in _layers:
+        if len(_layers) > 2:
+            _layers.clear()
+            torch.cuda.empty_cache()
+        dims = v4moe.dims(max(d.T, 1), d.H, d.I, d.E, d.topk)
+        ex = v4moe.upload_experts(inp.experts, dims, DEV)
+        _layers[key] = v4moe.MoELayer(d.H, d.I, d.E, d.topk, ex,
+                                      torch.from_numpy(inp.w_router).to(DEV), DEV)
+    return _layers[key]
+
+
+def dev_inputs(inp):
+    x = torch.from_numpy(inp.x.view(np.int16)).to(DEV)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(DEV)
+    tid = None if inp.token_ids is None else torch.from_numpy(inp.token_ids).to(DEV)
+    return x, bias, tid
+
+
+def run_unfused(inp):
+    layer = layer_for(inp)
+    x, bias, tid = dev_inputs(inp)
+    r = layer.forward_unfused(x, bias, inp.mode, tid)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in r.items()}
+
+
+def run_fused(inp):
+    layer = layer_for(inp)
+    x, bias, tid = dev_inputs(inp)
+    out, ids, w, off = layer.forward(x, bias, inp.mode, tid)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu().numpy(), ids=ids.cpu().numpy(), w=w.cpu().numpy(), offsets=off.cpu().numpy())
+
+
+def custom(T, H, I, E, k, seed=3, mode=0, bias=False):
+    ex = inputs.gen_experts(seed, E, H, I)
+    return inputs.Inputs(dims=inputs.Dims(T, H, I, E, k), mode=mode, x=inputs.gen_x(seed, T, H),
+                         w_router=inputs.gen_router(seed, H, E),
+                         bias=inputs.zipf_bias(seed, E) if bias else None,
+                         token_ids=np.arange(T, dtype=np.int64) * 3 + 1 if mode == 1 else None,
+                         experts=ex)
+
+
+def full_check(inp, label):
+    """Everything against the oracle on all tokens (small shapes)."""
+    print(f"[{label}] dims={inp.dims} mode={inp.mode}", flush=True)
+    ref = oracle.layer_forward(inp, want_y=True)
+    g = run_unfused(inp)
+    T, k = inp.dims.T, inp.dims.topk
+    assert np.array_equal(g["ids"], ref["ids"])
+    np.testing.assert_allclose(g["w"], ref["w"], rtol=1e-6, atol=0)
+    assert np.array_equal(g["offsets"], ref["offsets"])
+    assert np.array_equal(g["sorted_pair"], ref["sorted_pair"])
+    assert np.array_equal(g["pair_pos"], ref["pair_pos"])
+    assert np.array_equal(g["xq"], ref["xq"])
+    assert np.array_equal(g["xs"], ref["xs"])
+    check_out(g["y"], ref["y"], f"{label} y")
+    check_out(g["out"], ref["out"], f"{label} out")
+    f = run_fused(inp)
+    assert np.array_equal(f["ids"], g["ids"]) and np.array_equal(f["offsets"], g["offsets"])
+    assert np.array_equal(f["out"], g["out"]), "wave-scheduled path differs from the unfused path"
+    return g
+
+
+# ---------------------------------------------------------------------------------------------
+def test_dequant_export_tiny():
+    inp = inputs.make("tiny")
+    d = inp.dims
+    layer = layer_for(inp)
+    for name, N, K in (("gate", d.I, d.H), ("up", d.I, d.H), ("down", d.H, d.I)):
+        m = getattr(layer.experts, name)
+        hm = getattr(inp.experts, name)
+        for e in range(d.E):
+            out = torch.empty((N, K), dtype=torch.uint8, device=DEV)
+            v4moe.moe_dequant_fp8(m, N, K, e, out)
+            torch.cuda.synchronize()
+            ref = oracle.dequant_matrix(hm.fp4[e], hm.e8m0[e])
+            assert np.array_equal(out.cpu().numpy(), ref), (name, e)
+
+
+def test_dequant_lossless_window_all_exponents():
+    """Every code with every sub-block exponent of the lossless window [-8, 6],
+    through prepack and the dequant export, against the oracle and against
+    e2m1(code) * 2^b computed straight from the definition."""
+    H, I = 2048, 128
+    codes = np.arange(16, dtype=np.uint8)
+    row = np.tile(codes[0::2] | (codes[1::2] << 4), H // 16)
+    fp4 = np.broadcast_to(row, (1, I, H // 2)).copy()
+    fp4[0, 1::2] = np.roll(fp4[0, 1::2], 3, axis=1)
+    b = np.concatenate([np.arange(-8, 7), [0]])              # one exponent per 128-wide chunk
+    e8 = np.broadcast_to(np.repeat(127 + b, 4).astype(np.uint8), (1, I, H // 32)).copy()
+    e8[0, 5] = np.roll(e8[0, 5], 7)
+    gate = inputs.Matrix(fp4=fp4, e8m0=e8, blk=np.ones((1, I // 128, H // 128), np.float32))
+    down = inputs.Matrix(fp4=np.zeros((1, H, I // 2), np.uint8), e8m0=np.full((1, H, I // 32), 127, np.uint8),
+                         blk=np.ones((1, H // 128, I // 128), np.float32))
+    pk = v4moe.upload_experts(inputs.Experts(gate=gate, up=gate, down=down), v4moe.dims(1, H, I, 1, 1), DEV)
+    out = torch.empty((I, H), dtype=torch.uint8, device=DEV)
+    v4moe.moe_dequant_fp8(pk.gate, I, H, 0, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got, oracle.dequant_matrix(fp4[0], e8[0]))
+    vals = torch.from_numpy(got).view(torch.float8_e4m3fn).double().numpy()
+    el = np.empty((I, H), np.int64)
+    el[:, 0::2] = fp4[0] & 15
+    el[:, 1::2] = fp4[0] >> 4
+    mag = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])[el & 7] * np.where(el & 8, -1.0, 1.0)
+    want = mag * np.exp2(np.repeat(e8[0].astype(np.float64) - 127, 32, 1))
+    assert np.array_equal(vals, want)
+    assert np.array_equal(np.signbit(vals), (el & 8) > 0)     # negative zero kept
+
+
+def test_prepack_rejects_scales_outside_window():
+    E, H, I = 1, 256, 128
+    ex = inputs.gen_experts(9, E, H, I)
+    bad = inputs.Matrix(fp4=ex.up.fp4, e8m0=ex.up.e8m0.copy(), blk=ex.up.blk)
+    bad.e8m0[0, 5, 3] = 127 + 7
+    with pytest.raises(v4moe.V4MoeError) as ei:
+        v4moe.upload_experts(inputs.Experts(ex.gate, bad, ex.down), v4moe.dims(1, H, I, E, 1), DEV)
+    assert ei.value.code == -6
+
+
+def test_tiny_full_parity():
+    full_check(inputs.make("tiny"), "tiny")
+
+
+@pytest.mark.parametrize("T,H,I,E,k,mode,bias", [
+    (37, 256, 128, 8, 2, 0, False),     # ragged tail, 16-row tiles
+    (1, 256, 128, 8, 8, 0, False),      # one token to every expert
+    (100, 256, 384, 12, 4, 0, True),    # I = 3 blocks, partial scheduling wave, bias
+    (200, 512, 256, 8, 2, 0, False),    # 64-row tiles
+    (300, 256, 128, 16, 3, 1, False),   # hash routing, odd k
+    (600, 256, 256, 4, 2, 0, False),    # 128-row tiles, several per expert
+    (513, 768, 128, 5, 5, 0, False),    # k = E, 128-row tiles
+])
+def test_shapes_full_parity(T, H, I, E, k, mode, bias):
+    full_check(custom(T, H, I, E, k, mode=mode, bias=bias), f"T{T}H{H}I{I}E{E}k{k}")
+
+
+def test_zero_tokens():
+    inp = inputs.make("tiny", T=0)
+    layer = layer_for(inputs.make("tiny"))
+    x = torch.empty((0, 256), dtype=torch.int16, device=DEV)
+    out, ids, w, off = layer.forward(x)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
+    assert np.all(off.cpu().numpy() == 0)
+    del inp
+
+
+def test_skewed_experts_some_empty():
+    inp = custom(256, 256, 128, 8, 2, bias=True)
+    inp.bias[:] = np.array([6, 0, -30, -30, 3, -30, 0, -30], np.float32)   # 4 experts never picked
+    g = full_check(inp, "skew")
+    cnt = np.diff(g["offsets"])
+    assert (cnt == 0).sum() >= 3 and cnt.max() > 100
+
+
+# ---- full-size workloads (H=4096, I=2048, E=256, k=8) ----------------------------------------
+def sampled_check(inp, label, n_sample=12, seed=0):
+    d = inp.dims
+    print(f"[{label}] T={d.T}", flush=True)
+    g = run_unfused(inp)
+    sample = np.random.default_rng(seed).choice(d.T, size=min(n_sample, d.T), replace=False)
+    cnt = np.bincount(g["ids"].ravel(), minlength=d.E)
+    hot = int(np.argmax(cnt))
+    hot_tok = np.nonzero((g["ids"] == hot).any(1))[0][:2]
+    sample = np.unique(np.concatenate([sample, hot_tok, [0, d.T - 1]]))
+    ref = oracle.layer_forward(inp, subset=sample, want_y=True)
+    assert np.array_equal(g["ids"], ref["ids"])
+    np.testing.assert_allclose(g["w"], ref["w"], rtol=1e-6, atol=0)
+    assert np.array_equal(g["offsets"], ref["offsets"])
+    assert np.array_equal(g["sorted_pair"], ref["sorted_pair"])
+    assert np.array_equal(g["pair_pos"], ref["pair_pos"])
+    assert np.array_equal(g["xq"], ref["xq"])
+    assert np.array_equal(g["xs"], ref["xs"])
+    rows = (sample[:, None] * d.topk + np.arange(d.topk)[None, :]).ravel()
+    check_out(g["y"][rows], ref["y"][rows], f"{label} y[sample]")
+    check_out(g["out"][sample], ref["out"][sample], f"{label} out[sample]")
+    print(f"  load max/mean={cnt.max() / cnt.mean():.2f} idle={(cnt == 0).sum()}", flush=True)
+    f = run_fused(inp)
+    assert np.array_equal(f["out"], g["out"]), "wave-scheduled path differs from the unfused path"
+    return g, f
+
+
+@pytest.mark.slow
+def test_decode_full_size():
+    inp = inputs.make("decode")
+    g, f = sampled_check(inp, "decode", n_sample=24)
+    for _ in range(3):
+        assert np.array_equal(run_fused(inp)["out"], f["out"])
+
+
+@pytest.mark.slow
+def test_prefill_full_size():
+    inp = inputs.make("prefill")
+    g, f = sampled_check(inp, "prefill", n_sample=10)
+    assert np.array_equal(run_fused(inp)["out"], f["out"])
+
+
+@pytest.mark.slow
+def test_zipf_full_size():
+    g, _ = sampled_check(inputs.make("zipf"), "zipf", n_sample=8)
+    cnt = np.diff(g["offsets"])
+    assert cnt.max() > 10 * cnt.mean() and (cnt == 0).sum() > 0
+
+
+@pytest.mark.slow
+def test_hash_full_size():
+    g, _ = sampled_check(inputs.make("hash"), "hash", n_sample=8)
+    assert np.all(g["w"] == np.float32(1 / 8))
+
+
+@pytest.mark.slow
+def test_ragged_batch_invariance_and_determinism():
+    inp = inputs.make("ragged")
+    L = inp.lengths
+    starts = np.concatenate([[0], np.cumsum(L)])
+    print(f"[ragged] T={inp.dims.T} requests={len(L)}", flush=True)
+    g, f = sampled_check(inp, "ragged", n_sample=8)
+    layer = layer_for(inp)
+    x, _, _ = dev_inputs(inp)
+    for _ in range(10):
+        out, *_ = layer.forward(x)
+        assert np.array_equal(out.cpu().numpy(), f["out"])
+    for r in range(len(L)):
+        lo, hi = int(starts[r]), int(starts[r + 1])
+        out, ids, *_ = layer.forward(x[lo:hi].contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), f["out"][lo:hi]), f"request {r} differs alone vs batch"
+        assert np.array_equal(ids.cpu().numpy(), f["ids"][lo:hi])
