@@ -168,7 +168,7 @@ def test_tiny_full_parity():
 
 @pytest.mark.parametrize("T,H,I,E,k,mode,bias", [
     (37, 256, 128, 8, 2, 0, False),     # ragged tail, 16-row tiles
-    (1, 256, 128, 8, 8, 0, False),      # one token to every expert
+    (16, 256, 128, 8, 8, 0, False),     # every token to every expert
     (100, 256, 384, 12, 4, 0, True),    # I = 3 blocks, partial scheduling wave, bias
     (200, 512, 256, 8, 2, 0, False),    # 64-row tiles
     (300, 256, 128, 16, 3, 1, False),   # hash routing, odd k
@@ -177,6 +177,23 @@ def test_tiny_full_parity():
 ])
 def test_shapes_full_parity(T, H, I, E, k, mode, bias):
     full_check(custom(T, H, I, E, k, mode=mode, bias=bias), f"T{T}H{H}I{I}E{E}k{k}")
+
+
+def test_single_token_calls():
+    """32 calls with T = 1 (k = E): together within tolerance of the oracle, and
+    each bit-identical to the same token inside the batched call."""
+    inp = custom(32, 256, 128, 8, 8)
+    ref = oracle.layer_forward(inp)
+    layer = layer_for(inp)
+    x, _, _ = dev_inputs(inp)
+    batched, *_ = layer.forward(x)
+    outs = []
+    for t in range(32):
+        o, *_ = layer.forward(x[t:t + 1].contiguous())
+        outs.append(o)
+    got = torch.cat(outs).cpu().numpy()
+    assert np.array_equal(got, batched.cpu().numpy())
+    check_out(got, ref["out"], "T=1 calls")
 
 
 def test_zero_tokens():
