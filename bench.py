@@ -70,6 +70,10 @@ def run_gpu(name, steps, warmup, layer_cache):
         layer.forward(x, bias, inp.mode, tid, out=out)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:          # torch creates the HIP event on first record
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         v4moe.moe_time_next_ffn(*ev[i])

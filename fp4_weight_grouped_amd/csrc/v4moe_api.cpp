@@ -63,7 +63,7 @@ bool dims_ok(const v4moe_dims* d)
 
 // Workspace carving (offsets in bytes, each 256-aligned).
 struct Layout {
-    size_t xq, xs, sorted_pair, pair_pos, hist, mt_expert, mt_row0, ctrl, done1, queue, hq, hs, y;
+    size_t z, xq, xs, sorted_pair, pair_pos, hist, mt_expert, mt_row0, ctrl, done1, queue, hq, hs, y;
     size_t total;
     int MT, n_mt_bound, nblk;
 };
@@ -79,6 +79,7 @@ Layout layout(const v4moe_dims* d)
     const size_t NB1 = I / 128, NB2 = H / 256;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
+    L.z = take(T * E * 4);
     L.xq = take(T * H);
     L.xs = take(T * (H / 128) * 4);
     L.sorted_pair = take(P * 4);
@@ -188,17 +189,23 @@ __attribute__((visibility("default"))) const char* moe_strerror(int code)
 __attribute__((visibility("default"))) int moe_route(const v4moe_dims* d, const uint16_t* x,
                                                      const float* w_router, const float* bias,
                                                      int32_t mode, const int64_t* token_ids,
-                                                     int32_t* topk_ids, float* topk_w, void* stream)
+                                                     int32_t* topk_ids, float* topk_w, void* workspace,
+                                                     size_t ws_bytes, void* stream)
 {
     if (!dims_ok(d)) return V4MOE_EDIMS;
     if (mode != V4MOE_ROUTE_LEARNED && mode != V4MOE_ROUTE_HASH) return V4MOE_EDIMS;
     if (d->T == 0) return V4MOE_OK;
     if (!topk_ids || !topk_w) return V4MOE_ENULL;
-    if (mode == V4MOE_ROUTE_LEARNED && (!x || !w_router)) return V4MOE_ENULL;
-    if (mode == V4MOE_ROUTE_LEARNED && (!aligned16(x) || !aligned16(w_router))) return V4MOE_EALIGN;
+    if (mode == V4MOE_ROUTE_LEARNED && (!x || !w_router || !workspace)) return V4MOE_ENULL;
+    if (mode == V4MOE_ROUTE_LEARNED && (!aligned16(x) || !aligned16(w_router) || !aligned16(workspace)))
+        return V4MOE_EALIGN;
+    const Layout L = layout(d);
+    if (mode == V4MOE_ROUTE_LEARNED && ws_bytes < L.total) return V4MOE_EWORKSPACE;
     DeviceInfo* di = device_info();
     if (!di) return V4MOE_EDEVICE;
-    if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w,
+    float* z = mode == V4MOE_ROUTE_LEARNED ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + L.z)
+                                           : nullptr;
+    if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w, z,
                      as_stream(stream)) != hipSuccess)
         return V4MOE_ELAUNCH;
     return V4MOE_OK;
@@ -297,8 +304,8 @@ __attribute__((visibility("default"))) int moe_layer_forward(
     int32_t* sp = reinterpret_cast<int32_t*>(ws + L.sorted_pair);
     int32_t* pp = reinterpret_cast<int32_t*>(ws + L.pair_pos);
     uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
-    if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w, s) !=
-        hipSuccess)
+    if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w,
+                     reinterpret_cast<float*>(ws + L.z), s) != hipSuccess)
         return V4MOE_ELAUNCH;
     if (launch_quant_x(d->T, d->H, x, xq, xs, s) != hipSuccess) return V4MOE_ELAUNCH;
     if (launch_permute(d->T, d->topk, d->E, topk_ids, expert_offsets, sp, pp,

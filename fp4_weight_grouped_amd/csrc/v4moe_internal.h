@@ -40,7 +40,7 @@ struct FfnArgs {
 
 hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
                         const float* bias, int mode, const int64_t* token_ids,
-                        int32_t* ids, float* w, hipStream_t s);
+                        int32_t* ids, float* w, float* z, hipStream_t s);
 hipError_t launch_quant_x(int T, int H, const uint16_t* x, uint8_t* xq, float* xs, hipStream_t s);
 hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos, int32_t* hist, hipStream_t s);

@@ -31,99 +31,96 @@ namespace v4moe {
 // Routing
 // ---------------------------------------------------------------------------
 
-// Logits for TW tokens per block, every expert: thread = expert (E > 256 loops),
-// each thread runs TW independent fp32 fma chains over h ascending.  The x
-// values are block-uniform (scalar loads); W_r rows are read coalesced along e.
-// Then one wave per token selects the top k (logit descending, lower id on
-// ties), and lanes 0..k-1 compute sqrt(softplus(z)) and the normalised weights.
-template <int TW>
-__global__ __launch_bounds__(256) void k_route_learned(int T, int H, int E, int k,
-                                                       const uint16_t* __restrict__ x,
-                                                       const float* __restrict__ wr,
-                                                       const float* __restrict__ bias,
-                                                       int32_t* __restrict__ ids,
-                                                       float* __restrict__ wts)
+// Router logits.  Lane = token, wave = ES consecutive experts, so every
+// router weight W_r[h][e] a wave needs is wave-uniform (scalar loads, shared by
+// the 64 tokens) and each lane streams its own token row of x.  Each lane
+// runs ES independent fp32 fma chains over h ascending from +0; the optional
+// bias is one fp32 add afterwards.  z is [T][E].
+template <int ES>
+__global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
+                                                      const uint16_t* __restrict__ x,
+                                                      const float* __restrict__ wr,
+                                                      const float* __restrict__ bias,
+                                                      float* __restrict__ z)
 {
-    extern __shared__ float zs[];  // [TW][E]
-    const int t0 = blockIdx.x * TW;
-    const int tid = threadIdx.x;
-
-    for (int e0 = 0; e0 < E; e0 += 256) {
-        const int e = e0 + tid;
-        const bool ok = e < E;
-        const float* w = wr + (ok ? e : 0);
-        const uint32_t* xr[TW];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t = blockIdx.x * 64 + lane;
+    const int eg = (blockIdx.y * 4 + w) * ES;
+    if (eg >= E) return;
+    const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)min(t, T - 1) * H);
+    int col[ES];
 #pragma unroll
-        for (int i = 0; i < TW; i++) {
-            int tok = min(t0 + i, T - 1);
-            xr[i] = reinterpret_cast<const uint32_t*>(x + (size_t)tok * H);
+    for (int j = 0; j < ES; j++) col[j] = min(eg + j, E - 1);
+    float acc[ES];
+#pragma unroll
+    for (int j = 0; j < ES; j++) acc[j] = 0.0f;
+#pragma unroll 2
+    for (int h = 0; h < H; h += 8) {
+        const uint4 xx = xp[h / 8];
+        const uint32_t q[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const float xv = bf16_to_f32(u & 1 ? q[u / 2] >> 16 : q[u / 2] & 0xFFFFu);
+            const float* wrow = wr + (size_t)(h + u) * E;
+#pragma unroll
+            for (int j = 0; j < ES; j++) acc[j] = __builtin_fmaf(xv, wrow[col[j]], acc[j]);
         }
-        float acc[TW];
+    }
+    if (t < T) {
 #pragma unroll
-        for (int i = 0; i < TW; i++) acc[i] = 0.0f;
-        for (int h = 0; h < H; h += 8) {
-            float wv[8];
-#pragma unroll
-            for (int u = 0; u < 8; u++) wv[u] = w[(size_t)(h + u) * E];
-#pragma unroll
-            for (int i = 0; i < TW; i++) {
-                uint4 xx = *reinterpret_cast<const uint4*>(xr[i] + h / 2);
-                uint32_t q[4] = {xx.x, xx.y, xx.z, xx.w};
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    acc[i] = __builtin_fmaf(bf16_to_f32(q[u] & 0xFFFFu), wv[2 * u], acc[i]);
-                    acc[i] = __builtin_fmaf(bf16_to_f32(q[u] >> 16), wv[2 * u + 1], acc[i]);
-                }
-            }
-        }
-        if (ok) {
-#pragma unroll
-            for (int i = 0; i < TW; i++) {
-                float z = acc[i];
-                if (bias) z = z + bias[e];
-                zs[i * E + e] = z;
+        for (int j = 0; j < ES; j++) {
+            if (eg + j < E) {
+                float v = acc[j];
+                if (bias) v = v + bias[eg + j];
+                z[(size_t)t * E + eg + j] = v;
             }
         }
     }
-    __syncthreads();
+}
 
-    const int lane = tid & 63;
-    const int wv = tid >> 6;
-    for (int i = wv; i < TW; i += 4) {
-        const int t = t0 + i;
-        if (t >= T) break;
-        const float* z = zs + i * E;
-        uint32_t taken = 0;  // bit q: expert lane + 64q already picked
-        float my_z = 0.0f;
-        int my_e = 0;
-        for (int j = 0; j < k; j++) {
-            float bv = 0.0f;
-            int be = INT_MAX;
-            for (int q = 0; q * 64 < E; q++) {
-                int e = lane + 64 * q;
-                if (e < E && !((taken >> q) & 1u)) {
-                    float v = z[e];
-                    if (be == INT_MAX || v > bv) { bv = v; be = e; }
-                }
+// Top-k per token (one wave per token): the k largest logits, the lower expert
+// id winning ties, slot j = j-th pick; then lanes 0..k-1 compute the affinity
+// sqrt(softplus(z)) and the weights normalised over the k picks.
+__global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, const float* __restrict__ zg,
+                                                      int32_t* __restrict__ ids, float* __restrict__ wts)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* z = zg + (size_t)t * E;
+    float zv[16];
+#pragma unroll
+    for (int q = 0; q < 16; q++) zv[q] = (q * 64 < E && lane + 64 * q < E) ? z[lane + 64 * q] : 0.0f;
+    uint32_t taken = 0;  // bit q: expert lane + 64q already picked
+    float my_z = 0.0f;
+    int my_e = 0;
+    for (int j = 0; j < k; j++) {
+        float bv = 0.0f;
+        int be = INT_MAX;
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+            const int e = lane + 64 * q;
+            if (q * 64 < E && e < E && !((taken >> q) & 1u)) {
+                if (be == INT_MAX || zv[q] > bv) { bv = zv[q]; be = e; }
             }
-            for (int off = 32; off >= 1; off >>= 1) {
-                float ov = __shfl_xor(bv, off);
-                int oe = __shfl_xor(be, off);
-                bool better = oe != INT_MAX &&
-                              (be == INT_MAX || ov > bv || (ov == bv && oe < be));
-                if (better) { bv = ov; be = oe; }
-            }
-            if ((be & 63) == lane) taken |= 1u << (be >> 6);
-            if (lane == j) { my_z = bv; my_e = be; }
         }
-        // affinity sqrt(softplus(z)), softplus(z) = max(z,0) + log1p(exp(-|z|))
-        float a = sqrtf(fmaxf(my_z, 0.0f) + log1pf(expf(-fabsf(my_z))));
-        float sum = 0.0f;
-        for (int j = 0; j < k; j++) sum += __shfl(a, j);
-        if (lane < k) {
-            ids[(size_t)t * k + lane] = my_e;
-            wts[(size_t)t * k + lane] = sum > 0.0f ? a / sum : 1.0f / (float)k;
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oe = __shfl_xor(be, off);
+            const bool better = oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be));
+            if (better) { bv = ov; be = oe; }
         }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        if (lane == j) { my_z = bv; my_e = be; }
+    }
+    // affinity sqrt(softplus(z)), softplus(z) = max(z,0) + log1p(exp(-|z|))
+    const float a = sqrtf(fmaxf(my_z, 0.0f) + log1pf(expf(-fabsf(my_z))));
+    float sum = 0.0f;
+    for (int j = 0; j < k; j++) sum += __shfl(a, j);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = my_e;
+        wts[(size_t)t * k + lane] = sum > 0.0f ? a / sum : 1.0f / (float)k;
     }
 }
 
@@ -239,33 +236,72 @@ __global__ __launch_bounds__(64) void k_perm_pass(int P, int E, const int32_t* _
     }
 }
 
-// One block: expert totals, exclusive scan -> offsets[E+1], and per-block bases
-// (offsets[e] + counts of earlier blocks) written back over the counts.
+// Exclusive prefix sum of one int per thread over a 1024-thread block (wave
+// scans, then a scan of the 16 wave totals).  Returns the prefix; *total gets
+// the sum.  Every thread must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total)
+{
+    __shared__ int wsum[16];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        int s = lane < 16 ? wsum[lane] : 0;
+        const int orig = s;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int y = __shfl_up(s, off);
+            if (lane >= off) s += y;
+        }
+        if (lane < 16) wsum[lane] = s - orig;
+        if (lane == 15) *total = s;
+    }
+    __syncthreads();
+    const int r = x - v + wsum[wid];
+    __syncthreads();
+    return r;
+}
+
+// One block: expert totals, offsets[E+1] (exclusive scan), and per-block bases
+// (offsets[e] + counts of earlier blocks) written back over the counts.  The
+// blocks of a column are split into P contiguous parts summed in parallel.
 __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __restrict__ hist,
                                                     int32_t* __restrict__ offsets)
 {
-    __shared__ int32_t tot[1024];
-    const int e = threadIdx.x;
+    __shared__ int32_t part_sum[1024];
+    __shared__ int total_s;
+    const int tid = threadIdx.x;
+    const int P = max(1, min(1024 / E, nblk));
+    const int e = tid % E, part = tid / E;
+    const bool active = part < P;
+    const int b0 = active ? (int)((long long)part * nblk / P) : 0;
+    const int b1 = active ? (int)((long long)(part + 1) * nblk / P) : 0;
     int s = 0;
-    if (e < E)
-        for (int b = 0; b < nblk; b++) s += hist[(size_t)b * E + e];
-    tot[e] = s;
+    for (int b = b0; b < b1; b++) s += hist[(size_t)b * E + e];
+    part_sum[tid] = active ? s : 0;
     __syncthreads();
-    if (e == 0) {
+    int tot = 0;
+    if (tid < E)
+        for (int p = 0; p < P; p++) tot += part_sum[p * E + tid];
+    int total = 0;
+    const int off = block_exclusive_scan(tid < E ? tot : 0, &total_s);
+    total = total_s;
+    if (tid < E) offsets[tid] = off;
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    // part base = offsets[e] + sums of the earlier parts of the column
+    if (active) {
         int run = 0;
-        for (int i = 0; i < E; i++) {
-            int c = tot[i];
-            tot[i] = run;
-            run += c;
-        }
-        offsets[E] = run;
-    }
-    __syncthreads();
-    if (e < E) {
-        int run = tot[e];
-        offsets[e] = run;
-        for (int b = 0; b < nblk; b++) {
-            int c = hist[(size_t)b * E + e];
+        for (int p = 0; p < part; p++) run += part_sum[p * E + e];
+        run += offsets[e];
+        for (int b = b0; b < b1; b++) {
+            const int c = hist[(size_t)b * E + e];
             hist[(size_t)b * E + e] = run;
             run += c;
         }
@@ -289,54 +325,44 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
                                                       uint32_t* __restrict__ queue)
 {
     __shared__ int32_t base[1025];
-    __shared__ int32_t segpos[2 * 129];
+    __shared__ int32_t segpos[2 * 128];
+    __shared__ int total_s, qlen_s;
     const int tid = threadIdx.x;
-    int n = 0;
-    if (tid < E) n = (offsets[tid + 1] - offsets[tid] + M - 1) / M;
-    base[tid] = n;
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < E; i++) {
-            int c = base[i];
-            base[i] = run;
-            run += c;
-        }
-        base[E] = run;
-    }
+    const int n = tid < E ? (offsets[tid + 1] - offsets[tid] + M - 1) / M : 0;
+    const int my_base = block_exclusive_scan(n, &total_s);
+    base[tid] = my_base;
+    if (tid == 0) base[E] = total_s;
     __syncthreads();
     const int total = base[E];
-    if (tid < E) {
-        for (int m = 0; m < n; m++) {
-            mt_expert[base[tid] + m] = tid;
-            mt_row0[base[tid] + m] = offsets[tid] + m * M;
-        }
+    for (int m = 0; m < n; m++) {
+        mt_expert[my_base + m] = tid;
+        mt_row0[my_base + m] = offsets[tid] + m * M;
     }
     for (int i = tid; i < total; i += 1024) done1[i] = 0;
+    const int W = (E + kWaveExperts - 1) / kWaveExperts;
+    // Segment i of the queue: 0 = linear1 of wave 0; 2w-1 = linear1 of wave w
+    // and 2w = linear2 of wave w-1 (w >= 1); 2W-1 = linear2 of wave W-1.
+    int len = 0;
+    if (build_queue && tid < 2 * W) {
+        const int i = tid;
+        const int ph = (i == 0) ? 0 : (i == 2 * W - 1) ? 1 : ((i & 1) ? 0 : 1);
+        const int wv = (i == 0) ? 0 : (i == 2 * W - 1) ? W - 1 : (ph == 0 ? (i + 1) / 2 : i / 2 - 1);
+        const int a = base[min(E, (wv + 1) * kWaveExperts)] - base[wv * kWaveExperts];
+        len = a * (ph ? NB2 : NB1);
+    }
+    const int start = block_exclusive_scan(len, &qlen_s);
+    if (build_queue && tid < 2 * W) {
+        const int i = tid;
+        const int ph = (i == 0) ? 0 : (i == 2 * W - 1) ? 1 : ((i & 1) ? 0 : 1);
+        const int wv = (i == 0) ? 0 : (i == 2 * W - 1) ? W - 1 : (ph == 0 ? (i + 1) / 2 : i / 2 - 1);
+        segpos[2 * wv + ph] = start;
+    }
     if (tid == 0) {
         ctrl[0] = total;
         ctrl[1] = 0;
         ctrl[2] = build_queue ? total * (NB1 + NB2) : 0;
     }
     if (!build_queue) return;
-    const int W = (E + kWaveExperts - 1) / kWaveExperts;
-    if (tid == 0) {
-        // segment order: F1(0), [F1(w), F2(w-1)] for w = 1..W-1, F2(W-1)
-        int pos = 0;
-        for (int s = 0; s <= W; s++) {
-            if (s < W) {
-                int a = base[min(E, (s + 1) * kWaveExperts)] - base[s * kWaveExperts];
-                segpos[2 * s] = pos;
-                pos += a * NB1;
-            }
-            if (s >= 1) {
-                int w = s - 1;
-                int a = base[min(E, (w + 1) * kWaveExperts)] - base[w * kWaveExperts];
-                segpos[2 * w + 1] = pos;
-                pos += a * NB2;
-            }
-        }
-    }
     __syncthreads();
     for (int w = 0; w < W; w++) {
         const int lo = base[w * kWaveExperts];
@@ -362,41 +388,86 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
 // 32w..32w+31 of the block, so SwiGLU pairs sit in the same lane; phase 2:
 // columns 64w..64w+63) and all M rows.
 //
-// Per 128-wide K chunk:
-//   A (activation E4M3 rows, gathered through sorted_pair in phase 1, the
-//     contiguous sorted rows of hq in phase 2) is staged in LDS, double
-//     buffered, row stride 144 B so that the 16 rows of an MFMA operand read
-//     spread over all banks; its per-row scales ride along.
-//   B (weights) goes HBM -> registers with one 16-byte load per lane per
-//     n-tile (the packed layout makes a wave's load one contiguous 1 KiB),
-//     kPrefetch chunks ahead; it is dequantised FP4 -> E4M3 in registers
-//     with the per-block LDS table and fed to the matrix cores directly.
-//     No wave shares a B fragment with another, so B never visits LDS.
-//   Each 16x16 output tile: P = MFMA over the chunk, acc = fma(xs*blk, P, acc).
+// Data movement: an NS-stage ring in LDS, one stage per 128-wide K chunk,
+// filled NS-1 chunks ahead by gfx950 direct-to-LDS loads (global_load_lds):
+//   B  the wave's 4 packed FP4 records (4 x 1 KiB, contiguous in HBM) and
+//      their E8M0 bytes (4 x 64 B), 16-byte / 4-byte per lane, fully coalesced;
+//   A  the tile's M activation rows (E4M3, 128 B each), gathered through
+//      sorted_pair in phase 1 or contiguous hq rows in phase 2; lanes write
+//      LDS contiguously, so rows are stored with their 16-byte segments
+//      XOR-swizzled by (row/2)%8, which lets the 16 rows of an MFMA operand
+//      read hit distinct banks;
+//   X  the per-row activation scales of the chunk.
+// Stages are consumed in order: wait for the stage's loads (s_waitcnt
+// vmcnt counted per wave), one barrier, issue the loads of the stage NS-1
+// ahead into the slot just freed, compute.  Each wave then dequantises its B
+// fragments FP4 -> E4M3 in registers (per-block LDS table) and, per m-tile,
+// P = MFMA over the chunk, acc = fma(xs*blk, P, acc).
 // ---------------------------------------------------------------------------
-constexpr int kPrefetch = 2;
-constexpr int kAStride = 144;
 constexpr int kLutBytes = 256 * 8;
 
-template <int PHASE, int MT>
+// Direct-to-LDS copies: each lane moves 16 (or 4) bytes from its own global
+// address to lds_base + lane*16 (lane*4); lds_base is wave-uniform (M0).  As
+// inline asm they are invisible to the compiler's wait insertion, which would
+// otherwise drain the whole pipeline before every LDS read; completion is
+// awaited explicitly with wait_vm<N>() (at most N of this wave's vector memory
+// operations still outstanding).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// wait until at most OPS*k operations are outstanding, k = 0..3 at run time
+template <int OPS>
+__device__ __forceinline__ void wait_stages(int k)
+{
+    if (k >= 3) wait_vm<3 * OPS>();
+    else if (k == 2) wait_vm<2 * OPS>();
+    else if (k == 1) wait_vm<OPS>();
+    else wait_vm<0>();
+}
+
+__host__ __device__ constexpr int ring_stages(int MT) { return MT == 1 ? 4 : MT == 8 ? 4 : 3; }
+
+template <int MT>
 struct TileLayout {
     static constexpr int M = 16 * MT;
-    static constexpr int A_BYTES = 2 * M * kAStride;
-    static constexpr int STAGE = PHASE == 1 ? M * 128 : 16 * 256 * 2;
-    static constexpr int A_REGION = ((A_BYTES > STAGE ? A_BYTES : STAGE) + 15) / 16 * 16;
-    static constexpr int XS_OFF = A_REGION;           // [2][M] float
-    static constexpr int RED_OFF = XS_OFF + 2 * M * 4; // [4][M] float
-    static constexpr int ROW_OFF = RED_OFF + 4 * M * 4; // [M] int
-    static constexpr int BYTES = ROW_OFF + M * 4;
+    static constexpr int NS = ring_stages(MT);
+    static constexpr int AI = M >= 32 ? M / 32 : 1;          // A loads per wave per stage
+    static constexpr int XI = 1;                             // X loads per wave per stage
+    static constexpr int OPS = 4 + 1 + AI + XI;              // loads per wave per stage
+    static constexpr int B_OFF = 0;                          // 16 records x 1 KiB
+    static constexpr int S_OFF = 16384;                      // 16 records x 64 B
+    static constexpr int A_OFF = 17408;                      // M rows x 128 B (swizzled)
+    static constexpr int X_OFF = A_OFF + M * 128;            // max(M, 64) floats
+    static constexpr int STAGE = X_OFF + (M > 64 ? M : 64) * 4;
+    static constexpr int RING = NS * STAGE;
+    static constexpr int RED_OFF = RING;                     // [4][M] float
+    static constexpr int ROW_OFF = RED_OFF + 4 * M * 4;      // [M] int
+    static constexpr int BLK_OFF = ROW_OFF + M * 4;          // [2][128] float: block scales per chunk
+    static constexpr int BYTES = BLK_OFF + 2 * 128 * 4;
+    static_assert(OPS * (NS - 2) < 64, "vmcnt range");
+    static_assert(STAGE >= M * 128 && STAGE >= 16 * 256 * 2, "epilogue staging fits in one stage");
 };
 
 template <int PHASE, int MT>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8_t* smem,
                                          const uint2* lut)
 {
-    using TL = TileLayout<PHASE, MT>;
+    using TL = TileLayout<MT>;
     constexpr int M = TL::M;
-    constexpr int ASEG = (M * 8 + 255) / 256;  // A 16-byte segments per thread per chunk
+    constexpr int NS = TL::NS;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -406,67 +477,77 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     const int K = PHASE == 1 ? a.H : a.I;
     const int N = PHASE == 1 ? a.I : a.H;
     const int C = K / 128;
+    const uint32_t ring = (uint32_t)(uintptr_t)smem;
 
-    float* xsb = reinterpret_cast<float*>(smem + TL::XS_OFF);
     float* red = reinterpret_cast<float*>(smem + TL::RED_OFF);
     int32_t* rowinfo = reinterpret_cast<int32_t*>(smem + TL::ROW_OFF);
 
-    // phase 1: token of each row (for the gather); phase 2: pair id (for the scatter)
+    // phase 1: token of each row (rows past the end repeat the last valid
+    // row's token: finite filler, never stored); phase 2: pair id or -1.
     for (int r = tid; r < M; r += 256) {
-        int v = -1;
-        if (r < rows) {
-            int p = a.sorted_pair[row0 + r];
-            v = PHASE == 1 ? p / a.topk : p;
-        }
-        rowinfo[r] = v;
+        const int p = a.sorted_pair[row0 + min(r, rows - 1)];
+        rowinfo[r] = PHASE == 1 ? p / a.topk : (r < rows ? p : -1);
+    }
+    // The tile's 128x128 block scales for every chunk, staged in LDS (the
+    // kernel writes global memory, so per-chunk reads would be vector loads
+    // whose waits would drain the load ring).  Phase 1: [0] gate, [1] up;
+    // phase 2: the two 128-column blocks of the tile.
+    float* blkv = reinterpret_cast<float*>(smem + TL::BLK_OFF);
+    for (int i = tid; i < 2 * C; i += 256) {
+        const int h = i / C, c = i % C;
+        const float* src = PHASE == 1
+            ? (h == 0 ? a.gate.blk : a.up.blk) + ((size_t)e * (a.I / 128) + nb) * C
+            : a.down.blk + ((size_t)e * (a.H / 128) + nb * 2 + h) * C;
+        blkv[h * 128 + c] = src[c];
     }
     __syncthreads();
 
-    // A staging: thread owns segments s = tid + 256*j (row s/8, 16-byte column s%8).
-    const uint8_t* asrc[ASEG];
-    const float* xsrc[ASEG];
-#pragma unroll
-    for (int j = 0; j < ASEG; j++) {
-        const int s = tid + 256 * j;
-        const int r = s >> 3;
-        asrc[j] = nullptr;
-        xsrc[j] = nullptr;
-        if (s < M * 8 && r < rows) {
-            if (PHASE == 1) {
-                const int t = rowinfo[r];
-                asrc[j] = a.xq + (size_t)t * a.H + (s & 7) * 16;
-                xsrc[j] = a.xs + (size_t)t * (a.H / 128);
-            } else {
-                const size_t R = (size_t)(row0 + r);
-                asrc[j] = a.hq + R * a.I + (s & 7) * 16;
-                xsrc[j] = a.hs + R * (a.I / 128);
-            }
-        }
-    }
-
-    // B sources: 4 n-tiles of this wave, pointing at chunk 0 of lane's slot.
+    // Sources of this lane's loads, at chunk 0.
     const uint8_t* bsrc[4];
-    const uint8_t* ssrc[4];
-    const float* blk0;
-    const float* blk1;
+    const uint8_t* ssrc;
     {
         const int NT16 = N / 16;
+        const uint8_t* srec[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const MatPtr& m = PHASE == 1 ? (j < 2 ? a.gate : a.up) : a.down;
             const int tile = PHASE == 1 ? nb * 8 + 2 * w + (j & 1) : nb * 16 + 4 * w + j;
             const size_t rec = ((size_t)e * NT16 + tile) * C;
             bsrc[j] = m.fp4 + rec * 1024 + lane * 16;
-            ssrc[j] = m.e8m0 + rec * 64 + lane;
+            srec[j] = m.e8m0 + rec * 64;
         }
-        if (PHASE == 1) {
-            blk0 = a.gate.blk + ((size_t)e * (a.I / 128) + nb) * C;
-            blk1 = a.up.blk + ((size_t)e * (a.I / 128) + nb) * C;
-        } else {
-            blk0 = a.down.blk + ((size_t)e * (a.H / 128) + nb * 2 + (w >> 1)) * C;
-            blk1 = blk0;
-        }
+        ssrc = srec[lane >> 4] + (lane & 15) * 4;
     }
+    const float* blk0 = blkv + (PHASE == 1 ? 0 : (w >> 1) * 128);
+    const float* blk1 = blkv + (PHASE == 1 ? 128 : (w >> 1) * 128);
+    const uint8_t* asrc[TL::AI];
+#pragma unroll
+    for (int i = 0; i < TL::AI; i++) {
+        const int blk = (i * 4 + w) % (M / 8);                // 1 KiB block = 8 rows
+        const int g = blk * 64 + lane;                        // segment of the tile
+        const int r = g >> 3;
+        const int seg = (g & 7) ^ ((r >> 1) & 7);             // global segment stored at position g&7
+        const int rc = min(r, rows - 1);
+        asrc[i] = (PHASE == 1 ? a.xq + (size_t)rowinfo[r] * a.H : a.hq + (size_t)(row0 + rc) * a.I) + seg * 16;
+    }
+    const float* xsrc;
+    {
+        const int r = ((w % ((M + 63) / 64)) * 64 + lane);
+        const int rc = min(r, rows - 1);
+        xsrc = PHASE == 1 ? a.xs + (size_t)rowinfo[min(r, M - 1)] * (a.H / 128)
+                          : a.hs + (size_t)(row0 + rc) * (a.I / 128);
+    }
+
+    auto issue = [&](int c, int slot) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(ring + slot * TL::STAGE);
+#pragma unroll
+        for (int j = 0; j < 4; j++) dma16(bsrc[j] + (size_t)c * 1024, st + TL::B_OFF + (w * 4 + j) * 1024);
+        dma4(ssrc + (size_t)c * 64, st + TL::S_OFF + w * 256);
+#pragma unroll
+        for (int i = 0; i < TL::AI; i++)
+            dma16(asrc[i] + (size_t)c * 128, st + TL::A_OFF + ((i * 4 + w) % (M / 8)) * 1024);
+        dma4(xsrc + c, st + TL::X_OFF + (w % ((M + 63) / 64)) * 256);
+    };
 
     v4f acc[MT][4];
 #pragma unroll
@@ -474,94 +555,51 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    uint4 bq[kPrefetch][4];
-    uint32_t bs[kPrefetch][4];
 #pragma unroll
-    for (int u = 0; u < kPrefetch; u++)
-        if (u < C)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                bq[u][j] = *reinterpret_cast<const uint4*>(bsrc[j] + (size_t)u * 1024);
-                bs[u][j] = ssrc[j][(size_t)u * 64];
-            }
+    for (int u = 0; u < NS - 1; u++)
+        if (u < C) issue(u, u);
 
-    uint4 areg[ASEG];
-    float xreg[ASEG];
-    auto load_a = [&](int c) {
+    for (int c = 0; c < C; c++) {
+        wait_stages<TL::OPS>(min(NS - 2, C - 1 - c));
+        __syncthreads();
+        if (c + NS - 1 < C) issue(c + NS - 1, (c + NS - 1) % NS);
+
+        const uint8_t* st = smem + (c % NS) * TL::STAGE;
+        v8i bf[4];
 #pragma unroll
-        for (int j = 0; j < ASEG; j++) {
-            if (asrc[j]) {
-                areg[j] = *reinterpret_cast<const uint4*>(asrc[j] + (size_t)c * 128);
-                xreg[j] = xsrc[j][c];
-            } else {
-                areg[j] = make_uint4(0, 0, 0, 0);
-                xreg[j] = 0.0f;
-            }
+        for (int j = 0; j < 4; j++) {
+            const uint4 q = *reinterpret_cast<const uint4*>(st + TL::B_OFF + (w * 4 + j) * 1024 + lane * 16);
+            const uint32_t sb = st[TL::S_OFF + w * 256 + j * 64 + lane];
+            bf[j] = dequant_slot(q, lut[sb]);
         }
-    };
-    auto store_a = [&](int buf) {
+        const float sb0 = blk0[c];
+        const float sb1 = blk1[c];
 #pragma unroll
-        for (int j = 0; j < ASEG; j++) {
-            const int s = tid + 256 * j;
-            if (s < M * 8) {
-                const int r = s >> 3;
-                *reinterpret_cast<uint4*>(smem + buf * M * kAStride + r * kAStride + (s & 7) * 16) = areg[j];
-                if ((s & 7) == 0) xsb[buf * M + r] = xreg[j];
-            }
-        }
-    };
-
-    load_a(0);
-    store_a(0);
-    __syncthreads();
-
-    for (int c0 = 0; c0 < C; c0 += kPrefetch) {
+        for (int i = 0; i < MT; i++) {
+            if (i * 16 < rows) {
+                const int r = i * 16 + (lane & 15);
+                const int sw = (r >> 1) & 7;
+                const int s0 = (lane >> 4) * 2;
+                const uint8_t* arow = st + TL::A_OFF + r * 128;
+                const uint4 a0 = *reinterpret_cast<const uint4*>(arow + ((s0 ^ sw) * 16));
+                const uint4 a1 = *reinterpret_cast<const uint4*>(arow + (((s0 + 1) ^ sw) * 16));
+                v8i af;
+                af[0] = (int)a0.x; af[1] = (int)a0.y; af[2] = (int)a0.z; af[3] = (int)a0.w;
+                af[4] = (int)a1.x; af[5] = (int)a1.y; af[6] = (int)a1.z; af[7] = (int)a1.w;
+                const float4 x4 = *reinterpret_cast<const float4*>(st + TL::X_OFF + (i * 16 + (lane >> 4) * 4) * 4);
+                const float s0v[4] = {x4.x * sb0, x4.y * sb0, x4.z * sb0, x4.w * sb0};
+                const float s1v[4] = {x4.x * sb1, x4.y * sb1, x4.z * sb1, x4.w * sb1};
 #pragma unroll
-        for (int u = 0; u < kPrefetch; u++) {
-            const int c = c0 + u;
-            if (c < C) {
-                const int buf = c & 1;
-                if (c + 1 < C) load_a(c + 1);
-                v8i bf[4];
+                for (int j = 0; j < 4; j++) {
+                    const v4f P = mfma_chunk(af, bf[j]);
+                    const float* sc = (PHASE == 1 && j >= 2) ? s1v : s0v;
 #pragma unroll
-                for (int j = 0; j < 4; j++) bf[j] = dequant_slot(bq[u][j], lut[bs[u][j] & 0xFFu]);
-                if (c + kPrefetch < C) {
-#pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        bq[u][j] = *reinterpret_cast<const uint4*>(bsrc[j] + (size_t)(c + kPrefetch) * 1024);
-                        bs[u][j] = ssrc[j][(size_t)(c + kPrefetch) * 64];
-                    }
+                    for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(sc[q], P[q], acc[i][j][q]);
                 }
-                const float sb0 = blk0[c];
-                const float sb1 = blk1[c];
-                const uint8_t* Ab = smem + buf * M * kAStride;
-                const float* Xb = xsb + buf * M;
-#pragma unroll
-                for (int i = 0; i < MT; i++) {
-                    if (i * 16 < rows) {
-                        const uint8_t* ap = Ab + (i * 16 + (lane & 15)) * kAStride + (lane >> 4) * 32;
-                        const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
-                        const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
-                        v8i af;
-                        af[0] = (int)a0.x; af[1] = (int)a0.y; af[2] = (int)a0.z; af[3] = (int)a0.w;
-                        af[4] = (int)a1.x; af[5] = (int)a1.y; af[6] = (int)a1.z; af[7] = (int)a1.w;
-                        const float4 x4 = *reinterpret_cast<const float4*>(Xb + i * 16 + (lane >> 4) * 4);
-                        const float s0[4] = {x4.x * sb0, x4.y * sb0, x4.z * sb0, x4.w * sb0};
-                        const float s1[4] = {x4.x * sb1, x4.y * sb1, x4.z * sb1, x4.w * sb1};
-#pragma unroll
-                        for (int j = 0; j < 4; j++) {
-                            const v4f P = mfma_chunk(af, bf[j]);
-                            const float* sc = (PHASE == 1 && j >= 2) ? s1 : s0;
-#pragma unroll
-                            for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(sc[q], P[q], acc[i][j][q]);
-                        }
-                    }
-                }
-                if (c + 1 < C) store_a((c + 1) & 1);
-                __syncthreads();
             }
         }
     }
+    __syncthreads();   // every wave is done with the ring: its first stage becomes the staging area
 
     if (PHASE == 1) {
         // h = SiLU(g) * u, then E4M3 per (row, 128 columns of h): the amax of a
@@ -790,21 +828,27 @@ static inline unsigned blocks_for(size_t n, int per) { return (unsigned)((n + pe
 
 hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
                         const float* bias, int mode, const int64_t* token_ids,
-                        int32_t* ids, float* w, hipStream_t s)
+                        int32_t* ids, float* w, float* z, hipStream_t s)
 {
     if (mode == 1) {
         hipLaunchKernelGGL(k_route_hash, dim3(blocks_for(T, 256)), dim3(256), 0, s, T, E, k,
                            token_ids, ids, w);
-    } else if (T <= 1024) {
-        hipLaunchKernelGGL(k_route_learned<1>, dim3(T), dim3(256), (size_t)E * 4, s, T, H, E, k,
-                           x, wr, bias, ids, w);
-    } else if (T <= 4096) {
-        hipLaunchKernelGGL(k_route_learned<4>, dim3(blocks_for(T, 4)), dim3(256), (size_t)4 * E * 4, s,
-                           T, H, E, k, x, wr, bias, ids, w);
-    } else {
-        hipLaunchKernelGGL(k_route_learned<16>, dim3(blocks_for(T, 16)), dim3(256), (size_t)16 * E * 4,
-                           s, T, H, E, k, x, wr, bias, ids, w);
+        return hipGetLastError();
     }
+    // experts per wave: enough waves to fill the chip at small T, more reuse of
+    // each x row at large T
+    const int tg = (T + 63) / 64;
+    if (tg * E >= 256 * 4 * 8) {
+        hipLaunchKernelGGL(k_route_logits<8>, dim3(tg, blocks_for(E, 32)), dim3(256), 0, s, T, H, E, x, wr,
+                           bias, z);
+    } else if (tg * E >= 256 * 4 * 2) {
+        hipLaunchKernelGGL(k_route_logits<2>, dim3(tg, blocks_for(E, 8)), dim3(256), 0, s, T, H, E, x, wr,
+                           bias, z);
+    } else {
+        hipLaunchKernelGGL(k_route_logits<1>, dim3(tg, blocks_for(E, 4)), dim3(256), 0, s, T, H, E, x, wr,
+                           bias, z);
+    }
+    hipLaunchKernelGGL(k_route_select, dim3(blocks_for(T, 4)), dim3(256), 0, s, T, E, k, z, ids, w);
     return hipGetLastError();
 }
 
@@ -836,11 +880,24 @@ hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue, 
     return hipGetLastError();
 }
 
+// Kernels whose LDS exceeds the default 64 KiB limit must opt in once.
+template <typename F>
+static hipError_t allow_lds(F* kernel, size_t bytes, bool& done)
+{
+    if (done) return hipSuccess;
+    hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    done = r == hipSuccess;
+    return r;
+}
+
 template <int PHASE, int MT>
 static hipError_t launch_ffn_t(const FfnArgs& a, hipStream_t s)
 {
+    static bool lds_ok = false;
     const int NB = PHASE == 1 ? a.I / 128 : a.H / 256;
-    const size_t lds = kLutBytes + TileLayout<PHASE, MT>::BYTES;
+    const size_t lds = kLutBytes + TileLayout<MT>::BYTES;
+    if (allow_lds(k_ffn<PHASE, MT>, lds, lds_ok) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_ffn<PHASE, MT>), dim3((unsigned)a.n_mt_bound * NB), dim3(256), lds, s, a, NB);
     return hipGetLastError();
 }
@@ -863,13 +920,14 @@ hipError_t launch_ffn(int phase, int MT, const FfnArgs& a, hipStream_t s)
 template <int MT>
 static size_t persistent_lds()
 {
-    const size_t b1 = TileLayout<1, MT>::BYTES, b2 = TileLayout<2, MT>::BYTES;
-    return kLutBytes + (b1 > b2 ? b1 : b2);
+    return kLutBytes + TileLayout<MT>::BYTES;
 }
 
 template <int MT>
 static int persistent_occupancy()
 {
+    static bool lds_ok = false;
+    allow_lds(k_ffn_persistent<MT>, persistent_lds<MT>(), lds_ok);
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_ffn_persistent<MT>, 256, persistent_lds<MT>()) !=
         hipSuccess)
@@ -890,6 +948,8 @@ int persistent_blocks_per_cu(int MT)
 template <int MT>
 static hipError_t launch_persistent_t(const FfnArgs& a, int grid, hipStream_t s)
 {
+    static bool lds_ok = false;
+    if (allow_lds(k_ffn_persistent<MT>, persistent_lds<MT>(), lds_ok) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_ffn_persistent<MT>, dim3(grid), dim3(256), persistent_lds<MT>(), s, a);
     return hipGetLastError();
 }

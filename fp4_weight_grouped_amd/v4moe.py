@@ -62,7 +62,7 @@ def lib():
         L.moe_workspace_bytes.restype = _sz
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
-        L.moe_route.argtypes = [_DP, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
+        L.moe_route.argtypes = [_DP, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_permute.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_expert_ffn.argtypes = [_DP, _vp, _vp, _vp, _vp, ctypes.POINTER(ExpertsC), _vp, _vp, _sz, _vp]
         L.moe_combine.argtypes = [_DP, _vp, _vp, _vp, _vp]
@@ -133,9 +133,10 @@ def moe_workspace_bytes(d: Dims) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(d)))
 
 
-def moe_route(d: Dims, x, w_router, bias, mode, token_ids, topk_ids, topk_w):
+def moe_route(d: Dims, x, w_router, bias, mode, token_ids, topk_ids, topk_w, workspace):
     _check(lib().moe_route(ctypes.byref(d), _p(x), _p(w_router), _p(bias), mode, _p(token_ids),
-                           _p(topk_ids), _p(topk_w), _stream()))
+                           _p(topk_ids), _p(topk_w), _p(workspace),
+                           0 if workspace is None else workspace.numel(), _stream()))
 
 
 def moe_permute(d: Dims, x, topk_ids, expert_offsets, sorted_pair, pair_pos, xq, xs, workspace):
@@ -257,7 +258,7 @@ class MoELayer:
         y = torch.empty((max(P, 1), self.H), dtype=torch.int16, device=dev)
         out = torch.empty((T, self.H), dtype=torch.int16, device=dev)
         ws = self.workspace(T)
-        moe_route(d, x, self.w_router, bias, mode, token_ids, ids, w)
+        moe_route(d, x, self.w_router, bias, mode, token_ids, ids, w, ws)
         moe_permute(d, x, ids, off, sp, pp, xq, xs, ws)
         moe_expert_ffn(d, xq, xs, off, sp, self.experts, y, ws)
         moe_combine(d, y, w, out)

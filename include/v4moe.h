@@ -95,9 +95,10 @@ typedef struct {
 #define V4MOE_ROUTE_LEARNED 0
 #define V4MOE_ROUTE_HASH    1
 
-/* Workspace bytes needed by moe_permute, moe_expert_ffn and
+/* Workspace bytes needed by moe_route, moe_permute, moe_expert_ffn and
  * moe_layer_forward for these dimensions (host-only, pure).  Returns 0 for
- * invalid dims. */
+ * invalid dims.  The workspace is device memory owned by the caller,
+ * 16-byte aligned; its contents need no initialisation. */
 size_t moe_workspace_bytes(const v4moe_dims* d);
 
 /* Routing (P2, DeepSeekMoE notes: the affinity is sqrt(softplus(.)) in place
@@ -115,10 +116,12 @@ size_t moe_workspace_bytes(const v4moe_dims* d);
  *   token_ids int64 [T] or NULL (NULL: id = t); hash mode only.
  *   topk_ids  int32 [T][topk]   (out)
  *   topk_w    fp32  [T][topk]   (out)
- * x, w_router: 16-byte aligned. */
+ *   workspace moe_workspace_bytes(d) bytes (learned mode; may be NULL in hash mode)
+ * x, w_router, workspace: 16-byte aligned. */
 int moe_route(const v4moe_dims* d, const uint16_t* x, const float* w_router,
               const float* bias, int32_t mode, const int64_t* token_ids,
-              int32_t* topk_ids, float* topk_w, void* stream);
+              int32_t* topk_ids, float* topk_w, void* workspace, size_t ws_bytes,
+              void* stream);
 
 /* Dispatch on one GPU (P1 §1.1-1.2: the FP8 dispatch stage becomes a local
  * expert-sorted permutation; P1 §1.4: FP8 dispatch payload).

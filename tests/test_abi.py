@@ -49,11 +49,12 @@ def test_error_paths_without_device():
     p = ctypes.c_void_p(4096)          # aligned, never dereferenced: every call below fails first
     mis = ctypes.c_void_p(4097)
     ex = v4moe.ExpertsC(v4moe.Mat(4096, 4096, 4096), v4moe.Mat(4096, 4096, 4096), v4moe.Mat(4096, 4096, 4096))
-    assert L.moe_route(ctypes.byref(bd), p, p, None, 0, None, p, p, None) == -2
-    assert L.moe_route(ctypes.byref(d), p, p, None, 2, None, p, p, None) == -2
-    assert L.moe_route(ctypes.byref(d), None, p, None, 0, None, p, p, None) == -1
-    assert L.moe_route(ctypes.byref(d), mis, p, None, 0, None, p, p, None) == -3
-    assert L.moe_route(ctypes.byref(v4moe.dims(0, 256, 128, 8, 2)), p, p, None, 0, None, p, p, None) == 0
+    assert L.moe_route(ctypes.byref(bd), p, p, None, 0, None, p, p, p, 1 << 30, None) == -2
+    assert L.moe_route(ctypes.byref(d), p, p, None, 2, None, p, p, p, 1 << 30, None) == -2
+    assert L.moe_route(ctypes.byref(d), None, p, None, 0, None, p, p, p, 1 << 30, None) == -1
+    assert L.moe_route(ctypes.byref(d), mis, p, None, 0, None, p, p, p, 1 << 30, None) == -3
+    assert L.moe_route(ctypes.byref(d), p, p, None, 0, None, p, p, p, 10, None) == -4
+    assert L.moe_route(ctypes.byref(v4moe.dims(0, 256, 128, 8, 2)), p, p, None, 0, None, p, p, None, 0, None) == 0
     assert L.moe_permute(ctypes.byref(d), p, p, p, p, p, p, p, p, 10, None) == -4
     assert L.moe_permute(ctypes.byref(d), p, p, None, p, p, p, p, p, 1 << 30, None) == -1
     assert L.moe_permute(ctypes.byref(d), p, None, p, p, p, p, p, p, 1 << 30, None) == -1
