@@ -16,6 +16,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",                      # every fused multiply-add is written out
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",     # MFMA results in VGPRs (no accvgpr copies)
     "-fvisibility=hidden",
 ]
 

@@ -58,6 +58,9 @@ bool dims_ok(const v4moe_dims* d)
     if (d->E < 1 || d->E > 1024) return false;
     if (d->topk < 1 || d->topk > 16 || d->topk > d->E) return false;
     if ((int64_t)d->T * d->topk > (1ll << 24)) return false;
+    // the kernels address activations and intermediates with 32-bit offsets
+    if ((int64_t)d->T * d->H >= (1ll << 31)) return false;
+    if ((int64_t)d->T * d->topk * d->I >= (1ll << 31)) return false;
     return true;
 }
 
@@ -67,6 +70,10 @@ struct Layout {
     size_t total;
     int MT, n_mt_bound, nblk;
 };
+
+// One 128-byte line (or more) per row of h scales, so that rows of different
+// m-tiles never share a cache line.
+inline int hs_stride(int I) { return ((I / 128) + 31) / 32 * 32; }
 
 Layout layout(const v4moe_dims* d)
 {
@@ -91,7 +98,7 @@ Layout layout(const v4moe_dims* d)
     L.done1 = take((size_t)L.n_mt_bound * 4);
     L.queue = take((size_t)L.n_mt_bound * (NB1 + NB2) * 4);
     L.hq = take(P * I);
-    L.hs = take(P * (I / 128) * 4);
+    L.hs = take(P * hs_stride(d->I) * 4);
     L.y = take(P * H * 2);
     L.total = o;
     return L;
@@ -118,6 +125,7 @@ FfnArgs ffn_args(const v4moe_dims* d, const Layout& L, uint8_t* ws, const uint8_
     a.gate = mp(w->gate); a.up = mp(w->up); a.down = mp(w->down);
     a.hq = ws + L.hq;
     a.hs = reinterpret_cast<float*>(ws + L.hs);
+    a.hs_stride = hs_stride(d->I);
     a.y = y;
     a.mt_expert = reinterpret_cast<int32_t*>(ws + L.mt_expert);
     a.mt_row0 = reinterpret_cast<int32_t*>(ws + L.mt_row0);
@@ -136,14 +144,20 @@ int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws,
     hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return V4MOE_ELAUNCH;
-    if (launch_build_tiles(d->E, L.MT, NB1, NB2, persistent ? 1 : 0, a,
+    int per = di->persist_per_cu[L.MT];
+    int grid = di->cus * (per > 0 ? per : 1);
+    // Scheduling lag in waves: enough linear1 tiles between a wave's linear1 and
+    // linear2 entries to keep every running block busy meanwhile (estimate from
+    // the mean number of m-tiles per expert).
+    const double mt_per_expert = (double)d->T * d->topk / d->E / (16.0 * L.MT) + 0.5;
+    const double items_per_wave = kWaveExperts * (mt_per_expert < 1.0 ? 1.0 : mt_per_expert) * NB1;
+    const int lag = 1 + (int)(1.5 * grid / items_per_wave);
+    if (launch_build_tiles(d->E, L.MT, NB1, NB2, persistent ? 1 : 0, lag, a,
                            reinterpret_cast<int32_t*>(ws + L.mt_expert),
                            reinterpret_cast<int32_t*>(ws + L.mt_row0),
                            reinterpret_cast<uint32_t*>(ws + L.queue), s) != hipSuccess)
         return V4MOE_ELAUNCH;
     if (persistent) {
-        int per = di->persist_per_cu[L.MT];
-        int grid = di->cus * (per > 0 ? per : 1);
         const int max_items = L.n_mt_bound * (NB1 + NB2);
         if (grid > max_items) grid = max_items;
         if (launch_ffn_persistent(L.MT, a, grid, s) != hipSuccess) return V4MOE_ELAUNCH;

@@ -29,7 +29,8 @@ struct FfnArgs {
     const int32_t* sorted_pair;// [T*topk]
     MatPtr gate, up, down;
     uint8_t* hq;               // [T*topk][I] E4M3, rows in expert-sorted order
-    float* hs;                 // [T*topk][I/128]
+    float* hs;                 // [T*topk][hs_stride], first I/128 used
+    int hs_stride;             // floats per hs row: I/128 rounded up to a 128-byte line
     uint16_t* y;               // [T*topk][H] bf16, row = pair id
     const int32_t* mt_expert;  // [n_mt_bound] expert of each m-tile
     const int32_t* mt_row0;    // [n_mt_bound] first sorted row of each m-tile
@@ -44,7 +45,7 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
 hipError_t launch_quant_x(int T, int H, const uint16_t* x, uint8_t* xq, float* xs, hipStream_t s);
 hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos, int32_t* hist, hipStream_t s);
-hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue,
+hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue, int lag,
                               const FfnArgs& a, int32_t* mt_expert, int32_t* mt_row0,
                               uint32_t* queue, hipStream_t s);
 hipError_t launch_ffn(int phase, int MT, const FfnArgs& a, hipStream_t s);

@@ -312,11 +312,13 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __
 // m-tile list and persistent work queue.
 // m-tile = up to M = 16*MT consecutive sorted rows of one expert.  The queue
 // is ordered by scheduling waves of kWaveExperts experts (P1 §1.2, Fig. 5):
-// linear1 of wave 0, linear1 of wave 1, linear2 of wave 0, linear1 of wave 2,
-// linear2 of wave 1, ..., linear2 of the last wave.  Entry = phase<<31 |
-// mtile<<8 | n-block.  Also clears the counters used by the persistent kernel.
+// linear1 of waves 0..D-1, then for w >= D linear1 of wave w followed by
+// linear2 of wave w-D, then linear2 of the last D waves.  The lag D is chosen
+// by the host so that the linear1 tiles of a wave have been taken by running
+// blocks well before its linear2 tiles are, so linear2 rarely waits.  Entry =
+// phase<<31 | mtile<<8 | n-block.  Also clears the persistent kernel's counters.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int NB2, int build_queue,
+__global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int NB2, int build_queue, int D,
                                                       const int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ mt_expert,
                                                       int32_t* __restrict__ mt_row0,
@@ -340,23 +342,21 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
     }
     for (int i = tid; i < total; i += 1024) done1[i] = 0;
     const int W = (E + kWaveExperts - 1) / kWaveExperts;
-    // Segment i of the queue: 0 = linear1 of wave 0; 2w-1 = linear1 of wave w
-    // and 2w = linear2 of wave w-1 (w >= 1); 2W-1 = linear2 of wave W-1.
-    int len = 0;
+    D = max(1, min(D, W));
+    // Segment order: linear1 of wave i for i < D; then, for step s = D..W-1,
+    // linear1 of wave s and linear2 of wave s-D; then linear2 of waves W-D..W-1.
+    // Segment index i in 0..2W-1 -> (phase, wave).
+    int len = 0, ph = 0, wv = 0;
     if (build_queue && tid < 2 * W) {
         const int i = tid;
-        const int ph = (i == 0) ? 0 : (i == 2 * W - 1) ? 1 : ((i & 1) ? 0 : 1);
-        const int wv = (i == 0) ? 0 : (i == 2 * W - 1) ? W - 1 : (ph == 0 ? (i + 1) / 2 : i / 2 - 1);
+        if (i < D) { ph = 0; wv = i; }
+        else if (i < 2 * W - D) { const int s2 = i - D; ph = s2 & 1; wv = ph ? (D + s2 / 2) - D : D + s2 / 2; }
+        else { ph = 1; wv = W - D + (i - (2 * W - D)); }
         const int a = base[min(E, (wv + 1) * kWaveExperts)] - base[wv * kWaveExperts];
         len = a * (ph ? NB2 : NB1);
     }
     const int start = block_exclusive_scan(len, &qlen_s);
-    if (build_queue && tid < 2 * W) {
-        const int i = tid;
-        const int ph = (i == 0) ? 0 : (i == 2 * W - 1) ? 1 : ((i & 1) ? 0 : 1);
-        const int wv = (i == 0) ? 0 : (i == 2 * W - 1) ? W - 1 : (ph == 0 ? (i + 1) / 2 : i / 2 - 1);
-        segpos[2 * wv + ph] = start;
-    }
+    if (build_queue && tid < 2 * W) segpos[2 * wv + ph] = start;
     if (tid == 0) {
         ctrl[0] = total;
         ctrl[1] = 0;
@@ -406,6 +406,19 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
 // ---------------------------------------------------------------------------
 constexpr int kLutBytes = 256 * 8;
 
+// Stores that another XCD may read within the same launch: agent-scope
+// (relaxed) atomic stores, which on gfx950 write through the local L2.
+__device__ __forceinline__ void store_coherent(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint8_t* p, uint4 v)
+{
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    __hip_atomic_store(q, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Direct-to-LDS copies: each lane moves 16 (or 4) bytes from its own global
 // address to lds_base + lane*16 (lane*4); lds_base is wave-uniform (M0).  As
 // inline asm they are invisible to the compiler's wait insertion, which would
@@ -421,6 +434,28 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+// Same copies with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane
+// byte offset (one VGPR instead of two per address).
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
+}
+// A value known to be equal in every lane, moved to scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uniform(T* p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
 template <int N>
 __device__ __forceinline__ void wait_vm()
@@ -471,9 +506,9 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int e = a.mt_expert[mt];
-    const int row0 = a.mt_row0[mt];
-    const int rows = min(M, a.offsets[e + 1] - row0);
+    const int e = uniform(a.mt_expert[mt]);
+    const int row0 = uniform(a.mt_row0[mt]);
+    const int rows = uniform(min(M, a.offsets[e + 1] - row0));
     const int K = PHASE == 1 ? a.H : a.I;
     const int N = PHASE == 1 ? a.I : a.H;
     const int C = K / 128;
@@ -502,9 +537,10 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     }
     __syncthreads();
 
-    // Sources of this lane's loads, at chunk 0.
-    const uint8_t* bsrc[4];
-    const uint8_t* ssrc;
+    // Sources of this lane's loads at chunk 0: wave-uniform bases plus 32-bit
+    // per-lane byte offsets (the dimension checks keep every offset < 2^31).
+    const uint8_t* bbase[4];
+    const uint8_t* sptr;
     {
         const int NT16 = N / 16;
         const uint8_t* srec[4];
@@ -513,14 +549,16 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
             const MatPtr& m = PHASE == 1 ? (j < 2 ? a.gate : a.up) : a.down;
             const int tile = PHASE == 1 ? nb * 8 + 2 * w + (j & 1) : nb * 16 + 4 * w + j;
             const size_t rec = ((size_t)e * NT16 + tile) * C;
-            bsrc[j] = m.fp4 + rec * 1024 + lane * 16;
+            bbase[j] = uniform(m.fp4 + rec * 1024);
             srec[j] = m.e8m0 + rec * 64;
         }
-        ssrc = srec[lane >> 4] + (lane & 15) * 4;
+        sptr = srec[lane >> 4] + (lane & 15) * 4;
     }
+    const uint32_t boff = lane * 16;
     const float* blk0 = blkv + (PHASE == 1 ? 0 : (w >> 1) * 128);
     const float* blk1 = blkv + (PHASE == 1 ? 128 : (w >> 1) * 128);
-    const uint8_t* asrc[TL::AI];
+    const uint8_t* abase = uniform(PHASE == 1 ? a.xq : a.hq);
+    uint32_t aoff[TL::AI];
 #pragma unroll
     for (int i = 0; i < TL::AI; i++) {
         const int blk = (i * 4 + w) % (M / 8);                // 1 KiB block = 8 rows
@@ -528,25 +566,27 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         const int r = g >> 3;
         const int seg = (g & 7) ^ ((r >> 1) & 7);             // global segment stored at position g&7
         const int rc = min(r, rows - 1);
-        asrc[i] = (PHASE == 1 ? a.xq + (size_t)rowinfo[r] * a.H : a.hq + (size_t)(row0 + rc) * a.I) + seg * 16;
+        aoff[i] = (PHASE == 1 ? (uint32_t)rowinfo[r] * (uint32_t)a.H : (uint32_t)(row0 + rc) * (uint32_t)a.I) +
+                  seg * 16;
     }
-    const float* xsrc;
+    const float* xbase = uniform(PHASE == 1 ? a.xs : a.hs);
+    uint32_t xoff;
     {
         const int r = ((w % ((M + 63) / 64)) * 64 + lane);
         const int rc = min(r, rows - 1);
-        xsrc = PHASE == 1 ? a.xs + (size_t)rowinfo[min(r, M - 1)] * (a.H / 128)
-                          : a.hs + (size_t)(row0 + rc) * (a.I / 128);
+        xoff = 4u * (PHASE == 1 ? (uint32_t)rowinfo[min(r, M - 1)] * (uint32_t)(a.H / 128)
+                                : (uint32_t)(row0 + rc) * (uint32_t)a.hs_stride);
     }
 
     auto issue = [&](int c, int slot) {
         const uint32_t st = __builtin_amdgcn_readfirstlane(ring + slot * TL::STAGE);
 #pragma unroll
-        for (int j = 0; j < 4; j++) dma16(bsrc[j] + (size_t)c * 1024, st + TL::B_OFF + (w * 4 + j) * 1024);
-        dma4(ssrc + (size_t)c * 64, st + TL::S_OFF + w * 256);
+        for (int j = 0; j < 4; j++) dma16s(bbase[j], boff + c * 1024, st + TL::B_OFF + (w * 4 + j) * 1024);
+        dma4(sptr + (size_t)c * 64, st + TL::S_OFF + w * 256);
 #pragma unroll
         for (int i = 0; i < TL::AI; i++)
-            dma16(asrc[i] + (size_t)c * 128, st + TL::A_OFF + ((i * 4 + w) % (M / 8)) * 1024);
-        dma4(xsrc + c, st + TL::X_OFF + (w % ((M + 63) / 64)) * 256);
+            dma16s(abase, aoff[i] + c * 128, st + TL::A_OFF + ((i * 4 + w) % (M / 8)) * 1024);
+        dma4s(xbase, xoff + c * 4, st + TL::X_OFF + (w % ((M + 63) / 64)) * 256);
     };
 
     v4f acc[MT][4];
@@ -574,28 +614,31 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         }
         const float sb0 = blk0[c];
         const float sb1 = blk1[c];
+        // All m-tiles are computed (rows past the end hold finite filler and are
+        // never stored), so the four independent MFMAs of every m-tile can be
+        // in flight before their results are promoted.
 #pragma unroll
         for (int i = 0; i < MT; i++) {
-            if (i * 16 < rows) {
-                const int r = i * 16 + (lane & 15);
-                const int sw = (r >> 1) & 7;
-                const int s0 = (lane >> 4) * 2;
-                const uint8_t* arow = st + TL::A_OFF + r * 128;
-                const uint4 a0 = *reinterpret_cast<const uint4*>(arow + ((s0 ^ sw) * 16));
-                const uint4 a1 = *reinterpret_cast<const uint4*>(arow + (((s0 + 1) ^ sw) * 16));
-                v8i af;
-                af[0] = (int)a0.x; af[1] = (int)a0.y; af[2] = (int)a0.z; af[3] = (int)a0.w;
-                af[4] = (int)a1.x; af[5] = (int)a1.y; af[6] = (int)a1.z; af[7] = (int)a1.w;
-                const float4 x4 = *reinterpret_cast<const float4*>(st + TL::X_OFF + (i * 16 + (lane >> 4) * 4) * 4);
-                const float s0v[4] = {x4.x * sb0, x4.y * sb0, x4.z * sb0, x4.w * sb0};
-                const float s1v[4] = {x4.x * sb1, x4.y * sb1, x4.z * sb1, x4.w * sb1};
+            const int r = i * 16 + (lane & 15);
+            const int sw = (r >> 1) & 7;
+            const int s0 = (lane >> 4) * 2;
+            const uint8_t* arow = st + TL::A_OFF + r * 128;
+            const uint4 a0 = *reinterpret_cast<const uint4*>(arow + ((s0 ^ sw) * 16));
+            const uint4 a1 = *reinterpret_cast<const uint4*>(arow + (((s0 + 1) ^ sw) * 16));
+            v8i af;
+            af[0] = (int)a0.x; af[1] = (int)a0.y; af[2] = (int)a0.z; af[3] = (int)a0.w;
+            af[4] = (int)a1.x; af[5] = (int)a1.y; af[6] = (int)a1.z; af[7] = (int)a1.w;
+            v4f P[4];
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const v4f P = mfma_chunk(af, bf[j]);
-                    const float* sc = (PHASE == 1 && j >= 2) ? s1v : s0v;
+            for (int j = 0; j < 4; j++) P[j] = mfma_chunk(af, bf[j]);
+            const float4 x4 = *reinterpret_cast<const float4*>(st + TL::X_OFF + (i * 16 + (lane >> 4) * 4) * 4);
+            const float s0v[4] = {x4.x * sb0, x4.y * sb0, x4.z * sb0, x4.w * sb0};
+            const float s1v[4] = {x4.x * sb1, x4.y * sb1, x4.z * sb1, x4.w * sb1};
 #pragma unroll
-                    for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(sc[q], P[q], acc[i][j][q]);
-                }
+            for (int j = 0; j < 4; j++) {
+                const float* sc = (PHASE == 1 && j >= 2) ? s1v : s0v;
+#pragma unroll
+                for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(sc[q], P[j][q], acc[i][j][q]);
             }
         }
     }
@@ -635,14 +678,14 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
                 for (int j = 0; j < 2; j++)
                     stage[r * 128 + 32 * w + 16 * j + (lane & 15)] = (uint8_t)e4m3_rne_sat(hv[i][j][q] / s);
                 if (w == 0 && (lane & 15) == 0 && r < rows)
-                    a.hs[(size_t)(row0 + r) * (a.I / 128) + nb] = s;
+                    store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb, s);
             }
         __syncthreads();
         for (int s = tid; s < M * 8; s += 256) {
             const int r = s >> 3;
             if (r < rows)
-                *reinterpret_cast<uint4*>(a.hq + (size_t)(row0 + r) * a.I + nb * 128 + (s & 7) * 16) =
-                    *reinterpret_cast<const uint4*>(stage + r * 128 + (s & 7) * 16);
+                store_coherent(a.hq + (size_t)(row0 + r) * a.I + nb * 128 + (s & 7) * 16,
+                               *reinterpret_cast<const uint4*>(stage + r * 128 + (s & 7) * 16));
         }
         __syncthreads();
     } else {
@@ -711,16 +754,21 @@ __global__ __launch_bounds__(256) void k_ffn_persistent(FfnArgs a)
         const int mt = (int)((it >> 8) & 0x7FFFFFu);
         const int nb = (int)(it & 0xFFu);
         if ((it >> 31) == 0) {
+            // h and its scales were written with agent-coherent stores (through
+            // this XCD's L2); once every wave has them acknowledged, one counter
+            // increment publishes the tile.  No L2 write-back is needed.
             ffn_tile<1, MT>(a, mt, nb, smem + kLutBytes, lut);
-            __threadfence();
+            wait_vm<0>();
             __syncthreads();
-            if (threadIdx.x == 0) atomicAdd(&a.done1[mt], 1);
-        } else {
             if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(&a.done1[mt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            if (threadIdx.x == 0) {
                 while (__hip_atomic_load(&a.done1[mt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < NB1)
                     __builtin_amdgcn_s_sleep(2);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // drop any stale cached lines
+            }
             __syncthreads();
-            (void)__hip_atomic_load(&a.done1[mt], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
             ffn_tile<2, MT>(a, mt, nb, smem + kLutBytes, lut);
         }
     }
@@ -872,10 +920,10 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offs
     return hipGetLastError();
 }
 
-hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue, const FfnArgs& a,
+hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue, int lag, const FfnArgs& a,
                               int32_t* mt_expert, int32_t* mt_row0, uint32_t* queue, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, E, 16 * MT, NB1, NB2, build_queue,
+    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, E, 16 * MT, NB1, NB2, build_queue, lag,
                        a.offsets, mt_expert, mt_row0, a.ctrl, a.done1, queue);
     return hipGetLastError();
 }

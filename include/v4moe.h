@@ -49,9 +49,9 @@ extern "C" {
 #define V4MOE_ESCALE          -6   /* sub-block scale outside the lossless window       */
 #define V4MOE_EDEVICE         -7   /* current device is not a gfx950                    */
 
-/* Layer dimensions.  Requirements: 0 <= T; T*topk <= 2^24; H a multiple of
- * 256 with 256 <= H <= 16384; I a multiple of 128 with 128 <= I <= 16384;
- * 1 <= E <= 1024; 1 <= topk <= min(E, 16). */
+/* Layer dimensions.  Requirements: 0 <= T; T*topk <= 2^24; T*H < 2^31;
+ * T*topk*I < 2^31; H a multiple of 256 with 256 <= H <= 16384; I a multiple
+ * of 128 with 128 <= I <= 16384; 1 <= E <= 1024; 1 <= topk <= min(E, 16). */
 typedef struct {
     int32_t T;      /* tokens in the batch                          */
     int32_t H;      /* hidden size (linear1 K, linear2 N)           */
