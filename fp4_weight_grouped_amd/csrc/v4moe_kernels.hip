@@ -31,11 +31,15 @@ namespace v4moe {
 // Routing
 // ---------------------------------------------------------------------------
 
-// Router logits.  Lane = token, wave = ES consecutive experts, so every
-// router weight W_r[h][e] a wave needs is wave-uniform (scalar loads, shared by
-// the 64 tokens) and each lane streams its own token row of x.  Each lane
-// runs ES independent fp32 fma chains over h ascending from +0; the optional
-// bias is one fp32 add afterwards.  z is [T][E].
+// Router logits.  Lane = token (64 tokens per block), wave w = experts
+// eb0 + w*ES .. +ES (EB = 4*ES per block).  The block's slice of W_r is staged
+// through LDS 256 rows of h at a time (double buffered, the next slice loaded
+// into registers while the current one is used); every wave reads its ES
+// weights of a row with one broadcast LDS read, and each lane streams its own
+// row of x.  Each lane runs ES independent fp32 fma chains over h ascending
+// from +0; the optional bias is one fp32 add afterwards.  z is [T][E].
+// Needs E % 4 == 0 (16-byte rows of the weight slice); otherwise
+// k_route_logits_any is used.
 template <int ES>
 __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
                                                       const uint16_t* __restrict__ x,
@@ -43,40 +47,96 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
                                                       const float* __restrict__ bias,
                                                       float* __restrict__ z)
 {
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int EB = 4 * ES;
+    constexpr int HC = 256;
+    constexpr int F4 = HC * EB / 4;          // float4 per stage
+    constexpr int LD = F4 / 256;             // float4 loads per thread per stage
+    __shared__ float4 wt[2][F4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = blockIdx.x * 64 + lane;
-    const int eg = (blockIdx.y * 4 + w) * ES;
-    if (eg >= E) return;
-    const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)min(t, T - 1) * H);
-    int col[ES];
+    const int eb0 = blockIdx.y * EB;
+    const int nst = H / HC;
+    const float* wsrc[LD];
 #pragma unroll
-    for (int j = 0; j < ES; j++) col[j] = min(eg + j, E - 1);
+    for (int i = 0; i < LD; i++) {
+        const int f = tid + 256 * i;
+        const int row = f / (EB / 4), c4 = f % (EB / 4);
+        wsrc[i] = wr + (size_t)row * E + min(eb0 + c4 * 4, E - 4);
+    }
+    float4 nxt[LD];
+#pragma unroll
+    for (int i = 0; i < LD; i++) nxt[i] = *reinterpret_cast<const float4*>(wsrc[i]);
+#pragma unroll
+    for (int i = 0; i < LD; i++) wt[0][tid + 256 * i] = nxt[i];
+    __syncthreads();
+
+    const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)min(t, T - 1) * H);
     float acc[ES];
 #pragma unroll
     for (int j = 0; j < ES; j++) acc[j] = 0.0f;
-#pragma unroll 2
-    for (int h = 0; h < H; h += 8) {
-        const uint4 xx = xp[h / 8];
-        const uint32_t q[4] = {xx.x, xx.y, xx.z, xx.w};
+    for (int s = 0; s < nst; s++) {
+        if (s + 1 < nst) {
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const float xv = bf16_to_f32(u & 1 ? q[u / 2] >> 16 : q[u / 2] & 0xFFFFu);
-            const float* wrow = wr + (size_t)(h + u) * E;
-#pragma unroll
-            for (int j = 0; j < ES; j++) acc[j] = __builtin_fmaf(xv, wrow[col[j]], acc[j]);
+            for (int i = 0; i < LD; i++)
+                nxt[i] = *reinterpret_cast<const float4*>(wsrc[i] + (size_t)(s + 1) * HC * E);
         }
+        const float* wcur = reinterpret_cast<const float*>(wt[s & 1]);
+        uint4 xx = xp[s * (HC / 8)];
+        for (int h = 0; h < HC; h += 8) {
+            const uint4 xn = (h + 8 < HC) ? xp[(s * HC + h + 8) / 8] : xx;
+            const uint32_t q[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const float xv = bf16_to_f32(u & 1 ? q[u / 2] >> 16 : q[u / 2] & 0xFFFFu);
+                const float* wrow = wcur + (h + u) * EB + w * ES;
+                if (ES >= 4) {
+#pragma unroll
+                    for (int j4 = 0; j4 < ES / 4; j4++) {
+                        const float4 wv = *reinterpret_cast<const float4*>(wrow + 4 * j4);
+                        acc[4 * j4 + 0] = __builtin_fmaf(xv, wv.x, acc[4 * j4 + 0]);
+                        acc[4 * j4 + 1] = __builtin_fmaf(xv, wv.y, acc[4 * j4 + 1]);
+                        acc[4 * j4 + 2] = __builtin_fmaf(xv, wv.z, acc[4 * j4 + 2]);
+                        acc[4 * j4 + 3] = __builtin_fmaf(xv, wv.w, acc[4 * j4 + 3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < ES; j++) acc[j] = __builtin_fmaf(xv, wrow[j], acc[j]);
+                }
+            }
+            xx = xn;
+        }
+        if (s + 1 < nst) {
+#pragma unroll
+            for (int i = 0; i < LD; i++) wt[(s + 1) & 1][tid + 256 * i] = nxt[i];
+        }
+        __syncthreads();
     }
     if (t < T) {
 #pragma unroll
         for (int j = 0; j < ES; j++) {
-            if (eg + j < E) {
+            const int e = eb0 + w * ES + j;
+            if (e < E) {
                 float v = acc[j];
-                if (bias) v = v + bias[eg + j];
-                z[(size_t)t * E + eg + j] = v;
+                if (bias) v = v + bias[e];
+                z[(size_t)t * E + e] = v;
             }
         }
     }
+}
+
+// The same logits for any E: one thread per (token, expert).
+__global__ __launch_bounds__(256) void k_route_logits_any(int T, int H, int E, const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ wr,
+                                                          const float* __restrict__ bias, float* __restrict__ z)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)T * E) return;
+    const int t = (int)(i / E), e = (int)(i % E);
+    float acc = 0.0f;
+    for (int h = 0; h < H; h++) acc = __builtin_fmaf(bf16_to_f32(x[(size_t)t * H + h]), wr[(size_t)h * E + e], acc);
+    if (bias) acc = acc + bias[e];
+    z[i] = acc;
 }
 
 // Top-k per token (one wave per token): the k largest logits, the lower expert
@@ -886,15 +946,15 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
     // experts per wave: enough waves to fill the chip at small T, more reuse of
     // each x row at large T
     const int tg = (T + 63) / 64;
-    if (tg * E >= 256 * 4 * 8) {
-        hipLaunchKernelGGL(k_route_logits<8>, dim3(tg, blocks_for(E, 32)), dim3(256), 0, s, T, H, E, x, wr,
-                           bias, z);
-    } else if (tg * E >= 256 * 4 * 2) {
-        hipLaunchKernelGGL(k_route_logits<2>, dim3(tg, blocks_for(E, 8)), dim3(256), 0, s, T, H, E, x, wr,
-                           bias, z);
+    if (E % 4 != 0 || E < 4) {
+        hipLaunchKernelGGL(k_route_logits_any, dim3(blocks_for((size_t)T * E, 256)), dim3(256), 0, s, T, H, E, x,
+                           wr, bias, z);
+    } else if ((size_t)tg * E >= 256 * 32 && E % 32 == 0) {
+        hipLaunchKernelGGL(k_route_logits<8>, dim3(tg, E / 32), dim3(256), 0, s, T, H, E, x, wr, bias, z);
+    } else if ((size_t)tg * E >= 256 * 8 && E % 8 == 0) {
+        hipLaunchKernelGGL(k_route_logits<2>, dim3(tg, E / 8), dim3(256), 0, s, T, H, E, x, wr, bias, z);
     } else {
-        hipLaunchKernelGGL(k_route_logits<1>, dim3(tg, blocks_for(E, 4)), dim3(256), 0, s, T, H, E, x, wr,
-                           bias, z);
+        hipLaunchKernelGGL(k_route_logits<1>, dim3(tg, E / 4), dim3(256), 0, s, T, H, E, x, wr, bias, z);
     }
     hipLaunchKernelGGL(k_route_select, dim3(blocks_for(T, 4)), dim3(256), 0, s, T, E, k, z, ids, w);
     return hipGetLastError();
