@@ -26,7 +26,7 @@ struct DeviceInfo {
     std::once_flag once;
     int ok = 0;          // 1: gfx950
     int cus = 0;
-    int persist_per_cu[9] = {0};
+    int persist_per_cu[2][9] = {};   // [CW == 4][MT]
 };
 DeviceInfo g_dev[kMaxDevices];
 
@@ -41,7 +41,8 @@ DeviceInfo* device_info()
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
         di->ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         di->cus = prop.multiProcessorCount;
-        for (int mt : {1, 2, 4, 8}) di->persist_per_cu[mt] = persistent_blocks_per_cu(mt);
+        for (int mt : {1, 2, 4, 8})
+            for (int cw : {2, 4}) di->persist_per_cu[cw == 4][mt] = persistent_blocks_per_cu(mt, cw);
     });
     return di->ok ? di : nullptr;
 }
@@ -68,7 +69,7 @@ bool dims_ok(const v4moe_dims* d)
 struct Layout {
     size_t z, xq, xs, sorted_pair, pair_pos, hist, mt_expert, mt_row0, ctrl, done1, queue, hq, hs, y;
     size_t total;
-    int MT, n_mt_bound, nblk;
+    int MT, CW, n_mt_bound, nblk;
 };
 
 // One 128-byte line (or more) per row of h scales, so that rows of different
@@ -80,10 +81,11 @@ Layout layout(const v4moe_dims* d)
     Layout L{};
     const size_t T = d->T, H = d->H, I = d->I, E = d->E, P = (size_t)d->T * d->topk;
     L.MT = choose_mt(d->T, d->topk, d->E);
+    L.CW = choose_cw(L.MT, d->H, d->I);
     const size_t M = 16 * (size_t)L.MT;
     L.n_mt_bound = (int)(P / M + (P < E ? P : E) + 1);
     L.nblk = (int)((P + kPermChunk - 1) / kPermChunk);
-    const size_t NB1 = I / 128, NB2 = H / 256;
+    const size_t NB1 = I / (64 * L.CW), NB2 = H / (128 * L.CW);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
     L.z = take(T * E * 4);
@@ -140,11 +142,11 @@ thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws, bool persistent,
             DeviceInfo* di, hipStream_t s)
 {
-    const int NB1 = d->I / 128, NB2 = d->H / 256;
+    const int NB1 = d->I / (64 * L.CW), NB2 = d->H / (128 * L.CW);
     hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return V4MOE_ELAUNCH;
-    int per = di->persist_per_cu[L.MT];
+    int per = di->persist_per_cu[L.CW == 4][L.MT];
     int grid = di->cus * (per > 0 ? per : 1);
     // Scheduling lag in waves: enough linear1 tiles between a wave's linear1 and
     // linear2 entries to keep every running block busy meanwhile (estimate from
@@ -160,10 +162,10 @@ int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws,
     if (persistent) {
         const int max_items = L.n_mt_bound * (NB1 + NB2);
         if (grid > max_items) grid = max_items;
-        if (launch_ffn_persistent(L.MT, a, grid, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_ffn_persistent(L.MT, L.CW, a, grid, s) != hipSuccess) return V4MOE_ELAUNCH;
     } else {
-        if (launch_ffn(1, L.MT, a, s) != hipSuccess) return V4MOE_ELAUNCH;
-        if (launch_ffn(2, L.MT, a, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_ffn(1, L.MT, L.CW, a, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_ffn(2, L.MT, L.CW, a, s) != hipSuccess) return V4MOE_ELAUNCH;
     }
     if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return V4MOE_ELAUNCH;
     return V4MOE_OK;
@@ -376,7 +378,7 @@ __attribute__((visibility("default"))) int moe_dequant_fp8(const v4moe_mat* m, i
 {
     if (!m || !out) return V4MOE_ENULL;
     if (!mat_ok(*m)) return V4MOE_ENULL;
-    if (N < 16 || N % 16 || K < 128 || K % 128 || expert < 0) return V4MOE_EDIMS;
+    if (N < 64 || N % 64 || K < 128 || K % 128 || expert < 0) return V4MOE_EDIMS;
     if (!aligned16(out)) return V4MOE_EALIGN;
     DeviceInfo* di = device_info();
     if (!di) return V4MOE_EDEVICE;

@@ -49,65 +49,35 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
     return sign | q;
 }
 
-// Magnitude of the FP4 E2M1 code m (0..7): 0, 0.5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ float e2m1_mag(int m)
+// 16x16 output tile over one 128-wide K chunk on gfx950's block-scaled
+// matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4): A = E4M3 activations with
+// scale 1 (E8M0 127), B = E2M1 weight codes, each lane's 32 codes scaled by
+// 2^(sb_byte - 127), sb_byte = byte SEL of sb.  The hardware multiplies the
+// exact values e4m3(a) * e2m1(w) * 2^b; inside the window b in [-8, 6] every
+// e2m1(w) * 2^b is itself an E4M3 value (P1 §4: the FP4 -> FP8 conversion is
+// lossless), so the products are those of an FP8 x FP8 GEMM over the
+// dequantised weights, without materialising the E4M3 bytes.
+// Lane layouts (g = l/16):
+//   A: lane l holds row l%16; dwords 0-3 = K 16g..16g+15, dwords 4-7 = K
+//      64+16g..64+16g+15 of the chunk, one byte per element in K order;
+//   B: lane l holds column l%16 and K 32g..32g+31: element k in byte k/2, the
+//      low nibble for even k (four dwords);
+//   C: lane l holds rows 4g+i, i = 0..3, of column l%16.
+template <int SEL>
+__device__ __forceinline__ v4f mfma_e4m3_e2m1(v8i a, uint4 b, int sb)
 {
-    int e = m >> 1;
-    float frac = (m & 1) ? 1.5f : 1.0f;
-    return e == 0 ? 0.5f * (float)(m & 1) : ldexpf(frac, e - 1);
+    const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bv, z, 0, 4, 0, 127, SEL, sb);
 }
-
-// Dequantisation table, one entry per E8M0 byte s (sub-block exponent
-// b = s - 127): the E4M3 bytes of e2m1_mag(m) * 2^b for m = 0..3 (x) and
-// m = 4..7 (y).  P1 §4: FP4 -> FP8 is exact while b stays in the window where
-// every such product is an E4M3 value, b in [-8, 6]; outside it the entry is 0
-// (the prepack step rejects such scales).
-__device__ __forceinline__ uint2 dequant_lut_entry(int s)
+__device__ __forceinline__ v4f mfma_e4m3_e2m1_sel(int sel, v8i a, uint4 b, int sb)
 {
-    int b = s - 127;
-    uint32_t lo = 0, hi = 0;
-    if (b >= -8 && b <= 6) {
-        for (int m = 0; m < 4; m++) {
-            lo |= e4m3_rne_sat(ldexpf(e2m1_mag(m), b)) << (8 * m);
-            hi |= e4m3_rne_sat(ldexpf(e2m1_mag(m + 4), b)) << (8 * m);
-        }
+    switch (sel & 3) {   // sel is a constant after unrolling: one instruction remains
+    case 0: return mfma_e4m3_e2m1<0>(a, b, sb);
+    case 1: return mfma_e4m3_e2m1<1>(a, b, sb);
+    case 2: return mfma_e4m3_e2m1<2>(a, b, sb);
+    default: return mfma_e4m3_e2m1<3>(a, b, sb);
     }
-    return make_uint2(lo, hi);
-}
-
-// One 16-byte packed FP4 slot (32 codes) -> 32 E4M3 bytes in element order.
-// Byte j of the slot holds element 8*(j/4)+j%4 (low nibble) and that +4 (high
-// nibble), so per 32-bit word: the low nibbles give elements 8d..8d+3, the
-// high nibbles 8d+4..8d+7.  Each magnitude (3 bits) selects a byte of the
-// 8-byte table with v_perm_b32; the sign bit is moved to bit 7.  Negative
-// zero is kept (0x8 -> 0x80).
-__device__ __forceinline__ uint32_t dq_lo(uint32_t w, uint2 L)
-{
-    return __builtin_amdgcn_perm(L.y, L.x, w & 0x07070707u) | ((w << 4) & 0x80808080u);
-}
-__device__ __forceinline__ uint32_t dq_hi(uint32_t w, uint2 L)
-{
-    return __builtin_amdgcn_perm(L.y, L.x, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
-}
-__device__ __forceinline__ v8i dequant_slot(uint4 w, uint2 L)
-{
-    v8i o;
-    o[0] = (int)dq_lo(w.x, L); o[1] = (int)dq_hi(w.x, L);
-    o[2] = (int)dq_lo(w.y, L); o[3] = (int)dq_hi(w.y, L);
-    o[4] = (int)dq_lo(w.z, L); o[5] = (int)dq_hi(w.z, L);
-    o[6] = (int)dq_lo(w.w, L); o[7] = (int)dq_hi(w.w, L);
-    return o;
-}
-
-// 16x16 output tile over one 128-wide K chunk on the FP8 matrix cores
-// (v_mfma_f32_16x16x128_f8f6f4, both operands E4M3, no block scale).
-// Operand lane layout used throughout: lane l holds row/column l%16 and the
-// 32 consecutive K elements (l/16)*32 .. +31 of the chunk, as 8 dwords in
-// element order.  Result: lane l holds rows 4*(l/16)+i, i = 0..3, column l%16.
-__device__ __forceinline__ v4f mfma_chunk(v8i a, v8i b)
-{
-    v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
 // splitmix64 output function (Steele, Lea & Flood, OOPSLA 2014).

@@ -15,7 +15,7 @@ constexpr int kWaveExperts = 8;
 
 struct MatPtr {
     const uint8_t* fp4;   // packed [E][N/16][K/128][64][16]
-    const uint8_t* e8m0;  // packed [E][N/16][K/128][64]
+    const uint8_t* e8m0;  // packed [E][N/64][K/128][64][4]
     const float* blk;     // [E][N/128][K/128]
 };
 
@@ -48,9 +48,11 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offs
 hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue, int lag,
                               const FfnArgs& a, int32_t* mt_expert, int32_t* mt_row0,
                               uint32_t* queue, hipStream_t s);
-hipError_t launch_ffn(int phase, int MT, const FfnArgs& a, hipStream_t s);
-hipError_t launch_ffn_persistent(int MT, const FfnArgs& a, int grid, hipStream_t s);
-int persistent_blocks_per_cu(int MT);
+// CW = wave columns per tile (2 or 4, from choose_cw); MT = 8 tiles also have
+// two wave rows.
+hipError_t launch_ffn(int phase, int MT, int CW, const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_persistent(int MT, int CW, const FfnArgs& a, int grid, hipStream_t s);
+int persistent_blocks_per_cu(int MT, int CW);
 hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* w, uint16_t* out,
                           hipStream_t s);
 hipError_t launch_prepack(int E, int N, int K, const uint8_t* fp4_in, const uint8_t* e8_in,
@@ -62,5 +64,8 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 
 // Rows per m-tile (16 * MT) used for given dimensions.
 int choose_mt(int T, int k, int E);
+// Wave columns per tile: a tile covers 64*CW columns of h in linear1 and
+// 128*CW output columns in linear2.
+int choose_cw(int MT, int H, int I);
 
 }  // namespace v4moe

@@ -442,29 +442,31 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
 // ---------------------------------------------------------------------------
 // Expert FFN tiles.
 //
-// Tile (phase 1) = one m-tile of M rows x 128 columns of h (128 gate + 128 up
-// output columns), K = H.  Tile (phase 2) = M rows x 256 output columns, K = I.
-// 4 waves; wave w owns 4 16-column n-tiles (phase 1: gate and up columns
-// 32w..32w+31 of the block, so SwiGLU pairs sit in the same lane; phase 2:
-// columns 64w..64w+63) and all M rows.
+// A tile is one m-tile (M = 16*MT rows of one expert) by a block of output
+// columns, computed by NW = RW*CW waves: RW row groups of MTW = MT/RW m-tiles
+// each, and CW column groups.  Wave w = (rg, cg) = (w / CW, w % CW) owns eight
+// 16-column n-tiles of its row group:
+//   phase 1 (linear1 + SwiGLU + requant, K = H): gate n-tiles 4cg..4cg+3 and
+//     the up n-tiles of the same columns of the tile's HC = 64*CW columns of
+//     h, so both halves of a SwiGLU pair sit in one lane;
+//   phase 2 (linear2, K = I): output n-tiles 8cg..8cg+7 of OC = 128*CW columns.
 //
 // Data movement: an NS-stage ring in LDS, one stage per 128-wide K chunk,
 // filled NS-1 chunks ahead by gfx950 direct-to-LDS loads (global_load_lds):
-//   B  the wave's 4 packed FP4 records (4 x 1 KiB, contiguous in HBM) and
-//      their E8M0 bytes (4 x 64 B), 16-byte / 4-byte per lane, fully coalesced;
-//   A  the tile's M activation rows (E4M3, 128 B each), gathered through
-//      sorted_pair in phase 1 or contiguous hq rows in phase 2; lanes write
-//      LDS contiguously, so rows are stored with their 16-byte segments
-//      XOR-swizzled by (row/2)%8, which lets the 16 rows of an MFMA operand
-//      read hit distinct banks;
+//   B  the tile's 8*CW packed FP4 records (1 KiB each, contiguous in HBM) and
+//      2*CW E8M0 records (256 B: one dword per lane = the scale bytes of four
+//      n-tiles), 16 / 4 bytes per lane, fully coalesced;
+//   A  the tile's M activation rows (E4M3, 128 B per chunk), gathered through
+//      sorted_pair in phase 1, contiguous hq rows in phase 2.  Lanes write LDS
+//      contiguously, so each row's 16-byte segments are stored XOR-swizzled by
+//      (row/2)%8, which puts the 16 rows of one operand read on distinct banks;
 //   X  the per-row activation scales of the chunk.
-// Stages are consumed in order: wait for the stage's loads (s_waitcnt
-// vmcnt counted per wave), one barrier, issue the loads of the stage NS-1
-// ahead into the slot just freed, compute.  Each wave then dequantises its B
-// fragments FP4 -> E4M3 in registers (per-block LDS table) and, per m-tile,
-// P = MFMA over the chunk, acc = fma(xs*blk, P, acc).
+// Stages are consumed in order: wait for the stage's loads (s_waitcnt vmcnt,
+// counted per wave), one barrier, issue the loads NS-1 chunks ahead into the
+// slot just freed, compute: per m-tile, eight block-scaled MFMAs (FP4 codes
+// and their E8M0 scales straight from LDS, no dequantisation pass), then
+// acc = fma(xs*blk, P, acc).  A row group with no valid row skips its MFMAs.
 // ---------------------------------------------------------------------------
-constexpr int kLutBytes = 256 * 8;
 
 // Stores that another XCD may read within the same launch: agent-scope
 // (relaxed) atomic stores, which on gfx950 write through the local L2.
@@ -484,19 +486,8 @@ __device__ __forceinline__ void store_coherent(uint8_t* p, uint4 v)
 // inline asm they are invisible to the compiler's wait insertion, which would
 // otherwise drain the whole pipeline before every LDS read; completion is
 // awaited explicitly with wait_vm<N>() (at most N of this wave's vector memory
-// operations still outstanding).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_base) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(g), "s"(lds_base) : "memory", "m0");
-}
-// Same copies with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane
-// byte offset (one VGPR instead of two per address).
+// operations still outstanding).  The global address is a wave-uniform 64-bit
+// base (SGPRs) plus a 32-bit per-lane byte offset.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -523,108 +514,123 @@ __device__ __forceinline__ void wait_vm()
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// wait until at most OPS*k operations are outstanding, k = 0..3 at run time
+// wait until at most OPS*k operations are outstanding, k = 0..2 at run time
 template <int OPS>
 __device__ __forceinline__ void wait_stages(int k)
 {
-    if (k >= 3) wait_vm<3 * OPS>();
-    else if (k == 2) wait_vm<2 * OPS>();
+    if (k >= 2) wait_vm<2 * OPS>();
     else if (k == 1) wait_vm<OPS>();
     else wait_vm<0>();
 }
 
-__host__ __device__ constexpr int ring_stages(int MT) { return MT == 1 ? 4 : MT == 8 ? 4 : 3; }
+__host__ __device__ constexpr int ring_stages(int MT) { return MT == 1 ? 4 : 3; }
 
-template <int MT>
+template <int MT, int RW, int CW>
 struct TileLayout {
+    static constexpr int NW = RW * CW;
+    static constexpr int NT = 64 * NW;                       // threads
     static constexpr int M = 16 * MT;
+    static constexpr int MTW = MT / RW;                      // m-tiles per wave
+    static constexpr int RG = M / RW;                        // rows per row group
+    static constexpr int HC = 64 * CW;                       // phase-1 columns of h
+    static constexpr int OC = 128 * CW;                      // phase-2 output columns
     static constexpr int NS = ring_stages(MT);
-    static constexpr int AI = M >= 32 ? M / 32 : 1;          // A loads per wave per stage
-    static constexpr int XI = 1;                             // X loads per wave per stage
-    static constexpr int OPS = 4 + 1 + AI + XI;              // loads per wave per stage
-    static constexpr int B_OFF = 0;                          // 16 records x 1 KiB
-    static constexpr int S_OFF = 16384;                      // 16 records x 64 B
-    static constexpr int A_OFF = 17408;                      // M rows x 128 B (swizzled)
-    static constexpr int X_OFF = A_OFF + M * 128;            // max(M, 64) floats
-    static constexpr int STAGE = X_OFF + (M > 64 ? M : 64) * 4;
+    static constexpr int NBR = 8 / RW;                       // B records per wave per stage
+    static constexpr int NSR = 2 / RW;                       // scale records per wave per stage
+    static constexpr int AB = M / 8;                         // 1 KiB A blocks per stage
+    static constexpr int AI = AB >= NW ? AB / NW : 1;        // A loads per wave per stage
+    static constexpr int OPS = NBR + NSR + AI + 1;           // loads per wave per stage
+    static constexpr int B_OFF = 0;                          // 8*CW records x 1 KiB
+    static constexpr int S_OFF = 8 * CW * 1024;              // 2*CW records x 256 B
+    static constexpr int A_OFF = S_OFF + 2 * CW * 256;       // M rows x 128 B (swizzled)
+    static constexpr int X_OFF = A_OFF + M * 128;            // RW x 64 floats
+    static constexpr int STAGE = X_OFF + RW * 256;
     static constexpr int RING = NS * STAGE;
-    static constexpr int RED_OFF = RING;                     // [4][M] float
-    static constexpr int ROW_OFF = RED_OFF + 4 * M * 4;      // [M] int
-    static constexpr int BLK_OFF = ROW_OFF + M * 4;          // [2][128] float: block scales per chunk
-    static constexpr int BYTES = BLK_OFF + 2 * 128 * 4;
+    static constexpr int ROW_OFF = RING;                     // [M] int
+    static constexpr int BLK_OFF = ROW_OFF + M * 4;          // [CW][128] float: block scales per chunk
+    static constexpr int BYTES = BLK_OFF + CW * 128 * 4;
+    static constexpr int SP1 = HC + 16;                      // phase-1 staging pitch (bytes)
+    static constexpr int SP2 = OC + 8;                       // phase-2 staging pitch (bf16)
+    static_assert(MT % RW == 0 && RG <= 64, "a row group's scales fit one 64-lane load");
+    static_assert(CW == 2 || CW == 4, "a 128-column quantisation group spans two waves");
+    static_assert(RW == 1 || RW == 2, "");
+    static_assert(AB % NW == 0 || NW % AB == 0, "A blocks spread evenly over the waves");
     static_assert(OPS * (NS - 2) < 64, "vmcnt range");
-    static_assert(STAGE >= M * 128 && STAGE >= 16 * 256 * 2, "epilogue staging fits in one stage");
+    static_assert(NS >= 2 && STAGE >= M * SP1 && STAGE >= NW * RG * 4 && STAGE >= RW * 16 * SP2 * 2,
+                  "epilogue staging and amax partials fit in a stage");
 };
 
-template <int PHASE, int MT>
-__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8_t* smem,
-                                         const uint2* lut)
+// SiLU(g) * u in fp32 (the same code in every tile variant).
+__device__ __forceinline__ float swiglu(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
+
+template <int PHASE, int MT, int RW, int CW>
+__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8_t* smem)
 {
-    using TL = TileLayout<MT>;
-    constexpr int M = TL::M;
-    constexpr int NS = TL::NS;
+    using TL = TileLayout<MT, RW, CW>;
+    constexpr int M = TL::M, NS = TL::NS, NT = TL::NT, NW = TL::NW, MTW = TL::MTW, RG = TL::RG;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = w / CW, cg = w % CW;
     const int e = uniform(a.mt_expert[mt]);
     const int row0 = uniform(a.mt_row0[mt]);
     const int rows = uniform(min(M, a.offsets[e + 1] - row0));
+    const bool active = rows > rg * RG;                      // this row group has a valid row
     const int K = PHASE == 1 ? a.H : a.I;
     const int N = PHASE == 1 ? a.I : a.H;
     const int C = K / 128;
     const uint32_t ring = (uint32_t)(uintptr_t)smem;
 
-    float* red = reinterpret_cast<float*>(smem + TL::RED_OFF);
     int32_t* rowinfo = reinterpret_cast<int32_t*>(smem + TL::ROW_OFF);
 
     // phase 1: token of each row (rows past the end repeat the last valid
     // row's token: finite filler, never stored); phase 2: pair id or -1.
-    for (int r = tid; r < M; r += 256) {
+    for (int r = tid; r < M; r += NT) {
         const int p = a.sorted_pair[row0 + min(r, rows - 1)];
         rowinfo[r] = PHASE == 1 ? p / a.topk : (r < rows ? p : -1);
     }
-    // The tile's 128x128 block scales for every chunk, staged in LDS (the
-    // kernel writes global memory, so per-chunk reads would be vector loads
-    // whose waits would drain the load ring).  Phase 1: [0] gate, [1] up;
-    // phase 2: the two 128-column blocks of the tile.
+    // The tile's 128x128 block scales for every chunk, staged in LDS (per-chunk
+    // global reads would be vector loads whose waits drain the load ring).
+    // Phase 1: [2*hb] gate, [2*hb+1] up of h block hb of the tile; phase 2:
+    // output block cg of the tile.
     float* blkv = reinterpret_cast<float*>(smem + TL::BLK_OFF);
-    for (int i = tid; i < 2 * C; i += 256) {
+    for (int i = tid; i < CW * C; i += NT) {
         const int h = i / C, c = i % C;
         const float* src = PHASE == 1
-            ? (h == 0 ? a.gate.blk : a.up.blk) + ((size_t)e * (a.I / 128) + nb) * C
-            : a.down.blk + ((size_t)e * (a.H / 128) + nb * 2 + h) * C;
+            ? ((h & 1) ? a.up.blk : a.gate.blk) + ((size_t)e * (a.I / 128) + nb * (CW / 2) + (h >> 1)) * C
+            : a.down.blk + ((size_t)e * (a.H / 128) + nb * CW + h) * C;
         blkv[h * 128 + c] = src[c];
     }
     __syncthreads();
 
-    // Sources of this lane's loads at chunk 0: wave-uniform bases plus 32-bit
+    // Sources of this wave's loads at chunk 0: wave-uniform bases plus 32-bit
     // per-lane byte offsets (the dimension checks keep every offset < 2^31).
-    const uint8_t* bbase[4];
-    const uint8_t* sptr;
-    {
-        const int NT16 = N / 16;
-        const uint8_t* srec[4];
+    const uint8_t* bbase[TL::NBR];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const MatPtr& m = PHASE == 1 ? (j < 2 ? a.gate : a.up) : a.down;
-            const int tile = PHASE == 1 ? nb * 8 + 2 * w + (j & 1) : nb * 16 + 4 * w + j;
-            const size_t rec = ((size_t)e * NT16 + tile) * C;
-            bbase[j] = uniform(m.fp4 + rec * 1024);
-            srec[j] = m.e8m0 + rec * 64;
-        }
-        sptr = srec[lane >> 4] + (lane & 15) * 4;
+    for (int r = 0; r < TL::NBR; r++) {
+        const int rr = w * TL::NBR + r;                      // record of the tile, 0 .. 8*CW-1
+        const MatPtr& m = PHASE == 1 ? ((rr & 7) < 4 ? a.gate : a.up) : a.down;
+        const int tile = PHASE == 1 ? nb * 4 * CW + 4 * (rr >> 3) + (rr & 3) : nb * 8 * CW + rr;
+        bbase[r] = uniform(m.fp4 + ((size_t)e * (N / 16) + tile) * C * 1024);
     }
-    const uint32_t boff = lane * 16;
-    const float* blk0 = blkv + (PHASE == 1 ? 0 : (w >> 1) * 128);
-    const float* blk1 = blkv + (PHASE == 1 ? 128 : (w >> 1) * 128);
+    const uint8_t* sbase[TL::NSR];
+#pragma unroll
+    for (int r = 0; r < TL::NSR; r++) {
+        const int ss = w * TL::NSR + r;                      // scale record, 0 .. 2*CW-1
+        const MatPtr& m = PHASE == 1 ? ((ss & 1) ? a.up : a.gate) : a.down;
+        const int quad = PHASE == 1 ? nb * CW + (ss >> 1) : nb * 2 * CW + ss;
+        sbase[r] = uniform(m.e8m0 + ((size_t)e * (N / 64) + quad) * C * 256);
+    }
+    const float* blk0 = blkv + (PHASE == 1 ? 2 * (cg >> 1) : cg) * 128;
+    const float* blk1 = blkv + (PHASE == 1 ? 2 * (cg >> 1) + 1 : cg) * 128;
     const uint8_t* abase = uniform(PHASE == 1 ? a.xq : a.hq);
     uint32_t aoff[TL::AI];
 #pragma unroll
     for (int i = 0; i < TL::AI; i++) {
-        const int blk = (i * 4 + w) % (M / 8);                // 1 KiB block = 8 rows
-        const int g = blk * 64 + lane;                        // segment of the tile
+        const int blk = (i * NW + w) % TL::AB;               // 1 KiB block = 8 rows
+        const int g = blk * 64 + lane;                       // 16-byte segment of the tile
         const int r = g >> 3;
-        const int seg = (g & 7) ^ ((r >> 1) & 7);             // global segment stored at position g&7
+        const int seg = (g & 7) ^ ((r >> 1) & 7);            // global segment stored at position g&7
         const int rc = min(r, rows - 1);
         aoff[i] = (PHASE == 1 ? (uint32_t)rowinfo[r] * (uint32_t)a.H : (uint32_t)(row0 + rc) * (uint32_t)a.I) +
                   seg * 16;
@@ -632,28 +638,30 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     const float* xbase = uniform(PHASE == 1 ? a.xs : a.hs);
     uint32_t xoff;
     {
-        const int r = ((w % ((M + 63) / 64)) * 64 + lane);
-        const int rc = min(r, rows - 1);
-        xoff = 4u * (PHASE == 1 ? (uint32_t)rowinfo[min(r, M - 1)] * (uint32_t)(a.H / 128)
-                                : (uint32_t)(row0 + rc) * (uint32_t)a.hs_stride);
+        const int r = min(rg * RG + lane, M - 1);
+        xoff = 4u * (PHASE == 1 ? (uint32_t)rowinfo[r] * (uint32_t)(a.H / 128)
+                                : (uint32_t)(row0 + min(r, rows - 1)) * (uint32_t)a.hs_stride);
     }
 
     auto issue = [&](int c, int slot) {
         const uint32_t st = __builtin_amdgcn_readfirstlane(ring + slot * TL::STAGE);
 #pragma unroll
-        for (int j = 0; j < 4; j++) dma16s(bbase[j], boff + c * 1024, st + TL::B_OFF + (w * 4 + j) * 1024);
-        dma4(sptr + (size_t)c * 64, st + TL::S_OFF + w * 256);
+        for (int r = 0; r < TL::NBR; r++)
+            dma16s(bbase[r], lane * 16 + c * 1024, st + TL::B_OFF + (w * TL::NBR + r) * 1024);
+#pragma unroll
+        for (int r = 0; r < TL::NSR; r++)
+            dma4s(sbase[r], lane * 4 + c * 256, st + TL::S_OFF + (w * TL::NSR + r) * 256);
 #pragma unroll
         for (int i = 0; i < TL::AI; i++)
-            dma16s(abase, aoff[i] + c * 128, st + TL::A_OFF + ((i * 4 + w) % (M / 8)) * 1024);
-        dma4s(xbase, xoff + c * 4, st + TL::X_OFF + (w % ((M + 63) / 64)) * 256);
+            dma16s(abase, aoff[i] + c * 128, st + TL::A_OFF + ((i * NW + w) % TL::AB) * 1024);
+        dma4s(xbase, xoff + c * 4, st + TL::X_OFF + rg * 256);
     };
 
-    v4f acc[MT][4];
+    v4f acc[MTW][8];
 #pragma unroll
-    for (int i = 0; i < MT; i++)
+    for (int i = 0; i < MTW; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < 8; j++) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll
     for (int u = 0; u < NS - 1; u++)
@@ -663,110 +671,116 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         wait_stages<TL::OPS>(min(NS - 2, C - 1 - c));
         __syncthreads();
         if (c + NS - 1 < C) issue(c + NS - 1, (c + NS - 1) % NS);
+        if (!active) continue;
 
         const uint8_t* st = smem + (c % NS) * TL::STAGE;
-        v8i bf[4];
+        uint4 bq[8];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint4 q = *reinterpret_cast<const uint4*>(st + TL::B_OFF + (w * 4 + j) * 1024 + lane * 16);
-            const uint32_t sb = st[TL::S_OFF + w * 256 + j * 64 + lane];
-            bf[j] = dequant_slot(q, lut[sb]);
-        }
+        for (int j = 0; j < 8; j++)
+            bq[j] = *reinterpret_cast<const uint4*>(st + TL::B_OFF + (cg * 8 + j) * 1024 + lane * 16);
+        const int sc[2] = {*reinterpret_cast<const int*>(st + TL::S_OFF + (cg * 2) * 256 + lane * 4),
+                           *reinterpret_cast<const int*>(st + TL::S_OFF + (cg * 2 + 1) * 256 + lane * 4)};
         const float sb0 = blk0[c];
         const float sb1 = blk1[c];
-        // All m-tiles are computed (rows past the end hold finite filler and are
-        // never stored), so the four independent MFMAs of every m-tile can be
-        // in flight before their results are promoted.
+        // Every m-tile of the row group is computed (rows past the end hold
+        // finite filler and are never stored), so the eight independent MFMAs
+        // of an m-tile are all in flight before their results are promoted.
 #pragma unroll
-        for (int i = 0; i < MT; i++) {
-            const int r = i * 16 + (lane & 15);
+        for (int i = 0; i < MTW; i++) {
+            const int r = rg * RG + i * 16 + (lane & 15);
             const int sw = (r >> 1) & 7;
-            const int s0 = (lane >> 4) * 2;
+            const int g = lane >> 4;
             const uint8_t* arow = st + TL::A_OFF + r * 128;
-            const uint4 a0 = *reinterpret_cast<const uint4*>(arow + ((s0 ^ sw) * 16));
-            const uint4 a1 = *reinterpret_cast<const uint4*>(arow + (((s0 + 1) ^ sw) * 16));
+            const uint4 a0 = *reinterpret_cast<const uint4*>(arow + ((g ^ sw) * 16));
+            const uint4 a1 = *reinterpret_cast<const uint4*>(arow + (((g + 4) ^ sw) * 16));
             v8i af;
             af[0] = (int)a0.x; af[1] = (int)a0.y; af[2] = (int)a0.z; af[3] = (int)a0.w;
             af[4] = (int)a1.x; af[5] = (int)a1.y; af[6] = (int)a1.z; af[7] = (int)a1.w;
-            v4f P[4];
+            v4f P[8];
 #pragma unroll
-            for (int j = 0; j < 4; j++) P[j] = mfma_chunk(af, bf[j]);
-            const float4 x4 = *reinterpret_cast<const float4*>(st + TL::X_OFF + (i * 16 + (lane >> 4) * 4) * 4);
+            for (int j = 0; j < 8; j++) P[j] = mfma_e4m3_e2m1_sel(j & 3, af, bq[j], sc[j >> 2]);
+            const float4 x4 = *reinterpret_cast<const float4*>(st + TL::X_OFF + rg * 256 + (i * 16 + g * 4) * 4);
             const float s0v[4] = {x4.x * sb0, x4.y * sb0, x4.z * sb0, x4.w * sb0};
             const float s1v[4] = {x4.x * sb1, x4.y * sb1, x4.z * sb1, x4.w * sb1};
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float* sc = (PHASE == 1 && j >= 2) ? s1v : s0v;
+            for (int j = 0; j < 8; j++) {
+                const float* s = (PHASE == 1 && j >= 4) ? s1v : s0v;
 #pragma unroll
-                for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(sc[q], P[j][q], acc[i][j][q]);
+                for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s[q], P[j][q], acc[i][j][q]);
             }
         }
     }
-    __syncthreads();   // every wave is done with the ring: its first stage becomes the staging area
+    __syncthreads();   // every wave is done with the ring: its first stages become staging space
 
     if (PHASE == 1) {
         // h = SiLU(g) * u, then E4M3 per (row, 128 columns of h): the amax of a
-        // row is reduced over the 16 lanes of a row group, then over the 4 waves.
-        uint8_t* stage = smem;  // [M][128]
-        float hv[MT][2][4];
+        // row is reduced over the 16 lanes of a row group of the MFMA result,
+        // then over the two waves that share the 128 columns.
+        uint8_t* stage = smem;                                      // [M][SP1]
+        float* red = reinterpret_cast<float*>(smem + TL::STAGE);    // [NW][RG], ring stage 1
+        float hv[MTW][4][4];
 #pragma unroll
-        for (int i = 0; i < MT; i++)
+        for (int i = 0; i < MTW; i++)
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 float mx = 0.0f;
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const float g = acc[i][j][q];
-                    const float u = acc[i][2 + j][q];
-                    const float h = (g / (1.0f + expf(-g))) * u;
+                for (int j = 0; j < 4; j++) {
+                    const float h = swiglu(acc[i][j][q], acc[i][4 + j][q]);
                     hv[i][j][q] = h;
                     mx = fmaxf(mx, fabsf(h));
                 }
 #pragma unroll
                 for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-                if ((lane & 15) == 0) red[w * M + i * 16 + (lane >> 4) * 4 + q] = mx;
+                if ((lane & 15) == 0) red[w * RG + i * 16 + (lane >> 4) * 4 + q] = mx;
             }
         __syncthreads();
+        const int wp = rg * CW + (cg & ~1);
 #pragma unroll
-        for (int i = 0; i < MT; i++)
+        for (int i = 0; i < MTW; i++)
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const int r = i * 16 + (lane >> 4) * 4 + q;
-                const float amax = fmaxf(fmaxf(red[r], red[M + r]), fmaxf(red[2 * M + r], red[3 * M + r]));
+                const int rl = i * 16 + (lane >> 4) * 4 + q;
+                const int r = rg * RG + rl;
+                const float amax = fmaxf(red[wp * RG + rl], red[(wp + 1) * RG + rl]);
                 const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-                    stage[r * 128 + 32 * w + 16 * j + (lane & 15)] = (uint8_t)e4m3_rne_sat(hv[i][j][q] / s);
-                if (w == 0 && (lane & 15) == 0 && r < rows)
-                    store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb, s);
+                for (int j = 0; j < 4; j++)
+                    stage[r * TL::SP1 + 64 * cg + 16 * j + (lane & 15)] = (uint8_t)e4m3_rne_sat(hv[i][j][q] / s);
+                if ((cg & 1) == 0 && (lane & 15) == 0 && r < rows)
+                    store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * (CW / 2) + (cg >> 1), s);
             }
         __syncthreads();
-        for (int s = tid; s < M * 8; s += 256) {
-            const int r = s >> 3;
+        constexpr int SEGS = TL::HC / 16;
+        for (int s = tid; s < M * SEGS; s += NT) {
+            const int r = s / SEGS, sg = s % SEGS;
             if (r < rows)
-                store_coherent(a.hq + (size_t)(row0 + r) * a.I + nb * 128 + (s & 7) * 16,
-                               *reinterpret_cast<const uint4*>(stage + r * 128 + (s & 7) * 16));
+                store_coherent(a.hq + (size_t)(row0 + r) * a.I + nb * TL::HC + sg * 16,
+                               *reinterpret_cast<const uint4*>(stage + r * TL::SP1 + sg * 16));
         }
         __syncthreads();
     } else {
-        // bf16 rows scattered back to their pair slot p = t*topk + j.
-        uint16_t* stage = reinterpret_cast<uint16_t*>(smem);  // [16][256]
+        // bf16 rows scattered back to their pair slot p = t*topk + j, one m-tile
+        // of every row group at a time.
+        uint16_t* stage = reinterpret_cast<uint16_t*>(smem);        // [RW*16][SP2]
+        constexpr int SEGS = TL::OC / 8;
 #pragma unroll
-        for (int i = 0; i < MT; i++) {
+        for (int i = 0; i < MTW; i++) {
             if (i * 16 < rows) {
 #pragma unroll
-                for (int j = 0; j < 4; j++)
+                for (int j = 0; j < 8; j++)
 #pragma unroll
                     for (int q = 0; q < 4; q++)
-                        stage[((lane >> 4) * 4 + q) * 256 + 64 * w + 16 * j + (lane & 15)] =
+                        stage[(rg * 16 + (lane >> 4) * 4 + q) * TL::SP2 + 128 * cg + 16 * j + (lane & 15)] =
                             (uint16_t)f32_to_bf16(acc[i][j][q]);
                 __syncthreads();
-                for (int s = tid; s < 16 * 32; s += 256) {
-                    const int r = i * 16 + (s >> 5);
+                for (int s = tid; s < RW * 16 * SEGS; s += NT) {
+                    const int rs = s / SEGS, sg = s % SEGS;
+                    const int r = (rs >> 4) * RG + i * 16 + (rs & 15);
                     if (r < rows) {
                         const int p = rowinfo[r];
-                        *reinterpret_cast<uint4*>(a.y + (size_t)p * a.H + nb * 256 + (s & 31) * 8) =
-                            *reinterpret_cast<const uint4*>(stage + (s >> 5) * 256 + (s & 31) * 8);
+                        *reinterpret_cast<uint4*>(a.y + (size_t)p * a.H + nb * TL::OC + sg * 8) =
+                            *reinterpret_cast<const uint4*>(stage + rs * TL::SP2 + sg * 8);
                     }
                 }
                 __syncthreads();
@@ -775,17 +789,14 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     }
 }
 
-template <int PHASE, int MT>
-__global__ __launch_bounds__(256) void k_ffn(FfnArgs a, int NB)
+template <int PHASE, int MT, int RW, int CW>
+__global__ __launch_bounds__(64 * RW * CW) void k_ffn(FfnArgs a, int NB)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int mt = blockIdx.x / NB;
     const int nb = blockIdx.x % NB;
     if (mt >= a.ctrl[0]) return;
-    uint2* lut = reinterpret_cast<uint2*>(smem);
-    lut[threadIdx.x] = dequant_lut_entry(threadIdx.x);
-    __syncthreads();
-    ffn_tile<PHASE, MT>(a, mt, nb, smem + kLutBytes, lut);
+    ffn_tile<PHASE, MT, RW, CW>(a, mt, nb, smem);
 }
 
 // Persistent, wave-scheduled: blocks take queue entries in order.  A linear2
@@ -793,14 +804,12 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a, int NB)
 // earlier in the queue, were taken by running blocks and never wait, so every
 // wait ends.  Counters only signal readiness; no data is accumulated through
 // them, so the numerics are those of the unfused kernels.
-template <int MT>
-__global__ __launch_bounds__(256) void k_ffn_persistent(FfnArgs a)
+template <int MT, int RW, int CW>
+__global__ __launch_bounds__(64 * RW * CW) void k_ffn_persistent(FfnArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ uint32_t item;
-    uint2* lut = reinterpret_cast<uint2*>(smem);
-    lut[threadIdx.x] = dequant_lut_entry(threadIdx.x);
-    const int NB1 = a.I / 128;
+    const int NB1 = a.I / TileLayout<MT, RW, CW>::HC;
     const int total = a.ctrl[2];
     for (;;) {
         __syncthreads();
@@ -817,7 +826,7 @@ __global__ __launch_bounds__(256) void k_ffn_persistent(FfnArgs a)
             // h and its scales were written with agent-coherent stores (through
             // this XCD's L2); once every wave has them acknowledged, one counter
             // increment publishes the tile.  No L2 write-back is needed.
-            ffn_tile<1, MT>(a, mt, nb, smem + kLutBytes, lut);
+            ffn_tile<1, MT, RW, CW>(a, mt, nb, smem);
             wait_vm<0>();
             __syncthreads();
             if (threadIdx.x == 0)
@@ -829,7 +838,7 @@ __global__ __launch_bounds__(256) void k_ffn_persistent(FfnArgs a)
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // drop any stale cached lines
             }
             __syncthreads();
-            ffn_tile<2, MT>(a, mt, nb, smem + kLutBytes, lut);
+            ffn_tile<2, MT, RW, CW>(a, mt, nb, smem);
         }
     }
 }
@@ -865,8 +874,13 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const uint
 }
 
 // ---------------------------------------------------------------------------
-// Offline prepack (canonical -> packed) and the dequant test export.
+// Offline weight prepack and the dequantisation export
 // ---------------------------------------------------------------------------
+// Canonical -> packed.  One thread per 16-byte FP4 slot (expert, 16-row
+// n-tile, 128-wide K chunk, lane): the slot's 32 codes keep the canonical
+// nibble order (the matrix cores read element k from nibble k%2 of byte k/2);
+// the slot's E8M0 byte goes to byte tile%4 of the lane's dword in the record
+// of its n-tile quad.  Flags any scale outside the lossless window.
 __global__ __launch_bounds__(256) void k_prepack(int E, int N, int K, const uint8_t* __restrict__ fin,
                                                  const uint8_t* __restrict__ ein,
                                                  uint8_t* __restrict__ fout, uint8_t* __restrict__ eout,
@@ -883,50 +897,60 @@ __global__ __launch_bounds__(256) void k_prepack(int E, int N, int K, const uint
     const size_t e = rec / C / (N / 16);
     const int n = tile * 16 + (lane & 15);
     const int k0 = c * 128 + (lane >> 4) * 32;
-    const uint4 v = *reinterpret_cast<const uint4*>(fin + (e * N + n) * (size_t)(K / 2) + k0 / 2);
-    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-    uint32_t code[32];
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const uint32_t byte = (in[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        code[2 * i] = byte & 15u;
-        code[2 * i + 1] = byte >> 4;
-    }
-    uint32_t outw[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int el = 8 * (j >> 2) + (j & 3);
-        outw[j >> 2] |= (code[el] | (code[el + 4] << 4)) << (8 * (j & 3));
-    }
-    *reinterpret_cast<uint4*>(fout + slot * 16) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    *reinterpret_cast<uint4*>(fout + slot * 16) =
+        *reinterpret_cast<const uint4*>(fin + (e * N + n) * (size_t)(K / 2) + k0 / 2);
     const uint8_t s = ein[(e * N + n) * (size_t)(K / 32) + k0 / 32];
-    eout[slot] = s;
+    eout[((e * (N / 64) + tile / 4) * C + c) * 256 + lane * 4 + (tile & 3)] = s;
     if (s < 127 - 8 || s > 127 + 6) atomicOr(bad, 1);
 }
 
+// Test export of the weights exactly as the matrix kernels see them: one wave
+// per (n-tile, chunk) record of expert `expert` runs the same block-scaled
+// MFMA as the GEMM tiles against one-hot E4M3 rows (1.0 at K = 16r + row), so
+// every output is a single product 1 * w * 2^b, exact in fp32; it is then
+// encoded as E4M3, which is exact inside the lossless window.  out is [N][K].
 __global__ __launch_bounds__(256) void k_dequant_export(int N, int K, int expert,
                                                         const uint8_t* __restrict__ fp4,
                                                         const uint8_t* __restrict__ e8,
                                                         uint8_t* __restrict__ out)
 {
-    __shared__ uint2 lut[256];
-    lut[threadIdx.x] = dequant_lut_entry(threadIdx.x);
-    __syncthreads();
     const int C = K / 128;
-    const size_t total = (size_t)(N / 16) * C * 64;
-    const size_t slot = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (slot >= total) return;
-    const int lane = (int)(slot & 63);
-    const size_t rec = slot >> 6;
+    const int lane = threadIdx.x & 63;
+    const size_t rec = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rec >= (size_t)(N / 16) * C) return;   // whole waves
     const int c = (int)(rec % C);
     const int tile = (int)(rec / C);
-    const size_t g = (size_t)expert * (N / 16) * C * 64 + slot;
-    const v8i o = dequant_slot(*reinterpret_cast<const uint4*>(fp4 + g * 16), lut[e8[g]]);
-    const int n = tile * 16 + (lane & 15);
-    const int k0 = c * 128 + (lane >> 4) * 32;
-    uint4* dst = reinterpret_cast<uint4*>(out + (size_t)n * K + k0);
-    dst[0] = make_uint4((uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]);
-    dst[1] = make_uint4((uint32_t)o[4], (uint32_t)o[5], (uint32_t)o[6], (uint32_t)o[7]);
+    const uint4 b = *reinterpret_cast<const uint4*>(fp4 + (((size_t)expert * (N / 16) + tile) * C + c) * 1024 + lane * 16);
+    const int sb = *reinterpret_cast<const int*>(e8 + (((size_t)expert * (N / 64) + tile / 4) * C + c) * 256 + lane * 4);
+    const int g = lane >> 4, i = lane & 15;
+    const int one = 0x38 << (8 * (i & 3));      // E4M3 1.0 in byte i%4
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        v8i av = {0, 0, 0, 0, 0, 0, 0, 0};
+        // row i of A has its 1.0 at K = 16r + i: dwords 0-3 hold K 16g.., 4-7 hold K 64+16g..
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            av[d] = (r == g && (i >> 2) == d) ? one : 0;
+            av[4 + d] = (r == g + 4 && (i >> 2) == d) ? one : 0;
+        }
+        const v4f p = mfma_e4m3_e2m1_sel(tile & 3, av, b, sb);
+        // A zero product loses its sign in the accumulator (-0 + +0 = +0);
+        // the E4M3 byte of a zero weight keeps the sign of its code, read from
+        // the lane that holds it: lane (r/2)*16 + i, dword 2*(r%2) + g/2,
+        // nibble 4*(g%2) + q.
+        const int src = (r >> 1) * 16 + i;
+        const uint32_t w0 = (uint32_t)__shfl((int)((r & 1) ? b.z : b.x), src);
+        const uint32_t w1 = (uint32_t)__shfl((int)((r & 1) ? b.w : b.y), src);
+        const uint32_t codes = (g >> 1) ? w1 : w0;
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const uint32_t neg = (codes >> (4 * (4 * (g & 1) + q) + 3)) & 1u;
+            const uint32_t byte = p[q] == 0.0f ? neg << 7 : e4m3_rne_sat(p[q]);
+            word |= byte << (8 * q);
+        }
+        *reinterpret_cast<uint32_t*>(out + (size_t)(tile * 16 + i) * K + c * 128 + 16 * r + 4 * g) = word;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -999,78 +1023,93 @@ static hipError_t allow_lds(F* kernel, size_t bytes, bool& done)
     return r;
 }
 
-template <int PHASE, int MT>
+template <int PHASE, int MT, int RW, int CW>
 static hipError_t launch_ffn_t(const FfnArgs& a, hipStream_t s)
 {
+    using TL = TileLayout<MT, RW, CW>;
     static bool lds_ok = false;
-    const int NB = PHASE == 1 ? a.I / 128 : a.H / 256;
-    const size_t lds = kLutBytes + TileLayout<MT>::BYTES;
-    if (allow_lds(k_ffn<PHASE, MT>, lds, lds_ok) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_ffn<PHASE, MT>), dim3((unsigned)a.n_mt_bound * NB), dim3(256), lds, s, a, NB);
+    const int NB = PHASE == 1 ? a.I / TL::HC : a.H / TL::OC;
+    const size_t lds = TL::BYTES;
+    if (allow_lds(k_ffn<PHASE, MT, RW, CW>, lds, lds_ok) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_ffn<PHASE, MT, RW, CW>), dim3((unsigned)a.n_mt_bound * NB), dim3(TL::NT), lds, s, a, NB);
     return hipGetLastError();
 }
 
-hipError_t launch_ffn(int phase, int MT, const FfnArgs& a, hipStream_t s)
+template <int PHASE, int CW>
+static hipError_t launch_ffn_cw(int MT, const FfnArgs& a, hipStream_t s)
 {
-    switch (MT * 2 + (phase - 1)) {
-    case 2: return launch_ffn_t<1, 1>(a, s);
-    case 3: return launch_ffn_t<2, 1>(a, s);
-    case 4: return launch_ffn_t<1, 2>(a, s);
-    case 5: return launch_ffn_t<2, 2>(a, s);
-    case 8: return launch_ffn_t<1, 4>(a, s);
-    case 9: return launch_ffn_t<2, 4>(a, s);
-    case 16: return launch_ffn_t<1, 8>(a, s);
-    case 17: return launch_ffn_t<2, 8>(a, s);
+    switch (MT) {
+    case 1: return launch_ffn_t<PHASE, 1, 1, CW>(a, s);
+    case 2: return launch_ffn_t<PHASE, 2, 1, CW>(a, s);
+    case 4: return launch_ffn_t<PHASE, 4, 1, CW>(a, s);
+    case 8: return launch_ffn_t<PHASE, 8, 2, CW>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int MT>
-static size_t persistent_lds()
+hipError_t launch_ffn(int phase, int MT, int CW, const FfnArgs& a, hipStream_t s)
 {
-    return kLutBytes + TileLayout<MT>::BYTES;
+    if (CW == 2) return phase == 1 ? launch_ffn_cw<1, 2>(MT, a, s) : launch_ffn_cw<2, 2>(MT, a, s);
+    if (CW == 4) return phase == 1 ? launch_ffn_cw<1, 4>(MT, a, s) : launch_ffn_cw<2, 4>(MT, a, s);
+    return hipErrorInvalidValue;
 }
 
-template <int MT>
+template <int MT, int RW, int CW>
 static int persistent_occupancy()
 {
+    using TL = TileLayout<MT, RW, CW>;
     static bool lds_ok = false;
-    allow_lds(k_ffn_persistent<MT>, persistent_lds<MT>(), lds_ok);
+    if (allow_lds(k_ffn_persistent<MT, RW, CW>, TL::BYTES, lds_ok) != hipSuccess) return 1;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_ffn_persistent<MT>, 256, persistent_lds<MT>()) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_ffn_persistent<MT, RW, CW>, TL::NT, TL::BYTES) !=
         hipSuccess)
         n = 1;
     return n < 1 ? 1 : n;
 }
 
-int persistent_blocks_per_cu(int MT)
+template <int CW>
+static int persistent_occupancy_cw(int MT)
 {
     switch (MT) {
-    case 1: return persistent_occupancy<1>();
-    case 2: return persistent_occupancy<2>();
-    case 4: return persistent_occupancy<4>();
-    default: return persistent_occupancy<8>();
+    case 1: return persistent_occupancy<1, 1, CW>();
+    case 2: return persistent_occupancy<2, 1, CW>();
+    case 4: return persistent_occupancy<4, 1, CW>();
+    default: return persistent_occupancy<8, 2, CW>();
     }
 }
 
-template <int MT>
+int persistent_blocks_per_cu(int MT, int CW)
+{
+    return CW == 4 ? persistent_occupancy_cw<4>(MT) : persistent_occupancy_cw<2>(MT);
+}
+
+template <int MT, int RW, int CW>
 static hipError_t launch_persistent_t(const FfnArgs& a, int grid, hipStream_t s)
 {
+    using TL = TileLayout<MT, RW, CW>;
     static bool lds_ok = false;
-    if (allow_lds(k_ffn_persistent<MT>, persistent_lds<MT>(), lds_ok) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_ffn_persistent<MT>, dim3(grid), dim3(256), persistent_lds<MT>(), s, a);
+    if (allow_lds(k_ffn_persistent<MT, RW, CW>, TL::BYTES, lds_ok) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_ffn_persistent<MT, RW, CW>), dim3(grid), dim3(TL::NT), TL::BYTES, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_ffn_persistent(int MT, const FfnArgs& a, int grid, hipStream_t s)
+template <int CW>
+static hipError_t launch_persistent_cw(int MT, const FfnArgs& a, int grid, hipStream_t s)
 {
     switch (MT) {
-    case 1: return launch_persistent_t<1>(a, grid, s);
-    case 2: return launch_persistent_t<2>(a, grid, s);
-    case 4: return launch_persistent_t<4>(a, grid, s);
-    case 8: return launch_persistent_t<8>(a, grid, s);
+    case 1: return launch_persistent_t<1, 1, CW>(a, grid, s);
+    case 2: return launch_persistent_t<2, 1, CW>(a, grid, s);
+    case 4: return launch_persistent_t<4, 1, CW>(a, grid, s);
+    case 8: return launch_persistent_t<8, 2, CW>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_ffn_persistent(int MT, int CW, const FfnArgs& a, int grid, hipStream_t s)
+{
+    if (CW == 2) return launch_persistent_cw<2>(MT, a, grid, s);
+    if (CW == 4) return launch_persistent_cw<4>(MT, a, grid, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* w, uint16_t* out,
@@ -1118,6 +1157,14 @@ int choose_mt(int T, int k, int E)
     if (avg <= 40.0) return 2;
     if (avg <= 96.0) return 4;
     return 8;
+}
+
+int choose_cw(int MT, int H, int I)
+{
+    // Small m-tiles stream weights: two-wave-column tiles keep two blocks per
+    // CU.  Large m-tiles are MFMA-bound: four wave columns (and two row groups
+    // at MT = 8, two waves per SIMD) halve the operand traffic per MFMA.
+    return (MT >= 4 && I % 256 == 0 && H % 512 == 0) ? 4 : 2;
 }
 
 }  // namespace v4moe

@@ -69,13 +69,16 @@ typedef struct {
  *   e8m0 uint8 [E][N][K/32]    sub-block scale 2^b stored as the byte 127+b
  *   blk  fp32  [E][N/128][K/128]  scale of each 128x128 block
  * PACKED layout (output of moe_prepack_weights; what every compute entry
- * point reads).  Same byte counts; blk is unchanged.  For each expert, each
- * 16-row group n16 and each 128-wide K chunk c, a 1 KiB record holds 64
- * slots of 16 bytes; slot s covers row n16*16 + (s%16) and the 32 elements
- * k = c*128 + (s/16)*32 + [0,32); byte j of a slot holds element 8*(j/4)+j%4
- * of those 32 in its low nibble and element 8*(j/4)+j%4+4 in its high nibble.
- *   fp4  uint8 [E][N/16][K/128][64][16]
- *   e8m0 uint8 [E][N/16][K/128][64]   (the scale byte of slot s)
+ * point reads).  Same byte counts; blk is unchanged.  N must be a multiple
+ * of 64 (true for every matrix: N is I or H).
+ *   fp4  uint8 [E][N/16][K/128][64][16]  for each expert, 16-row group n16 and
+ *        128-wide K chunk c, a 1 KiB record of 64 slots of 16 bytes; slot s
+ *        holds row n16*16 + s%16, elements k = c*128 + (s/16)*32 + [0, 32),
+ *        in canonical nibble order (element k in byte k/2, low nibble when k
+ *        is even);
+ *   e8m0 uint8 [E][N/64][K/128][64][4]   for each group of four consecutive
+ *        n16 and each chunk c, a 256-byte record; byte t of its dword s is the
+ *        sub-block scale of slot s of n16 = 4*group + t;
  *   blk  fp32  [E][N/128][K/128]
  */
 typedef struct {
@@ -183,9 +186,12 @@ int moe_prepack_weights(const v4moe_dims* d, const v4moe_experts* canonical,
                         const v4moe_experts* packed, void* workspace, size_t ws_bytes,
                         void* stream);
 
-/* Test export of the dequantisation used inside the matrix kernels:
- * expert `expert` of the PACKED matrix m (N rows, K inputs) -> E4M3 bytes
- * [N][K] in canonical row-major order. */
+/* Test export of the weights exactly as the matrix kernels consume them:
+ * expert `expert` of the PACKED matrix m (N rows, K inputs; N % 64 == 0,
+ * K % 128 == 0) is read through the same block-scaled FP8 x FP4 MFMA path as
+ * the GEMMs and written as E4M3 bytes [N][K] in canonical row-major order
+ * (P1 §4: inside the window every FP4 value times its sub-block scale is an
+ * E4M3 value, so the bytes are exact; a zero keeps its code's sign). */
 int moe_dequant_fp8(const v4moe_mat* m, int32_t N, int32_t K, int32_t expert,
                     uint8_t* out, void* stream);
 
