@@ -145,7 +145,6 @@ int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws,
     const int NB1 = d->I / (64 * L.CW), NB2 = d->H / (128 * L.CW);
     hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
-    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return V4MOE_ELAUNCH;
     int per = di->persist_per_cu[L.CW == 4][L.MT];
     int grid = di->cus * (per > 0 ? per : 1);
     // Scheduling lag in waves: enough linear1 tiles between a wave's linear1 and
@@ -159,6 +158,7 @@ int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws,
                            reinterpret_cast<int32_t*>(ws + L.mt_row0),
                            reinterpret_cast<uint32_t*>(ws + L.queue), s) != hipSuccess)
         return V4MOE_ELAUNCH;
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return V4MOE_ELAUNCH;
     if (persistent) {
         const int max_items = L.n_mt_bound * (NB1 + NB2);
         if (grid > max_items) grid = max_items;

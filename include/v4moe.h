@@ -198,8 +198,9 @@ int moe_dequant_fp8(const v4moe_mat* m, int32_t N, int32_t K, int32_t expert,
 /* Profiling hook (no effect on results).  start/stop are hipEvent_t handles
  * created by the caller (or NULL to clear).  The next moe_expert_ffn or
  * moe_layer_forward call made by this host thread records `start` on its
- * stream just before its expert-FFN kernels and `stop` just after them, then
- * forgets both; elapsed time between them is the expert FFN's device time. */
+ * stream just before its expert-FFN matrix kernels (after the tile-list
+ * build) and `stop` just after them, then forgets both; elapsed time between
+ * them is the device time of the FFN kernels alone. */
 void moe_time_next_ffn(void* start_event, void* stop_event);
 
 /* Text for an error code. */
