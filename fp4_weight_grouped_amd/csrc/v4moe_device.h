@@ -19,34 +19,59 @@ constexpr int kWave = 64;
 // bf16 bits -> fp32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+// fp32 pair -> two bf16 (a in the low half), round to nearest even
+// (v_cvt_pk_bf16_f32; equal to rounding the fp32 bit pattern for every finite
+// input).
+__device__ __forceinline__ uint32_t bf16x2(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
-// fp32 -> OCP E4M3 byte: nearest value, ties to even mantissa, magnitudes at or
-// beyond 464 (half an ulp above 448) saturate to +-448, never NaN.  Works on
-// the fp32 bit pattern: normal results keep the top 3 mantissa bits with
-// round-to-nearest-even on the 20 dropped bits (a carry moves into the
-// exponent field); results below 2^-6 are multiples of 2^-9.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
+// fp32 pair -> two OCP E4M3 bytes (a in the low byte): nearest value, ties to
+// even, magnitudes beyond 448 saturate to +-448, never NaN.  gfx950's
+// v_cvt_pk_fp8_f32 rounds to nearest even but turns overflow into NaN, so the
+// inputs are clamped to +-448 first (a value that rounds to 448 stays 448).
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b)
 {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    if (a >= 0x43E80000u)                         // |v| >= 464
-        return sign | 0x7Eu;
-    if (a < 0x3C800000u) {                        // |v| < 2^-6
-        float s = __uint_as_float(a) * 512.0f;    // exact scaling, in [0, 8)
-        return sign | (uint32_t)__builtin_rintf(s);
-    }
-    uint32_t q = ((((a >> 23) - 127u + 7u)) << 3) | ((a >> 20) & 7u);
-    uint32_t rem = a & 0xFFFFFu;
-    q += (rem > 0x80000u) | ((rem == 0x80000u) & (q & 1u));
-    q = q > 0x7Eu ? 0x7Eu : q;
-    return sign | q;
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// SiLU(g) * u with the hardware exp2 and reciprocal (about 2 ulp; the result
+// is requantised to E4M3 right after).
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in every lane
+// of the row: rotations by 1, 2, 4 and 8 within the row.
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
+    return v;
+}
+
+// The value of lane l^1 (DPP quad_perm [1,0,3,2]).
+__device__ __forceinline__ float lane_pair_swap(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
+// Lanes l (even) and l+1 hold adjacent columns c, c+1 of two rows ra and rb
+// (values va, vb).  Returns the pair of row ra (even lane) or of row rb (odd
+// lane) in column order, so that each lane can write two adjacent elements.
+__device__ __forceinline__ float2 column_pair(float va, float vb, bool odd)
+{
+    const float recv = lane_pair_swap(odd ? va : vb);
+    return odd ? make_float2(recv, vb) : make_float2(va, recv);
 }
 
 // 16x16 output tile over one 128-wide K chunk on gfx950's block-scaled

@@ -234,12 +234,8 @@ __global__ __launch_bounds__(256) void k_quant_x(int T, int H, const uint16_t* _
     for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if (!ok) return;
     const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-        lo |= e4m3_rne_sat(f[u] / s) << (8 * u);
-        hi |= e4m3_rne_sat(f[u + 4] / s) << (8 * u);
-    }
+    const uint32_t lo = e4m3x2(f[0] / s, f[1] / s) | (e4m3x2(f[2] / s, f[3] / s) << 16);
+    const uint32_t hi = e4m3x2(f[4] / s, f[5] / s) | (e4m3x2(f[6] / s, f[7] / s) << 16);
     *reinterpret_cast<uint2*>(xq + idx * 8) = make_uint2(lo, hi);
     if ((idx & 15) == 0) xs[idx / 16] = s;
 }
@@ -714,10 +710,11 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
 
     if (PHASE == 1) {
         // h = SiLU(g) * u, then E4M3 per (row, 128 columns of h): the amax of a
-        // row is reduced over the 16 lanes of a row group of the MFMA result,
-        // then over the two waves that share the 128 columns.
+        // row is reduced over the 16 lanes of a row group of the MFMA result
+        // (one DPP row), then over the two waves that share the 128 columns.
         uint8_t* stage = smem;                                      // [M][SP1]
         float* red = reinterpret_cast<float*>(smem + TL::STAGE);    // [NW][RG], ring stage 1
+        const bool odd = lane & 1;
         float hv[MTW][4][4];
 #pragma unroll
         for (int i = 0; i < MTW; i++)
@@ -726,30 +723,38 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
                 float mx = 0.0f;
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    const float h = swiglu(acc[i][j][q], acc[i][4 + j][q]);
+                    const float h = silu_mul(acc[i][j][q], acc[i][4 + j][q]);
                     hv[i][j][q] = h;
                     mx = fmaxf(mx, fabsf(h));
                 }
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+                mx = row16_max(mx);
                 if ((lane & 15) == 0) red[w * RG + i * 16 + (lane >> 4) * 4 + q] = mx;
             }
         __syncthreads();
         const int wp = rg * CW + (cg & ~1);
 #pragma unroll
-        for (int i = 0; i < MTW; i++)
+        for (int i = 0; i < MTW; i++) {
+            float inv[4];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int rl = i * 16 + (lane >> 4) * 4 + q;
-                const int r = rg * RG + rl;
                 const float amax = fmaxf(red[wp * RG + rl], red[(wp + 1) * RG + rl]);
                 const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    stage[r * TL::SP1 + 64 * cg + 16 * j + (lane & 15)] = (uint8_t)e4m3_rne_sat(hv[i][j][q] / s);
-                if ((cg & 1) == 0 && (lane & 15) == 0 && r < rows)
-                    store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * (CW / 2) + (cg >> 1), s);
+                inv[q] = 1.0f / s;
+                if ((cg & 1) == 0 && (lane & 15) == 0 && rg * RG + rl < rows)
+                    store_coherent(a.hs + (size_t)(row0 + rg * RG + rl) * a.hs_stride + nb * (CW / 2) + (cg >> 1), s);
             }
+            // two adjacent columns per lane: even lanes write rows 4g+2m, odd lanes 4g+2m+1
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int m = 0; m < 2; m++) {
+                    const float2 pr = column_pair(hv[i][j][2 * m] * inv[2 * m], hv[i][j][2 * m + 1] * inv[2 * m + 1], odd);
+                    const int r = rg * RG + i * 16 + (lane >> 4) * 4 + 2 * m + (odd ? 1 : 0);
+                    *reinterpret_cast<uint16_t*>(stage + r * TL::SP1 + 64 * cg + 16 * j + (lane & 14)) =
+                        (uint16_t)e4m3x2(pr.x, pr.y);
+                }
+        }
         __syncthreads();
         constexpr int SEGS = TL::HC / 16;
         for (int s = tid; s < M * SEGS; s += NT) {
@@ -764,15 +769,19 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         // of every row group at a time.
         uint16_t* stage = reinterpret_cast<uint16_t*>(smem);        // [RW*16][SP2]
         constexpr int SEGS = TL::OC / 8;
+        const bool odd = lane & 1;
 #pragma unroll
         for (int i = 0; i < MTW; i++) {
             if (i * 16 < rows) {
 #pragma unroll
                 for (int j = 0; j < 8; j++)
 #pragma unroll
-                    for (int q = 0; q < 4; q++)
-                        stage[(rg * 16 + (lane >> 4) * 4 + q) * TL::SP2 + 128 * cg + 16 * j + (lane & 15)] =
-                            (uint16_t)f32_to_bf16(acc[i][j][q]);
+                    for (int m = 0; m < 2; m++) {
+                        const float2 pr = column_pair(acc[i][j][2 * m], acc[i][j][2 * m + 1], odd);
+                        const int r = rg * 16 + (lane >> 4) * 4 + 2 * m + (odd ? 1 : 0);
+                        *reinterpret_cast<uint32_t*>(stage + r * TL::SP2 + 128 * cg + 16 * j + (lane & 14)) =
+                            bf16x2(pr.x, pr.y);
+                    }
                 __syncthreads();
                 for (int s = tid; s < RW * 16 * SEGS; s += NT) {
                     const int rs = s / SEGS, sg = s % SEGS;
@@ -865,11 +874,8 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const uint
             acc[2 * u + 1] = __builtin_fmaf(wj, bf16_to_f32(q[u] >> 16), acc[2 * u + 1]);
         }
     }
-    uint4 o;
-    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-    o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-    o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+    const uint4 o = make_uint4(bf16x2(acc[0], acc[1]), bf16x2(acc[2], acc[3]), bf16x2(acc[4], acc[5]),
+                               bf16x2(acc[6], acc[7]));
     *reinterpret_cast<uint4*>(out + t * H + c * 8) = o;
 }
 
@@ -942,12 +948,11 @@ __global__ __launch_bounds__(256) void k_dequant_export(int N, int K, int expert
         const uint32_t w0 = (uint32_t)__shfl((int)((r & 1) ? b.z : b.x), src);
         const uint32_t w1 = (uint32_t)__shfl((int)((r & 1) ? b.w : b.y), src);
         const uint32_t codes = (g >> 1) ? w1 : w0;
-        uint32_t word = 0;
+        uint32_t word = e4m3x2(p[0], p[1]) | (e4m3x2(p[2], p[3]) << 16);
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const uint32_t neg = (codes >> (4 * (4 * (g & 1) + q) + 3)) & 1u;
-            const uint32_t byte = p[q] == 0.0f ? neg << 7 : e4m3_rne_sat(p[q]);
-            word |= byte << (8 * q);
+            if (p[q] == 0.0f) word = (word & ~(0xFFu << (8 * q))) | (neg << (8 * q + 7));
         }
         *reinterpret_cast<uint32_t*>(out + (size_t)(tile * 16 + i) * K + c * 128 + 16 * r + 4 * g) = word;
     }

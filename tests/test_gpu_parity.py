@@ -196,6 +196,37 @@ def test_single_token_calls():
     check_out(got, ref["out"], "T=1 calls")
 
 
+def test_dispatch_payload_every_bf16_value():
+    """The FP8 dispatch payload (E4M3 codes and fp32 scales of x) bit-exact
+    for every finite bf16 value: once in groups of similar magnitude (so the
+    codes exercise every rounding case) and once in random groups (zeros,
+    saturation, subnormal codes).  Routing is bypassed with fixed valid ids."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (pats & 0x7F80) != 0x7F80
+    vals = np.where(finite, pats, 0).astype(np.uint16)
+    mags = (vals.astype(np.uint32) << 16).view(np.float32)
+    by_mag = vals[np.argsort(np.abs(mags), kind="stable")]
+    shuffled = np.random.default_rng(7).permutation(vals)
+    H, E, k = 256, 8, 2
+    x = np.concatenate([by_mag, shuffled]).reshape(-1, H)
+    T = x.shape[0]
+    ref_q, ref_s = oracle.quant_x(x)
+    d = v4moe.dims(T, H, 128, E, k)
+    ids = torch.from_numpy((np.arange(T * k, dtype=np.int32) % E).reshape(T, k)).to(DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    sp = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    pp = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    xq = torch.empty((T, H), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((T, H // 128), dtype=torch.float32, device=DEV)
+    ws = torch.empty(v4moe.moe_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    xd = torch.from_numpy(x.view(np.int16)).to(DEV)
+    print(f"[payload] T={T} H={H}", flush=True)
+    v4moe.moe_permute(d, xd, ids, off, sp, pp, xq, xs, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), ref_q)
+
+
 def test_zero_tokens():
     inp = inputs.make("tiny", T=0)
     layer = layer_for(inputs.make("tiny"))
