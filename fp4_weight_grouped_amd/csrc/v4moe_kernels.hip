@@ -31,93 +31,186 @@ namespace v4moe {
 // Routing
 // ---------------------------------------------------------------------------
 
-// Router logits.  Lane = token (64 tokens per block), wave w = experts
-// eb0 + w*ES .. +ES (EB = 4*ES per block).  The block's slice of W_r is staged
-// through LDS 256 rows of h at a time (double buffered, the next slice loaded
-// into registers while the current one is used); every wave reads its ES
-// weights of a row with one broadcast LDS read, and each lane streams its own
-// row of x.  Each lane runs ES independent fp32 fma chains over h ascending
-// from +0; the optional bias is one fp32 add afterwards.  z is [T][E].
-// Needs E % 4 == 0 (16-byte rows of the weight slice); otherwise
-// k_route_logits_any is used.
-template <int ES>
+// Wait until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct-to-LDS copy: each lane moves 16 bytes from its own global address to
+// lds_base + lane*16 (lds_base wave-uniform, in M0); lanes outside EXEC do not
+// write.  As inline asm it is invisible to the compiler's wait insertion:
+// completion is awaited with an explicit wait_vm.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+
+// Router logits.  Block = 4 waves, 64*TS tokens x 4*ES experts: lane l runs
+// the chains of tokens t0 + l + 64*i (i < TS) for the ES experts of its wave,
+// TS*ES independent fp32 fma chains over h in increasing order from +0; the
+// optional bias is one fp32 add afterwards.  The block's slice of W_r is
+// staged through LDS HC rows at a time, transposed to expert-major rows (padded
+// by 4 floats against bank conflicts), so one broadcast LDS read gives four
+// consecutive h of one expert; the next slice is loaded into registers while
+// the current one is used.  With XL the tokens' x rows are staged too, by
+// direct-to-LDS loads issued a stage ahead (rows padded by 16 bytes), for
+// batches too small to hide global-load latency behind a lane's few chains;
+// otherwise each lane reads its x rows from global memory one step ahead.
+// z is [T][E].  Needs E % (4*ES) == 0 and H % HC == 0.
+template <int TS, int ES, int HC, bool XL>
 __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
                                                       const uint16_t* __restrict__ x,
                                                       const float* __restrict__ wr,
                                                       const float* __restrict__ bias,
                                                       float* __restrict__ z)
 {
-    constexpr int EB = 4 * ES;
-    constexpr int HC = 256;
-    constexpr int F4 = HC * EB / 4;          // float4 per stage
-    constexpr int LD = F4 / 256;             // float4 loads per thread per stage
-    __shared__ float4 wt[2][F4];
+    constexpr int EB = 4 * ES;               // experts per block
+    constexpr int PITCH = HC + 4;            // floats per expert row in LDS
+    constexpr int NV = HC * EB / 4;          // float4 of W per stage
+    constexpr int LD = (NV + 255) / 256;     // float4 loads per thread per stage
+    constexpr int XP = HC / 8 + 1;           // uint4 per staged x row
+    constexpr int NSLOT = XL ? 64 * TS * XP : 0;      // uint4 slots of staged x per stage
+    constexpr int HS = XL ? 64 : 8;          // h per inner step (one LDS wait per step)
+    __shared__ __align__(16) float wt[2][EB * PITCH];
+    __shared__ __align__(16) uint4 xt[XL ? 2 : 1][XL ? 64 * TS * XP : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t = blockIdx.x * 64 + lane;
+    const int t0 = blockIdx.x * 64 * TS;
     const int eb0 = blockIdx.y * EB;
     const int nst = H / HC;
-    const float* wsrc[LD];
-#pragma unroll
-    for (int i = 0; i < LD; i++) {
-        const int f = tid + 256 * i;
-        const int row = f / (EB / 4), c4 = f % (EB / 4);
-        wsrc[i] = wr + (size_t)row * E + min(eb0 + c4 * 4, E - 4);
-    }
+
+    // staging: float4 f of the [HC][EB] slice = row f / (EB/4), experts 4*(f % (EB/4)) .. +3;
+    // uint4 g of the x slice = token row g / (HC/8), 8 h at column g % (HC/8)
     float4 nxt[LD];
+    // x slice of stage st into buffer buf: DMA k (of this wave: k = w, w+4, ...)
+    // fills slots 64k .. 64k+63; slot = row*XP + col, the padding column
+    // repeats the last real one.
+    auto dma_x = [&](int st, int buf) {
+        if (XL) {
+            const uint32_t base = (uint32_t)(uintptr_t)&xt[XL ? buf : 0][0];
+            for (int k = w; k * 64 < NSLOT; k += 4) {
+                const int slot = 64 * k + lane;
+                const int row = slot / XP, col = min(slot % XP, HC / 8 - 1);
+                if (slot < NSLOT)
+                    dma16(x + (size_t)min(t0 + row, T - 1) * H + st * HC + col * 8,
+                          __builtin_amdgcn_readfirstlane(base + k * 1024));
+            }
+        }
+    };
+    auto load_stage = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < LD; i++) nxt[i] = *reinterpret_cast<const float4*>(wsrc[i]);
+        for (int i = 0; i < LD; i++) {
+            const int f = tid + 256 * i;
+            if (f < NV)
+                nxt[i] = *reinterpret_cast<const float4*>(wr + (size_t)(st * HC + f / (EB / 4)) * E + eb0 +
+                                                          4 * (f % (EB / 4)));
+        }
+    };
+    auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < LD; i++) wt[0][tid + 256 * i] = nxt[i];
+        for (int i = 0; i < LD; i++) {
+            const int f = tid + 256 * i;
+            if (f < NV) {
+                const int h = f / (EB / 4), e4 = 4 * (f % (EB / 4));
+                wt[buf][(e4 + 0) * PITCH + h] = nxt[i].x;
+                wt[buf][(e4 + 1) * PITCH + h] = nxt[i].y;
+                wt[buf][(e4 + 2) * PITCH + h] = nxt[i].z;
+                wt[buf][(e4 + 3) * PITCH + h] = nxt[i].w;
+            }
+        }
+    };
+    dma_x(0, 0);
+    load_stage(0);
+    store_stage(0);
+    wait_vm<0>();
     __syncthreads();
 
-    const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)min(t, T - 1) * H);
-    float acc[ES];
+    const uint4* xp[TS];
 #pragma unroll
-    for (int j = 0; j < ES; j++) acc[j] = 0.0f;
+    for (int i = 0; i < TS; i++) xp[i] = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + lane + 64 * i, T - 1) * H);
+    float acc[TS][ES];
+#pragma unroll
+    for (int i = 0; i < TS; i++)
+#pragma unroll
+        for (int j = 0; j < ES; j++) acc[i][j] = 0.0f;
+
+    // x of 8 consecutive h of token i, for the step starting at stage-relative h
+    auto xload = [&](int s, int i, int h) -> uint4 {
+        if (XL) return xt[XL ? (s & 1) : 0][(lane + 64 * i) * XP + h / 8];
+        const int g = s * HC + h;
+        return xp[i][(g < H ? g : H - 8) / 8];
+    };
     for (int s = 0; s < nst; s++) {
         if (s + 1 < nst) {
-#pragma unroll
-            for (int i = 0; i < LD; i++)
-                nxt[i] = *reinterpret_cast<const float4*>(wsrc[i] + (size_t)(s + 1) * HC * E);
+            dma_x(s + 1, (s + 1) & 1);
+            load_stage(s + 1);
         }
-        const float* wcur = reinterpret_cast<const float*>(wt[s & 1]);
-        uint4 xx = xp[s * (HC / 8)];
-        for (int h = 0; h < HC; h += 8) {
-            const uint4 xn = (h + 8 < HC) ? xp[(s * HC + h + 8) / 8] : xx;
-            const uint32_t q[4] = {xx.x, xx.y, xx.z, xx.w};
+        const float* wb = wt[s & 1] + w * ES * PITCH;
+        float4 wc[ES][HS / 4];
+        uint4 xc[TS][HS / 8];
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
-                const float xv = bf16_to_f32(u & 1 ? q[u / 2] >> 16 : q[u / 2] & 0xFFFFu);
-                const float* wrow = wcur + (h + u) * EB + w * ES;
-                if (ES >= 4) {
+        for (int j = 0; j < ES; j++)
 #pragma unroll
-                    for (int j4 = 0; j4 < ES / 4; j4++) {
-                        const float4 wv = *reinterpret_cast<const float4*>(wrow + 4 * j4);
-                        acc[4 * j4 + 0] = __builtin_fmaf(xv, wv.x, acc[4 * j4 + 0]);
-                        acc[4 * j4 + 1] = __builtin_fmaf(xv, wv.y, acc[4 * j4 + 1]);
-                        acc[4 * j4 + 2] = __builtin_fmaf(xv, wv.z, acc[4 * j4 + 2]);
-                        acc[4 * j4 + 3] = __builtin_fmaf(xv, wv.w, acc[4 * j4 + 3]);
+            for (int v = 0; v < HS / 4; v++) wc[j][v] = *reinterpret_cast<const float4*>(wb + j * PITCH + 4 * v);
+#pragma unroll
+        for (int i = 0; i < TS; i++)
+#pragma unroll
+            for (int v = 0; v < HS / 8; v++) xc[i][v] = xload(s, i, 8 * v);
+#pragma unroll 1
+        for (int h = 0; h < HC; h += HS) {
+            // operands of the next step (this stage's last step re-reads its own)
+            const int hn = h + HS < HC ? h + HS : h;
+            float4 wn[ES][HS / 4];
+            uint4 xn[TS][HS / 8];
+#pragma unroll
+            for (int j = 0; j < ES; j++)
+#pragma unroll
+                for (int v = 0; v < HS / 4; v++) wn[j][v] = *reinterpret_cast<const float4*>(wb + j * PITCH + hn + 4 * v);
+#pragma unroll
+            for (int i = 0; i < TS; i++)
+#pragma unroll
+                for (int v = 0; v < HS / 8; v++) xn[i][v] = xload(s, i, (XL ? hn : h + HS) + 8 * v);
+#pragma unroll
+            for (int u = 0; u < HS; u++) {
+#pragma unroll
+                for (int i = 0; i < TS; i++) {
+                    const uint4 xq = xc[i][u / 8];
+                    const int k8 = u & 7;
+                    const uint32_t q = k8 < 2 ? xq.x : k8 < 4 ? xq.y : k8 < 6 ? xq.z : xq.w;
+                    const float xv = __uint_as_float((u & 1) ? (q & 0xFFFF0000u) : (q << 16));
+#pragma unroll
+                    for (int j = 0; j < ES; j++) {
+                        const float4 v = wc[j][u >> 2];
+                        const float wv = (u & 3) == 0 ? v.x : (u & 3) == 1 ? v.y : (u & 3) == 2 ? v.z : v.w;
+                        acc[i][j] = __builtin_fmaf(xv, wv, acc[i][j]);
                     }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < ES; j++) acc[j] = __builtin_fmaf(xv, wrow[j], acc[j]);
                 }
             }
-            xx = xn;
-        }
-        if (s + 1 < nst) {
 #pragma unroll
-            for (int i = 0; i < LD; i++) wt[(s + 1) & 1][tid + 256 * i] = nxt[i];
+            for (int j = 0; j < ES; j++)
+#pragma unroll
+                for (int v = 0; v < HS / 4; v++) wc[j][v] = wn[j][v];
+#pragma unroll
+            for (int i = 0; i < TS; i++)
+#pragma unroll
+                for (int v = 0; v < HS / 8; v++) xc[i][v] = xn[i][v];
         }
+        if (s + 1 < nst) store_stage((s + 1) & 1);
+        if (XL) wait_vm<0>();
         __syncthreads();
     }
-    if (t < T) {
 #pragma unroll
-        for (int j = 0; j < ES; j++) {
-            const int e = eb0 + w * ES + j;
-            if (e < E) {
-                float v = acc[j];
+    for (int i = 0; i < TS; i++) {
+        const int t = t0 + lane + 64 * i;
+        if (t < T) {
+#pragma unroll
+            for (int j = 0; j < ES; j++) {
+                const int e = eb0 + w * ES + j;
+                float v = acc[i][j];
                 if (bias) v = v + bias[e];
                 z[(size_t)t * E + e] = v;
             }
@@ -503,12 +596,6 @@ __device__ __forceinline__ T* uniform(T* p)
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
-}
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 // wait until at most OPS*k operations are outstanding, k = 0..2 at run time
 template <int OPS>
@@ -972,18 +1059,21 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
                            token_ids, ids, w);
         return hipGetLastError();
     }
-    // experts per wave: enough waves to fill the chip at small T, more reuse of
-    // each x row at large T
-    const int tg = (T + 63) / 64;
-    if (E % 4 != 0 || E < 4) {
+    // Large batches: two tokens x eight experts per lane (W reads shared by
+    // the tokens, x conversions by the experts).  Small batches: one chain per
+    // lane, for as many waves as possible (each chain is H dependent fmas).
+    if (E % 4 != 0 || H % 256 != 0) {
         hipLaunchKernelGGL(k_route_logits_any, dim3(blocks_for((size_t)T * E, 256)), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
-    } else if ((size_t)tg * E >= 256 * 32 && E % 32 == 0) {
-        hipLaunchKernelGGL(k_route_logits<8>, dim3(tg, E / 32), dim3(256), 0, s, T, H, E, x, wr, bias, z);
-    } else if ((size_t)tg * E >= 256 * 8 && E % 8 == 0) {
-        hipLaunchKernelGGL(k_route_logits<2>, dim3(tg, E / 8), dim3(256), 0, s, T, H, E, x, wr, bias, z);
+    } else if (E % 32 == 0 && (size_t)((T + 127) / 128) * (E / 32) >= 512) {
+        hipLaunchKernelGGL((k_route_logits<2, 8, 256, false>), dim3((T + 127) / 128, E / 32), dim3(256), 0, s, T, H, E, x,
+                           wr, bias, z);
+    } else if (E % 8 == 0 && (size_t)((T + 63) / 64) * (E / 8) >= 512) {
+        hipLaunchKernelGGL((k_route_logits<1, 2, 256, true>), dim3((T + 63) / 64, E / 8), dim3(256), 0, s, T, H, E, x,
+                           wr, bias, z);
     } else {
-        hipLaunchKernelGGL(k_route_logits<1>, dim3(tg, E / 4), dim3(256), 0, s, T, H, E, x, wr, bias, z);
+        hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4), dim3(256), 0, s, T, H, E, x,
+                           wr, bias, z);
     }
     hipLaunchKernelGGL(k_route_select, dim3(blocks_for(T, 4)), dim3(256), 0, s, T, E, k, z, ids, w);
     return hipGetLastError();
