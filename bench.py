@@ -207,7 +207,9 @@ def main():
         roof["traffic"] = measured_traffic(r["workload"])
         roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
         roof["algorithmic_bytes"] = r["weight_bytes"]
-        roof["kernel"] = "k_ffn_persistent (expert FFN: both grouped GEMMs, SwiGLU, requant, scatter)"
+        roof["kernel"] = ("k_ffn_persistent (expert FFN: both grouped GEMMs, SwiGLU, requant, scatter)"
+                          if r["T"] <= 1024 else
+                          "k_ffn<1,...> + k_ffn<2,...> (expert FFN: linear1+SwiGLU+requant, linear2+scatter)")
         roof["kernel_ms"] = r["ffn_ms"]
         return roof
 

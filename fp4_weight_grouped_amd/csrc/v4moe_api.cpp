@@ -41,7 +41,7 @@ DeviceInfo* device_info()
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
         di->ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         di->cus = prop.multiProcessorCount;
-        for (int mt : {1, 2, 4, 8})
+        for (int mt : {1, 2, 4})
             for (int cw : {2, 4}) di->persist_per_cu[cw == 4][mt] = persistent_blocks_per_cu(mt, cw);
     });
     return di->ok ? di : nullptr;
@@ -328,7 +328,11 @@ __attribute__((visibility("default"))) int moe_layer_forward(
                        reinterpret_cast<int32_t*>(ws + L.hist), s) != hipSuccess)
         return V4MOE_ELAUNCH;
     const FfnArgs a = ffn_args(d, L, ws, xq, xs, expert_offsets, sp, w, y);
-    int rc = run_ffn(d, L, a, ws, true, di, s);
+    // The wave-scheduled persistent kernel for weight-streaming batches (m-tiles
+    // of at most 64 rows); with 128-row m-tiles it measured 5-10% slower than
+    // the two launches on one GPU, where there is no transfer to hide.  Both
+    // run the same tiles: the results are identical.
+    int rc = run_ffn(d, L, a, ws, L.MT < 8, di, s);
     if (rc) return rc;
     if (launch_combine(d->T, d->H, d->topk, y, topk_w, out, s) != hipSuccess) return V4MOE_ELAUNCH;
     return V4MOE_OK;

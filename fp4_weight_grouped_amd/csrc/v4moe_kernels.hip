@@ -1162,14 +1162,15 @@ static int persistent_occupancy()
     return n < 1 ? 1 : n;
 }
 
+// The persistent kernel serves m-tiles of up to 64 rows (MT <= 4); 128-row
+// m-tiles run as the two launches.
 template <int CW>
 static int persistent_occupancy_cw(int MT)
 {
     switch (MT) {
     case 1: return persistent_occupancy<1, 1, CW>();
     case 2: return persistent_occupancy<2, 1, CW>();
-    case 4: return persistent_occupancy<4, 1, CW>();
-    default: return persistent_occupancy<8, 2, CW>();
+    default: return persistent_occupancy<4, 1, CW>();
     }
 }
 
@@ -1195,7 +1196,6 @@ static hipError_t launch_persistent_cw(int MT, const FfnArgs& a, int grid, hipSt
     case 1: return launch_persistent_t<1, 1, CW>(a, grid, s);
     case 2: return launch_persistent_t<2, 1, CW>(a, grid, s);
     case 4: return launch_persistent_t<4, 1, CW>(a, grid, s);
-    case 8: return launch_persistent_t<8, 2, CW>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -163,11 +163,14 @@ int moe_expert_ffn(const v4moe_dims* d, const uint8_t* xq, const float* xs,
 int moe_combine(const v4moe_dims* d, const uint16_t* y, const float* topk_w,
                 uint16_t* out, void* stream);
 
-/* The whole layer: route, dispatch, then one persistent kernel that runs the
- * experts in waves of 8 (P1 §1.2 and Fig. 5: the compute of wave w overlaps
- * the gather of wave w+1 and the scatter-back of finished experts), then the
- * combine.  Same arithmetic as the four calls above, so the output is
- * bit-identical to moe_route + moe_permute + moe_expert_ffn + moe_combine.
+/* The whole layer: route, dispatch, then the expert FFN, then the combine.
+ * When experts get at most 64 rows per m-tile (weight-streaming batches) the
+ * FFN is one persistent kernel that runs the experts in waves of 8 (P1 §1.2
+ * and Fig. 5: the compute of wave w overlaps the gather of wave w+1 and the
+ * scatter-back of finished experts); with 128-row m-tiles it is the two
+ * launches of moe_expert_ffn, which measured faster there.  Same tiles and
+ * arithmetic either way, so the output is bit-identical to moe_route +
+ * moe_permute + moe_expert_ffn + moe_combine.
  *   topk_ids, topk_w, expert_offsets: outputs exported for checking.
  *   out bf16 [T][H]. */
 int moe_layer_forward(const v4moe_dims* d, const uint16_t* x, const float* w_router,
