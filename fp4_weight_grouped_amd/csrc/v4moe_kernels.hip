@@ -1071,6 +1071,10 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
     } else if (E % 8 == 0 && (size_t)((T + 63) / 64) * (E / 8) >= 512) {
         hipLaunchKernelGGL((k_route_logits<1, 2, 256, true>), dim3((T + 63) / 64, E / 8), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
+    } else if (H % 512 == 0) {
+        // longer stages: the next slice's loads hide behind 512 dependent fmas
+        hipLaunchKernelGGL((k_route_logits<1, 1, 512, true>), dim3((T + 63) / 64, E / 4), dim3(256), 0, s, T, H, E, x,
+                           wr, bias, z);
     } else {
         hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
