@@ -48,32 +48,6 @@ __device__ __forceinline__ float silu_mul(float g, float u)
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in every lane
-// of the row: rotations by 1, 2, 4 and 8 within the row.
-__device__ __forceinline__ float row16_max(float v)
-{
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
-    return v;
-}
-
-// The value of lane l^1 (DPP quad_perm [1,0,3,2]).
-__device__ __forceinline__ float lane_pair_swap(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-}
-
-// Lanes l (even) and l+1 hold adjacent columns c, c+1 of two rows ra and rb
-// (values va, vb).  Returns the pair of row ra (even lane) or of row rb (odd
-// lane) in column order, so that each lane can write two adjacent elements.
-__device__ __forceinline__ float2 column_pair(float va, float vb, bool odd)
-{
-    const float recv = lane_pair_swap(odd ? va : vb);
-    return odd ? make_float2(recv, vb) : make_float2(va, recv);
-}
-
 // 16x16 output tile over one 128-wide K chunk on gfx950's block-scaled
 // matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4): A = E4M3 activations with
 // scale 1 (E8M0 127), B = E2M1 weight codes, each lane's 32 codes scaled by
@@ -95,6 +69,27 @@ __device__ __forceinline__ v4f mfma_e4m3_e2m1(v8i a, uint4 b, int sb)
     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bv, z, 0, 4, 0, 127, SEL, sb);
 }
+// The same instruction with the operands swapped: A = E2M1 weight codes (lane l:
+// weight row l%16, K 32(l/16)..+31, its E8M0 byte SEL of sw as scale), B = E4M3
+// activations (lane l: token l%16, the split K layout of A above).  Result:
+// lane l holds weight rows 4(l/16)+i, i = 0..3, for token l%16.
+template <int SEL>
+__device__ __forceinline__ v4f mfma_e2m1_e4m3(uint4 w, int sw, v8i x)
+{
+    const v8i wv = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, x, z, 4, 0, SEL, sw, 0, 127);
+}
+__device__ __forceinline__ v4f mfma_e2m1_e4m3_sel(int sel, uint4 w, int sw, v8i x)
+{
+    switch (sel & 3) {   // sel is a constant after unrolling: one instruction remains
+    case 0: return mfma_e2m1_e4m3<0>(w, sw, x);
+    case 1: return mfma_e2m1_e4m3<1>(w, sw, x);
+    case 2: return mfma_e2m1_e4m3<2>(w, sw, x);
+    default: return mfma_e2m1_e4m3<3>(w, sw, x);
+    }
+}
+
 __device__ __forceinline__ v4f mfma_e4m3_e2m1_sel(int sel, v8i a, uint4 b, int sb)
 {
     switch (sel & 3) {   // sel is a constant after unrolling: one instruction remains

@@ -719,9 +719,13 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
                   seg * 16;
     }
     const float* xbase = uniform(PHASE == 1 ? a.xs : a.hs);
+    // activation scales of the row group, stored token-major: position
+    // t*MTW + i holds row i*16 + t, so a lane reads the scales of its token in
+    // all MTW token tiles with one LDS read
     uint32_t xoff;
     {
-        const int r = min(rg * RG + lane, M - 1);
+        const int p = min(lane, RG - 1);
+        const int r = min(rg * RG + (p % MTW) * 16 + p / MTW, M - 1);
         xoff = 4u * (PHASE == 1 ? (uint32_t)rowinfo[r] * (uint32_t)(a.H / 128)
                                 : (uint32_t)(row0 + min(r, rows - 1)) * (uint32_t)a.hs_stride);
     }
@@ -765,9 +769,24 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
                            *reinterpret_cast<const int*>(st + TL::S_OFF + (cg * 2 + 1) * 256 + lane * 4)};
         const float sb0 = blk0[c];
         const float sb1 = blk1[c];
-        // Every m-tile of the row group is computed (rows past the end hold
+        // this lane's token in each token tile: one activation scale per tile
+        float xsv[MTW];
+        {
+            const float* xr = reinterpret_cast<const float*>(st + TL::X_OFF + rg * 256) + (lane & 15) * MTW;
+            if (MTW == 4) {
+                const float4 v = *reinterpret_cast<const float4*>(xr);
+                xsv[0] = v.x; xsv[1] = v.y; xsv[2 % MTW] = v.z; xsv[3 % MTW] = v.w;
+            } else if (MTW == 2) {
+                const float2 v = *reinterpret_cast<const float2*>(xr);
+                xsv[0] = v.x; xsv[1 % MTW] = v.y;
+            } else {
+#pragma unroll
+                for (int i = 0; i < MTW; i++) xsv[i] = xr[i];
+            }
+        }
+        // Every token tile of the row group is computed (rows past the end hold
         // finite filler and are never stored), so the eight independent MFMAs
-        // of an m-tile are all in flight before their results are promoted.
+        // of a token tile are all in flight before their results are promoted.
 #pragma unroll
         for (int i = 0; i < MTW; i++) {
             const int r = rg * RG + i * 16 + (lane & 15);
@@ -776,71 +795,62 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
             const uint8_t* arow = st + TL::A_OFF + r * 128;
             const uint4 a0 = *reinterpret_cast<const uint4*>(arow + ((g ^ sw) * 16));
             const uint4 a1 = *reinterpret_cast<const uint4*>(arow + (((g + 4) ^ sw) * 16));
-            v8i af;
-            af[0] = (int)a0.x; af[1] = (int)a0.y; af[2] = (int)a0.z; af[3] = (int)a0.w;
-            af[4] = (int)a1.x; af[5] = (int)a1.y; af[6] = (int)a1.z; af[7] = (int)a1.w;
+            const v8i xf = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
             v4f P[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) P[j] = mfma_e4m3_e2m1_sel(j & 3, af, bq[j], sc[j >> 2]);
-            const float4 x4 = *reinterpret_cast<const float4*>(st + TL::X_OFF + rg * 256 + (i * 16 + g * 4) * 4);
-            const float s0v[4] = {x4.x * sb0, x4.y * sb0, x4.z * sb0, x4.w * sb0};
-            const float s1v[4] = {x4.x * sb1, x4.y * sb1, x4.z * sb1, x4.w * sb1};
+            for (int j = 0; j < 8; j++) P[j] = mfma_e2m1_e4m3_sel(j & 3, bq[j], sc[j >> 2], xf);
+            const float s0 = xsv[i] * sb0;
+            const float s1 = xsv[i] * sb1;
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                const float* s = (PHASE == 1 && j >= 4) ? s1v : s0v;
+                const float s = (PHASE == 1 && j >= 4) ? s1 : s0;
 #pragma unroll
-                for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s[q], P[j][q], acc[i][j][q]);
+                for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, P[j][q], acc[i][j][q]);
             }
         }
     }
     __syncthreads();   // every wave is done with the ring: its first stages become staging space
 
     if (PHASE == 1) {
-        // h = SiLU(g) * u, then E4M3 per (row, 128 columns of h): the amax of a
-        // row is reduced over the 16 lanes of a row group of the MFMA result
-        // (one DPP row), then over the two waves that share the 128 columns.
+        // h = SiLU(g) * u, then E4M3 per (row, 128 columns of h).  Lane l holds,
+        // for the token l%16 of each token tile, h columns 64cg + 16j + 4(l/16)
+        // + q (j < 4, q < 4): the row amax is reduced over the lane's 16 values,
+        // the four lanes of the token (xor 16, 32), then over the two waves
+        // that share the 128 columns.
         uint8_t* stage = smem;                                      // [M][SP1]
         float* red = reinterpret_cast<float*>(smem + TL::STAGE);    // [NW][RG], ring stage 1
-        const bool odd = lane & 1;
+        const int g = lane >> 4;
         float hv[MTW][4][4];
 #pragma unroll
-        for (int i = 0; i < MTW; i++)
+        for (int i = 0; i < MTW; i++) {
+            float mx = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                float mx = 0.0f;
+            for (int j = 0; j < 4; j++)
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
+                for (int q = 0; q < 4; q++) {
                     const float h = silu_mul(acc[i][j][q], acc[i][4 + j][q]);
                     hv[i][j][q] = h;
                     mx = fmaxf(mx, fabsf(h));
                 }
-                mx = row16_max(mx);
-                if ((lane & 15) == 0) red[w * RG + i * 16 + (lane >> 4) * 4 + q] = mx;
-            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (g == 0) red[w * RG + i * 16 + (lane & 15)] = mx;
+        }
         __syncthreads();
         const int wp = rg * CW + (cg & ~1);
 #pragma unroll
         for (int i = 0; i < MTW; i++) {
-            float inv[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int rl = i * 16 + (lane >> 4) * 4 + q;
-                const float amax = fmaxf(red[wp * RG + rl], red[(wp + 1) * RG + rl]);
-                const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-                inv[q] = 1.0f / s;
-                if ((cg & 1) == 0 && (lane & 15) == 0 && rg * RG + rl < rows)
-                    store_coherent(a.hs + (size_t)(row0 + rg * RG + rl) * a.hs_stride + nb * (CW / 2) + (cg >> 1), s);
-            }
-            // two adjacent columns per lane: even lanes write rows 4g+2m, odd lanes 4g+2m+1
+            const int rl = i * 16 + (lane & 15);
+            const int r = rg * RG + rl;
+            const float amax = fmaxf(red[wp * RG + rl], red[(wp + 1) * RG + rl]);
+            const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            const float inv = 1.0f / s;
+            if ((cg & 1) == 0 && g == 0 && r < rows)
+                store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * (CW / 2) + (cg >> 1), s);
 #pragma unroll
             for (int j = 0; j < 4; j++)
-#pragma unroll
-                for (int m = 0; m < 2; m++) {
-                    const float2 pr = column_pair(hv[i][j][2 * m] * inv[2 * m], hv[i][j][2 * m + 1] * inv[2 * m + 1], odd);
-                    const int r = rg * RG + i * 16 + (lane >> 4) * 4 + 2 * m + (odd ? 1 : 0);
-                    *reinterpret_cast<uint16_t*>(stage + r * TL::SP1 + 64 * cg + 16 * j + (lane & 14)) =
-                        (uint16_t)e4m3x2(pr.x, pr.y);
-                }
+                *reinterpret_cast<uint32_t*>(stage + r * TL::SP1 + 64 * cg + 16 * j + 4 * g) =
+                    e4m3x2(hv[i][j][0] * inv, hv[i][j][1] * inv) | (e4m3x2(hv[i][j][2] * inv, hv[i][j][3] * inv) << 16);
         }
         __syncthreads();
         constexpr int SEGS = TL::HC / 16;
@@ -856,19 +866,14 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         // of every row group at a time.
         uint16_t* stage = reinterpret_cast<uint16_t*>(smem);        // [RW*16][SP2]
         constexpr int SEGS = TL::OC / 8;
-        const bool odd = lane & 1;
 #pragma unroll
         for (int i = 0; i < MTW; i++) {
             if (i * 16 < rows) {
 #pragma unroll
                 for (int j = 0; j < 8; j++)
-#pragma unroll
-                    for (int m = 0; m < 2; m++) {
-                        const float2 pr = column_pair(acc[i][j][2 * m], acc[i][j][2 * m + 1], odd);
-                        const int r = rg * 16 + (lane >> 4) * 4 + 2 * m + (odd ? 1 : 0);
-                        *reinterpret_cast<uint32_t*>(stage + r * TL::SP2 + 128 * cg + 16 * j + (lane & 14)) =
-                            bf16x2(pr.x, pr.y);
-                    }
+                    *reinterpret_cast<uint2*>(stage + (rg * 16 + (lane & 15)) * TL::SP2 + 128 * cg + 16 * j +
+                                              4 * (lane >> 4)) =
+                        make_uint2(bf16x2(acc[i][j][0], acc[i][j][1]), bf16x2(acc[i][j][2], acc[i][j][3]));
                 __syncthreads();
                 for (int s = tid; s < RW * 16 * SEGS; s += NT) {
                     const int rs = s / SEGS, sg = s % SEGS;
