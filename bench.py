@@ -13,8 +13,8 @@ that the library records around it on its own stream in every timed step:
   decode:  algorithmic bytes = active experts x (FP4 codes + E8M0 sub-block
            scales + fp32 block scales) = 13,375,488 B each, against 8 TB/s;
   prefill: algorithmic FLOP = 2*T*k*3*H*I against the dense FP8 peak 5.0 PFLOP/s.
-HBM traffic of that kernel (roofline.traffic) comes from the committed
-rocprofv3 TCC counter summary (FETCH_SIZE + WRITE_SIZE per launch, scaled by
+HBM traffic of the FFN (roofline.traffic) comes from the committed rocprofv3
+TCC counter summary (FETCH_SIZE + WRITE_SIZE per FFN, scaled by
 the same counters' reading for a plain copy kernel of known size); it is
 reported only while the kernel sources hash to the value recorded with it.
 The CPU baseline is the C oracle (test infrastructure) timed on the host cores.
@@ -63,7 +63,7 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch of the FFN kernel for `workload` from the committed
     counter summary, or None when absent or taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "k_ffn_persistent_hbm_traffic.txt")
+    path = os.path.join(ROOT, "profiles", "expert_ffn_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -205,7 +205,7 @@ def main():
             roof = dict(bound="mfma", achieved=r["ffn_tflops"], peak=FP8_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
                         frac=r["ffn_tflops"] / FP8_DENSE_PEAK_TFLOPS)
         roof["traffic"] = measured_traffic(r["workload"])
-        roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        roof["traffic_unit"] = "HBM bytes per FFN (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
         roof["algorithmic_bytes"] = r["weight_bytes"]
         roof["kernel"] = ("k_ffn_persistent (expert FFN: both grouped GEMMs, SwiGLU, requant, scatter)"
                           if r["T"] <= 1024 else
