@@ -179,6 +179,18 @@ def test_shapes_full_parity(T, H, I, E, k, mode, bias):
     full_check(custom(T, H, I, E, k, mode=mode, bias=bias), f"T{T}H{H}I{I}E{E}k{k}")
 
 
+def test_largest_hidden_and_intermediate():
+    """H = I = 16384, the largest supported K: 128 chunks per linear, the full
+    width of the per-tile block-scale staging; every token to both experts."""
+    full_check(custom(2, 16384, 16384, 2, 2, seed=11), "T2H16384I16384E2k2")
+
+
+def test_most_experts_and_topk():
+    """E = 1024 experts with top-16: the selector's widest case and the tile
+    builder's largest expert count (128 scheduling waves)."""
+    full_check(custom(64, 256, 128, 1024, 16, seed=12), "T64H256I128E1024k16")
+
+
 def test_single_token_calls():
     """32 calls with T = 1 (k = E): together within tolerance of the oracle, and
     each bit-identical to the same token inside the batched call."""
