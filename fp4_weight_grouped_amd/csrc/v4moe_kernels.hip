@@ -341,19 +341,17 @@ __global__ __launch_bounds__(256) void k_quant_x(int T, int H, const uint16_t* _
 // follow pair order exactly.  Pass <true> writes per-block counts; the scan
 // turns them into per-block bases; pass <false> writes the positions.
 // ---------------------------------------------------------------------------
+// One wave over one chunk of kPermChunk pairs starting at p0, in pair order.
+// cnt[E] (LDS) holds the chunk's running per-expert counts (zero on entry).
+// A pair's rank among the equal-expert pairs of its 64 is found by ballots
+// over the 11 bits of the expert id.  Count pass: cnt ends as the chunk's
+// histogram.  Position pass: pair p goes to row[e] + (earlier pairs of e in
+// the chunk), row[e] being the chunk's base for expert e.
 template <bool kCount>
-__global__ __launch_bounds__(64) void k_perm_pass(int P, int E, const int32_t* __restrict__ ids,
-                                                  int32_t* __restrict__ hist,
-                                                  int32_t* __restrict__ sorted_pair,
-                                                  int32_t* __restrict__ pair_pos)
+__device__ __forceinline__ void perm_chunk(int P, int p0, int lane, const int32_t* __restrict__ ids,
+                                           int32_t* cnt, const int32_t* row,
+                                           int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos)
 {
-    extern __shared__ int32_t cnt[];  // [E]
-    const int lane = threadIdx.x;
-    const int b = blockIdx.x;
-    int32_t* row = hist + (size_t)b * E;
-    for (int e = lane; e < E; e += 64) cnt[e] = 0;
-    __syncthreads();
-    const int p0 = b * kPermChunk;
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int it = 0; it < kPermChunk; it += 64) {
         const int p = p0 + it + lane;
@@ -379,6 +377,23 @@ __global__ __launch_bounds__(64) void k_perm_pass(int P, int E, const int32_t* _
         if (valid && rank == tot - 1) cnt[e] = base + tot;
         __builtin_amdgcn_wave_barrier();
     }
+}
+
+// Chunk b = blockIdx.x: histogram (kCount) or positions from the per-chunk
+// bases that k_perm_scan wrote over the histograms.
+template <bool kCount>
+__global__ __launch_bounds__(64) void k_perm_pass(int P, int E, const int32_t* __restrict__ ids,
+                                                  int32_t* __restrict__ hist,
+                                                  int32_t* __restrict__ sorted_pair,
+                                                  int32_t* __restrict__ pair_pos)
+{
+    extern __shared__ int32_t cnt[];  // [E]
+    const int lane = threadIdx.x;
+    const int b = blockIdx.x;
+    int32_t* row = hist + (size_t)b * E;
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+    __syncthreads();
+    perm_chunk<kCount>(P, b * kPermChunk, lane, ids, cnt, row, sorted_pair, pair_pos);
     if (kCount) {
         __syncthreads();
         for (int e = lane; e < E; e += 64) row[e] = cnt[e];
@@ -457,6 +472,43 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __
     }
 }
 
+// The whole permutation in one 1024-thread block when there are at most 16
+// chunks (wave w handles chunk w): histograms, offsets and per-chunk bases,
+// positions.  Same results as the three kernels above.  LDS: hist[nblk][E]
+// then cnt[nblk][E].
+__global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t* __restrict__ ids,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_pair,
+                                                     int32_t* __restrict__ pair_pos)
+{
+    extern __shared__ int32_t sh[];
+    __shared__ int total_s;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nblk = (P + kPermChunk - 1) / kPermChunk;
+    int32_t* hist = sh;
+    int32_t* cnt = sh + nblk * E;
+    for (int i = tid; i < 2 * nblk * E; i += 1024) sh[i] = 0;
+    __syncthreads();
+    if (w < nblk) perm_chunk<true>(P, w * kPermChunk, lane, ids, hist + w * E, nullptr, sorted_pair, pair_pos);
+    __syncthreads();
+    int tot = 0;
+    if (tid < E)
+        for (int b = 0; b < nblk; b++) tot += hist[b * E + tid];
+    const int off = block_exclusive_scan(tid < E ? tot : 0, &total_s);
+    if (tid < E) {
+        offsets[tid] = off;
+        int run = off;
+        for (int b = 0; b < nblk; b++) {
+            const int c = hist[b * E + tid];
+            hist[b * E + tid] = run;
+            run += c;
+        }
+    }
+    if (tid == 0) offsets[E] = total_s;
+    __syncthreads();
+    if (w < nblk) perm_chunk<false>(P, w * kPermChunk, lane, ids, cnt + w * E, hist + w * E, sorted_pair, pair_pos);
+}
+
 // ---------------------------------------------------------------------------
 // m-tile list and persistent work queue.
 // m-tile = up to M = 16*MT consecutive sorted rows of one expert.  The queue
@@ -476,7 +528,8 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
                                                       uint32_t* __restrict__ queue)
 {
     __shared__ int32_t base[1025];
-    __shared__ int32_t segpos[2 * 128];
+    __shared__ int32_t qstart[257];   // start of queue segment i (queue order), then the end
+    __shared__ int32_t qkey[256];     // 2*wave + phase of segment i
     __shared__ int total_s, qlen_s;
     const int tid = threadIdx.x;
     const int n = tid < E ? (offsets[tid + 1] - offsets[tid] + M - 1) / M : 0;
@@ -505,26 +558,31 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
         len = a * (ph ? NB2 : NB1);
     }
     const int start = block_exclusive_scan(len, &qlen_s);
-    if (build_queue && tid < 2 * W) segpos[2 * wv + ph] = start;
+    if (build_queue && tid < 2 * W) {
+        qstart[tid] = start;
+        qkey[tid] = 2 * wv + ph;
+    }
     if (tid == 0) {
+        qstart[2 * W] = total * (NB1 + NB2);
         ctrl[0] = total;
         ctrl[1] = 0;
         ctrl[2] = build_queue ? total * (NB1 + NB2) : 0;
     }
     if (!build_queue) return;
     __syncthreads();
-    for (int w = 0; w < W; w++) {
-        const int lo = base[w * kWaveExperts];
-        const int a = base[min(E, (w + 1) * kWaveExperts)] - lo;
-        for (int ph = 0; ph < 2; ph++) {
-            const int NB = ph ? NB2 : NB1;
-            const int pos = segpos[2 * w + ph];
-            for (int i = tid; i < a * NB; i += 1024) {
-                const int mt = lo + i / NB;
-                const int nb = i % NB;
-                queue[pos + i] = ((uint32_t)ph << 31) | ((uint32_t)mt << 8) | (uint32_t)nb;
-            }
+    // every entry on its own: its segment is the last one starting at or before
+    // it (empty segments share their start with the next one)
+    for (int q = tid; q < total * (NB1 + NB2); q += 1024) {
+        int lo = 0, hi = 2 * W - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (qstart[mid] <= q) lo = mid; else hi = mid - 1;
         }
+        const int swv = qkey[lo] >> 1, sph = qkey[lo] & 1;
+        const int NB = sph ? NB2 : NB1;
+        const int i = q - qstart[lo];
+        const int mt = base[swv * kWaveExperts] + i / NB;
+        queue[q] = ((uint32_t)sph << 31) | ((uint32_t)mt << 8) | (uint32_t)(i % NB);
     }
 }
 
@@ -1100,6 +1158,11 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offs
 {
     const int P = T * k;
     const int nblk = (P + kPermChunk - 1) / kPermChunk;
+    if (nblk <= 16 && nblk * E <= 4096) {   // dynamic LDS <= 32 KiB
+        hipLaunchKernelGGL(k_perm_small, dim3(1), dim3(1024), (size_t)2 * nblk * E * 4, s, P, E, ids, offsets,
+                           sorted_pair, pair_pos);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_perm_pass<true>, dim3(nblk), dim3(64), (size_t)E * 4, s, P, E, ids, hist,
                        sorted_pair, pair_pos);
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, E, nblk, hist, offsets);
