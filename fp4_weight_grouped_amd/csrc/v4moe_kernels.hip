@@ -5,21 +5,24 @@
 //   P2 = "DeepSeek V4架构学习笔记"
 //
 // Kernels, in the order a layer forward runs them:
-//   k_route_learned / k_route_hash   routing (P2, DeepSeekMoE notes)
+//   k_route_logits / k_route_logits_any + k_route_select, or k_route_hash
+//                                    routing (P2, DeepSeekMoE notes)
 //   k_quant_x                        FP8 dispatch payload (P1 §1.4)
-//   k_perm_pass<count> + k_perm_scan expert histogram, offsets, stable positions
+//   k_perm_small, or k_perm_pass<count> + k_perm_scan + k_perm_pass<positions>
+//                                    expert histogram, offsets, stable positions
 //   k_build_tiles                    m-tile list and the wave-ordered work queue
-//   k_ffn<1,MT>, k_ffn<2,MT>         linear1+SwiGLU+requant, linear2+scatter (unfused)
-//   k_ffn_persistent<MT>             the same tiles, wave-scheduled in one launch
+//   k_ffn<1,...>, k_ffn<2,...>       linear1+SwiGLU+requant, linear2+scatter
+//   k_ffn_persistent<...>            the same tiles, wave-scheduled in one launch
+//                                    (m-tiles of up to 64 rows)
 //   k_combine                        fixed-order weighted un-permute
 // plus the offline k_prepack and the test export k_dequant_export.
 //
 // Every tile of linear1/linear2 runs the same per-element arithmetic whatever
-// the tile height MT or the schedule: one 16x16x128 FP8 MFMA per 128-wide K
-// chunk, then acc = fma(xs*blk, P, acc) with chunks in increasing order.  A
-// row's result therefore does not depend on which rows share its tile (P1
-// §3.1, batch invariance; no split-K) and never on timing (P1 §3.2: no atomic
-// accumulation anywhere).
+// the tile shape or the schedule: one 16x16x128 block-scaled FP8 x FP4 MFMA
+// per 128-wide K chunk, then acc = fma(xs*blk, P, acc) with chunks in
+// increasing order.  A row's result therefore does not depend on which rows
+// share its tile (P1 §3.1, batch invariance; no split-K) and never on timing
+// (P1 §3.2: no atomic accumulation anywhere).
 #include "v4moe_device.h"
 #include "v4moe_internal.h"
 
@@ -607,12 +610,16 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
 //      sorted_pair in phase 1, contiguous hq rows in phase 2.  Lanes write LDS
 //      contiguously, so each row's 16-byte segments are stored XOR-swizzled by
 //      (row/2)%8, which puts the 16 rows of one operand read on distinct banks;
-//   X  the per-row activation scales of the chunk.
+//   X  the per-row activation scales of the chunk, token-major (a lane reads
+//      its token's scales for all its token tiles at once).
 // Stages are consumed in order: wait for the stage's loads (s_waitcnt vmcnt,
 // counted per wave), one barrier, issue the loads NS-1 chunks ahead into the
-// slot just freed, compute: per m-tile, eight block-scaled MFMAs (FP4 codes
-// and their E8M0 scales straight from LDS, no dequantisation pass), then
-// acc = fma(xs*blk, P, acc).  A row group with no valid row skips its MFMAs.
+// slot just freed, compute: per 16-token tile, eight block-scaled MFMAs with
+// the weights as the A operand (FP4 codes and their E8M0 scales straight from
+// LDS, no dequantisation pass) and the tokens as the B operand, so a lane gets
+// four consecutive output columns of one token; then acc = fma(xs*blk, P, acc)
+// with one activation scale per token tile.  A row group with no valid row
+// skips its MFMAs.
 // ---------------------------------------------------------------------------
 
 // Stores that another XCD may read within the same launch: agent-scope
