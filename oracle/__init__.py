@@ -76,6 +76,9 @@ def lib():
         L.orc_quant_rows.argtypes = [ci, ci, f32p, u8p, f32p]; L.orc_quant_rows.restype = None
         L.orc_quant_x.argtypes = [ci, ci, u16p, u8p, f32p]; L.orc_quant_x.restype = None
         L.orc_permute.argtypes = [ci, ci, ci, i32p, i32p, i32p, i32p]; L.orc_permute.restype = None
+        L.orc_e2m1_encode.argtypes = [ctypes.c_double]; L.orc_e2m1_encode.restype = ci
+        L.orc_quantize_weights.argtypes = [ci, ci, ci, f32p, u8p, u8p, f32p]
+        L.orc_quantize_weights.restype = ctypes.c_int64
         L.orc_layer_forward.argtypes = [ci, ci, ci, ci, ci, u16p, f32p, vp, ci, vp,
                                         ctypes.POINTER(OrcWeights), i32p, f32p, i32p, i32p, i32p,
                                         u8p, f32p, vp, vp, vp, vp, ci]
@@ -174,6 +177,21 @@ def quant_rows(v: np.ndarray):
     s = np.empty((R, C // 128), np.float32)
     lib().orc_quant_rows(R, C, np.ascontiguousarray(v, dtype=np.float32), q, s)
     return q, s
+
+
+def e2m1_encode(v: float) -> int:
+    return lib().orc_e2m1_encode(float(v))
+
+
+def quantize_weights(w: np.ndarray):
+    """FP32 master weights [E][N][K] -> (fp4 [E][N][K/2], e8m0 [E][N][K/32],
+    blk [E][N/128][K/128], clamped sub-block count), canonical layout."""
+    E, N, K = w.shape
+    fp4 = np.empty((E, N, K // 2), np.uint8)
+    e8 = np.empty((E, N, K // 32), np.uint8)
+    blk = np.empty((E, N // 128, K // 128), np.float32)
+    clamped = lib().orc_quantize_weights(E, N, K, np.ascontiguousarray(w, dtype=np.float32), fp4, e8, blk)
+    return fp4, e8, blk, int(clamped)
 
 
 def quant_x(x: np.ndarray):

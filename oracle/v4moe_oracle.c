@@ -310,6 +310,87 @@ EXPORT void orc_quant_x(int T, int H, const uint16_t* x, uint8_t* xq, float* xs)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Weight quantisation: FP32 master weights -> MXFP4 under 128x128 blocks      */
+/* (P1 §4, P4 §4: the QAT forward quantises the FP32 master weights to MXFP4;  */
+/* the pages cite the OCP MX paper for the format and give no formulas, so the */
+/* readings are stated here).                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest E2M1 code of x: ties go to the even code (mantissa bit 0),
+ * magnitudes at or beyond 6 saturate to 6, the sign of x is kept (also when
+ * the magnitude rounds to zero). */
+EXPORT int orc_e2m1_encode(double x)
+{
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    const int neg = signbit(x) ? 8 : 0;
+    const double m = fabs(x);
+    int best = 7;
+    for (int i = 0; i < 7; i++) {
+        const double mid = 0.5 * (grid[i] + grid[i + 1]);
+        if (m < mid) { best = i; break; }
+        if (m == mid) { best = (i % 2 == 0) ? i : i + 1; break; }
+    }
+    return neg | best;
+}
+
+/* w: fp32 [E][N][K] (N, K multiples of 128) -> canonical fp4 [E][N][K/2],
+ * e8m0 [E][N][K/32], blk [E][N/128][K/128].  Per 128x128 block:
+ *   s = amax / 384 in fp32 (s = 1 for an all-zero block): the block's largest
+ *       magnitude lands on 6 * 2^6, the largest value an FP4 element reaches
+ *       at the top of the lossless window b <= 6 (and 384 <= 448, E4M3's max);
+ *   per 1x32 sub-block of a row: v = w / s in fp32; b = floor(log2(max|v|))
+ *       - 2 (the OCP MX shared-exponent rule, E2M1's largest exponent being
+ *       2), raised to -8 when below the window (the sub-block is then counted
+ *       as clamped: its scale ratio to the block exceeds what E4M3 absorbs),
+ *       b = 0 for an all-zero sub-block; codes = orc_e2m1_encode(v * 2^-b).
+ * Returns the number of clamped sub-blocks. */
+EXPORT int64_t orc_quantize_weights(int E, int N, int K, const float* w, uint8_t* fp4, uint8_t* e8m0,
+                                    float* blk)
+{
+    const int NB = N / 128, KB = K / 128;
+    int64_t clamped = 0;
+#pragma omp parallel for schedule(dynamic) reduction(+ : clamped)
+    for (long id = 0; id < (long)E * NB * KB; id++) {
+        const int e = (int)(id / ((long)NB * KB)), nb = (int)((id / KB) % NB), kb = (int)(id % KB);
+        const float* src = w + ((size_t)e * N + (size_t)nb * 128) * K + (size_t)kb * 128;
+        float amax = 0.0f;
+        for (int r = 0; r < 128; r++)
+            for (int c = 0; c < 128; c++) {
+                const float a = fabsf(src[(size_t)r * K + c]);
+                if (a > amax) amax = a;
+            }
+        const float s = amax > 0.0f ? amax / 384.0f : 1.0f;
+        blk[((size_t)e * NB + nb) * KB + kb] = s;
+        for (int r = 0; r < 128; r++) {
+            const size_t n = (size_t)e * N + (size_t)nb * 128 + r;
+            for (int sb = 0; sb < 4; sb++) {
+                float v[32];
+                float am = 0.0f;
+                for (int j = 0; j < 32; j++) {
+                    v[j] = src[(size_t)r * K + sb * 32 + j] / s;
+                    if (fabsf(v[j]) > am) am = fabsf(v[j]);
+                }
+                int b = 0;
+                if (am > 0.0f) {
+                    int ex;
+                    frexp((double)am, &ex);   /* am = m * 2^ex, m in [0.5, 1) */
+                    b = (ex - 1) - 2;
+                    if (b < -8) { b = -8; clamped++; }
+                    if (b > 6) b = 6;
+                }
+                e8m0[n * (K / 32) + (size_t)kb * 4 + sb] = (uint8_t)(127 + b);
+                for (int j = 0; j < 32; j += 2) {
+                    const int lo = orc_e2m1_encode(ldexp((double)v[j], -b));
+                    const int hi = orc_e2m1_encode(ldexp((double)v[j + 1], -b));
+                    fp4[n * (K / 2) + ((size_t)kb * 128 + sb * 32 + j) / 2] = (uint8_t)(lo | (hi << 4));
+                }
+            }
+        }
+    }
+    return clamped;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dispatch as a local permutation (P1 §1.1-§1.2; token order, P1 §3.2)      */
 /* ------------------------------------------------------------------------ */
 
