@@ -18,6 +18,8 @@ TCC counter summary (FETCH_SIZE + WRITE_SIZE per FFN, scaled by
 the same counters' reading for a plain copy kernel of known size); it is
 reported only while the kernel sources hash to the value recorded with it.
 The CPU baseline is the C oracle (test infrastructure) timed on the host cores.
+The weight quantiser (FP32 master -> MXFP4, one layer's experts) is reported
+as a side record against the HBM peak.
 
 `--copy-bytes N` runs only a plain device copy of N bytes (the calibration
 kernel for those counters) and prints what it did.
@@ -150,6 +152,38 @@ def run_gpu(name, steps, warmup, layer_cache):
     return r, inp
 
 
+def run_quantizer(E, H, I, reps):
+    """FP32 master -> MXFP4 quantisation of every expert's gate, up and down
+    matrices of one layer (moe_quantize_weights, one launch per matrix).
+    Algorithmic bytes per weight: 4 read + 1/2 + 1/32 written (+ 4 per
+    128x128 block)."""
+    import torch
+    from fp4_weight_grouped_amd import v4moe
+
+    dev = "cuda:0"
+    shapes = [(E, I, H), (E, I, H), (E, H, I)]
+    ws = [torch.randn(sh, device=dev) * 0.02 for sh in shapes]
+    outs = [v4moe.quantize_weights(w) for w in ws]
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for w, o in zip(ws, outs):
+            v4moe.moe_quantize_weights(w, o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    n = sum(int(np.prod(sh)) for sh in shapes)
+    nbytes = n * 4 + n // 2 + n // 32 + (n // (128 * 128)) * 4
+    del ws, outs
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"[bench] weight quantiser: {ms:.3f} ms for {n / 1e9:.2f} G weights, {gbs:.0f} GB/s")
+    return dict(E=E, H=H, I=I, weights=n, ms=ms, algorithmic_bytes=nbytes, bound="hbm", achieved=gbs,
+                peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                kernel="k_quantize_weights (fp32 master -> fp4 e2m1 + e8m0 + fp32 block scale)")
+
+
 def cpu_baseline(inp, max_tokens=128, min_seconds=10.0, max_reps=8):
     """The oracle's layer forward on the same inputs, repeated until about
     min_seconds of CPU work have been timed."""
@@ -178,6 +212,7 @@ def main():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill side report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantizer", action="store_true", help="skip the weight-quantiser side report")
     ap.add_argument("--copy-bytes", type=int, default=0, help="only run the counter-calibration copy")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -196,6 +231,10 @@ def main():
     side = None
     if not args.no_prefill and args.workload != "prefill":
         side, _ = run_gpu("prefill", max(5, args.steps // 2), max(2, args.warmup // 2), cache)
+
+    quant = None
+    if not args.no_quantizer:
+        quant = run_quantizer(head["E"], head["H"], head["I"], max(3, args.steps // 4))
 
     def roofline(r):
         if r["T"] <= 1024:
@@ -242,6 +281,8 @@ def main():
     }
     if side is not None:
         rec["prefill"] = dict(side, roofline=roofline(side))
+    if quant is not None:
+        rec["weight_quantizer"] = quant
     print(json.dumps(rec), flush=True)
 
 

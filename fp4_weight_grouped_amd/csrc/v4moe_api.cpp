@@ -377,6 +377,22 @@ __attribute__((visibility("default"))) int moe_prepack_weights(const v4moe_dims*
     return flag ? V4MOE_ESCALE : V4MOE_OK;
 }
 
+__attribute__((visibility("default"))) int moe_quantize_weights(int32_t E, int32_t N, int32_t K,
+                                                                const float* w, const v4moe_mat* out,
+                                                                uint64_t* clamped, void* stream)
+{
+    if (!w || !out || !mat_ok(*out)) return V4MOE_ENULL;
+    if (E < 1 || N < 128 || N % 128 || K < 128 || K % 128) return V4MOE_EDIMS;
+    if (!aligned16(w) || !aligned16(out->fp4)) return V4MOE_EALIGN;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    if (launch_quantize_weights(E, N, K, w, static_cast<uint8_t*>(const_cast<void*>(out->fp4)),
+                                static_cast<uint8_t*>(const_cast<void*>(out->e8m0)), const_cast<float*>(out->blk),
+                                reinterpret_cast<unsigned long long*>(clamped), as_stream(stream)) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
 __attribute__((visibility("default"))) int moe_dequant_fp8(const v4moe_mat* m, int32_t N, int32_t K,
                                                            int32_t expert, uint8_t* out, void* stream)
 {

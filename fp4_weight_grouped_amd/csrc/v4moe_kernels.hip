@@ -1067,6 +1067,81 @@ __global__ __launch_bounds__(256) void k_prepack(int E, int N, int K, const uint
     if (s < 127 - 8 || s > 127 + 6) atomicOr(bad, 1);
 }
 
+// FP32 master weights -> MXFP4 under fp32 128x128 block scales (P1 §4 and
+// P4 §4: the QAT forward quantises the FP32 master weights to FP4; format per
+// the OCP MX paper the pages cite).  One block of 256 threads per 128x128
+// block; float4 f = i*256 + tid of the block is row f/32, columns 4*(f%32)..+3,
+// so a 1x32 sub-block is 8 consecutive lanes.
+//   s = amax / 384 (fp32; 1 for an all-zero block): the block's largest
+//       magnitude lands on 6 * 2^6, FP4's largest value at the top of the
+//       lossless window;
+//   v = w / s (fp32); sub-block exponent b = floor(log2(max|v|)) - 2 (OCP MX
+//       shared exponent, E2M1's largest exponent being 2), raised to -8 below
+//       the window (counted in *clamped), 0 for an all-zero sub-block;
+//   code = nearest E2M1 of v * 2^-b, ties to the even code, saturating at 6,
+//       sign kept.
+__global__ __launch_bounds__(256) void k_quantize_weights(int N, int K, const float* __restrict__ w,
+                                                          uint8_t* __restrict__ fp4, uint8_t* __restrict__ e8,
+                                                          float* __restrict__ blk,
+                                                          unsigned long long* __restrict__ clamped)
+{
+    __shared__ float red[4];
+    const int NB = N / 128, KB = K / 128;
+    const int kb = blockIdx.x % KB;
+    const int nb = (blockIdx.x / KB) % NB;
+    const size_t e = blockIdx.x / ((size_t)KB * NB);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c4 = tid & 31;                                 // float4 column in the block row
+    const size_t row0 = e * N + (size_t)nb * 128;
+    float4 v[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int r = i * 8 + (tid >> 5);
+        v[i] = *reinterpret_cast<const float4*>(w + (row0 + r) * K + (size_t)kb * 128 + 4 * c4);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (lane == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax > 0.0f ? amax / 384.0f : 1.0f;
+    if (tid == 0) blk[(e * NB + nb) * KB + kb] = s;
+    auto code = [](float x) -> uint32_t {
+        const float m = fabsf(x);
+        const uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) +
+                           (m > 5.0f);
+        return c | ((__float_as_uint(x) >> 28) & 8u);
+    };
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int r = i * 8 + (tid >> 5);
+        const float q[4] = {v[i].x / s, v[i].y / s, v[i].z / s, v[i].w / s};
+        float am = fmaxf(fmaxf(fabsf(q[0]), fabsf(q[1])), fmaxf(fabsf(q[2]), fabsf(q[3])));
+        am = fmaxf(am, __shfl_xor(am, 1));
+        am = fmaxf(am, __shfl_xor(am, 2));
+        am = fmaxf(am, __shfl_xor(am, 4));
+        int b = 0;
+        bool clip = false;
+        if (am > 0.0f) {
+            const int ex = (int)((__float_as_uint(am) >> 23) & 255u);   // 0: subnormal, far below the window
+            b = ex == 0 ? -1000 : ex - 127 - 2;
+            if (b < -8) { b = -8; clip = true; }
+            b = min(b, 6);
+        }
+        const float sc = __uint_as_float((uint32_t)(127 - b) << 23);   // 2^-b, exact
+        const uint32_t c0 = code(q[0] * sc), c1 = code(q[1] * sc), c2 = code(q[2] * sc), c3 = code(q[3] * sc);
+        const size_t n = row0 + r;
+        *reinterpret_cast<uint16_t*>(fp4 + n * (K / 2) + ((size_t)kb * 128 + 4 * c4) / 2) =
+            (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+        if ((c4 & 7) == 0) {
+            e8[n * (K / 32) + (size_t)kb * 4 + (c4 >> 3)] = (uint8_t)(127 + b);
+            if (clip && clamped) atomicAdd(clamped, 1ull);
+        }
+    }
+}
+
 // Test export of the weights exactly as the matrix kernels see them: one wave
 // per (n-tile, chunk) record of expert `expert` runs the same block-scaled
 // MFMA as the GEMM tiles against one-hot E4M3 rows (1.0 at K = 16r + row), so
@@ -1300,6 +1375,15 @@ hipError_t launch_prepack(int E, int N, int K, const uint8_t* fp4_in, const uint
     const size_t total = (size_t)E * (N / 16) * (K / 128) * 64;
     hipLaunchKernelGGL(k_prepack, dim3(blocks_for(total, 256)), dim3(256), 0, s, E, N, K, fp4_in, e8_in,
                        fp4_out, e8_out, bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_weights(int E, int N, int K, const float* w, uint8_t* fp4, uint8_t* e8, float* blk,
+                                  unsigned long long* clamped, hipStream_t s)
+{
+    const size_t blocks = (size_t)E * (N / 128) * (K / 128);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quantize_weights, dim3((unsigned)blocks), dim3(256), 0, s, N, K, w, fp4, e8, blk, clamped);
     return hipGetLastError();
 }
 

@@ -179,6 +179,27 @@ int moe_layer_forward(const v4moe_dims* d, const uint16_t* x, const float* w_rou
                       int32_t* expert_offsets, uint16_t* out,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/* FP32 master weights -> CANONICAL FP4 weights (P1 §4 and P4 §4: FP4
+ * quantisation-aware training quantises the FP32 master weights to FP4 in the
+ * forward pass; element format and shared-exponent rule per the OCP MX
+ * specification the pages cite).
+ *   w: device fp32 [E][N][K], row-major, finite values; N % 128 == 0,
+ *      K % 128 == 0; 16-byte aligned.
+ *   out: device CANONICAL matrix (fp4 [E][N][K/2], e8m0 [E][N][K/32],
+ *      blk [E][N/128][K/128]), written in full.
+ * Per 128x128 block, s = max|w| / 384 in fp32 (1 for an all-zero block), so
+ * the block's largest magnitude maps to 6 * 2^6, FP4's largest value at the
+ * top of the lossless window.  Per 1x32 sub-block of a row, v = w / s in fp32,
+ * b = floor(log2(max|v|)) - 2, raised to -8 when below the window (such a
+ * sub-block is "clamped": it keeps fewer significant codes), 0 for an
+ * all-zero sub-block; each element is the E2M1 code nearest to v * 2^-b,
+ * ties to the even code, saturating at 6, sign kept (-0.0 gives code 8).
+ * clamped: device uint64 to which the number of clamped sub-blocks is added
+ * (the caller clears it), or NULL.  Asynchronous on `stream`; allocates
+ * nothing.  The output passes moe_prepack_weights' window check. */
+int moe_quantize_weights(int32_t E, int32_t N, int32_t K, const float* w,
+                         const v4moe_mat* out, uint64_t* clamped, void* stream);
+
 /* Offline: canonical -> packed weight layout (both device buffers of equal
  * size; blk pointers of `packed` may alias those of `canonical`).  Checks that
  * every sub-block exponent b lies in the lossless window [-8, 6] (P1 §4: the
