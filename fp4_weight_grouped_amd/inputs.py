@@ -13,6 +13,9 @@ Workloads (all seed 0 unless stated):
 * ``zipf``     T=4096, same dims, per-expert router bias -1.2*ln(rank)
 * ``hash``     T=4096, same dims, hash routing, equal weights
 * ``ragged``   64 requests with lognormal(5, 1.2) lengths clipped to [1, 4096]
+* ``tiny_relu2``, ``decode_relu2``, ``prefill_relu2``: the gate-less expert
+  FFN with squared ReLU; the large ones at I=3072, the parameter count of the
+  SwiGLU experts at I=2048 (2*H*3072 = 3*H*2048); ``tiny_relu2`` at I=256.
 
 Distributions: x ~ N(0,1) rounded to bf16; router W_r ~ N(0, 0.02) fp32 [H][E];
 FP4 codes uniform over all 16 nibbles; the power-of-two sub-block exponent b is
@@ -45,6 +48,11 @@ _TAG = {
 ROUTE_LEARNED = 0
 ROUTE_HASH = 1
 
+# Expert activations: SwiGLU (gate, up, down) or a gate-less one (up, down).
+ACT_SWIGLU = 0
+ACT_RELU2 = 1
+ACT_RELU = 2
+
 
 @dataclasses.dataclass(frozen=True)
 class Dims:
@@ -53,6 +61,7 @@ class Dims:
     I: int
     E: int
     topk: int
+    act: int = ACT_SWIGLU
 
 
 @dataclasses.dataclass(frozen=True)
@@ -74,6 +83,9 @@ WORKLOADS = {
     "zipf": Workload("zipf", Dims(T=4096, **_BIG), zipf_bias=True),
     "hash": Workload("hash", Dims(T=4096, **_BIG), mode=ROUTE_HASH),
     "ragged": Workload("ragged", Dims(T=0, **_BIG), ragged_requests=64),
+    "tiny_relu2": Workload("tiny_relu2", Dims(T=64, H=256, I=256, E=8, topk=2, act=ACT_RELU2)),
+    "decode_relu2": Workload("decode_relu2", Dims(T=128, H=4096, I=3072, E=256, topk=8, act=ACT_RELU2)),
+    "prefill_relu2": Workload("prefill_relu2", Dims(T=8192, H=4096, I=3072, E=256, topk=8, act=ACT_RELU2)),
 }
 
 
@@ -102,7 +114,7 @@ class Matrix:
 
 @dataclasses.dataclass
 class Experts:
-    gate: Matrix   # N=I, K=H
+    gate: Optional[Matrix]   # N=I, K=H; None for the gate-less activations
     up: Matrix     # N=I, K=H
     down: Matrix   # N=H, K=I
 
@@ -130,9 +142,9 @@ def gen_matrix(seed: int, tag: str, E: int, N: int, K: int,
 
 
 @functools.lru_cache(maxsize=2)
-def gen_experts(seed: int, E: int, H: int, I: int, b_range=(-4, 0)) -> Experts:
+def gen_experts(seed: int, E: int, H: int, I: int, b_range=(-4, 0), gated: bool = True) -> Experts:
     return Experts(
-        gate=gen_matrix(seed, "gate", E, I, H, b_range),
+        gate=gen_matrix(seed, "gate", E, I, H, b_range) if gated else None,
         up=gen_matrix(seed, "up", E, I, H, b_range),
         down=gen_matrix(seed, "down", E, H, I, b_range),
     )
@@ -185,12 +197,12 @@ def make(name_or_wl, seed: int = 0, T: Optional[int] = None) -> Inputs:
         Tn = d.T
     if T is not None:
         Tn = T
-    dims = Dims(T=Tn, H=d.H, I=d.I, E=d.E, topk=d.topk)
+    dims = Dims(T=Tn, H=d.H, I=d.I, E=d.E, topk=d.topk, act=d.act)
     x = gen_x(seed, Tn, d.H)
     wr = gen_router(seed, d.H, d.E)
     bias = zipf_bias(seed, d.E) if wl.zipf_bias else None
     token_ids = np.arange(Tn, dtype=np.int64) if wl.mode == ROUTE_HASH else None
-    ex = gen_experts(seed, d.E, d.H, d.I, wl.b_range)
+    ex = gen_experts(seed, d.E, d.H, d.I, wl.b_range, d.act == ACT_SWIGLU)
     return Inputs(dims=dims, mode=wl.mode, x=x, w_router=wr, bias=bias,
                   token_ids=token_ids, experts=ex, lengths=lengths)
 

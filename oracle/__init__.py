@@ -44,6 +44,13 @@ vp = ctypes.c_void_p
 ci = ctypes.c_int
 
 
+# Activations (orc_layer_forward's act): SwiGLU, and the gate-less squared
+# ReLU and ReLU.
+ACT_SWIGLU = 0
+ACT_RELU2 = 1
+ACT_RELU = 2
+
+
 class OrcWeights(ctypes.Structure):
     _fields_ = [("fp4", vp * 3), ("e8m0", vp * 3), ("blk", vp * 3)]
 
@@ -79,7 +86,7 @@ def lib():
         L.orc_e2m1_encode.argtypes = [ctypes.c_double]; L.orc_e2m1_encode.restype = ci
         L.orc_quantize_weights.argtypes = [ci, ci, ci, f32p, u8p, u8p, f32p]
         L.orc_quantize_weights.restype = ctypes.c_int64
-        L.orc_layer_forward.argtypes = [ci, ci, ci, ci, ci, u16p, f32p, vp, ci, vp,
+        L.orc_layer_forward.argtypes = [ci, ci, ci, ci, ci, ci, u16p, f32p, vp, ci, vp,
                                         ctypes.POINTER(OrcWeights), i32p, f32p, i32p, i32p, i32p,
                                         u8p, f32p, vp, vp, vp, vp, ci]
         L.orc_layer_forward.restype = ci
@@ -231,6 +238,8 @@ def layer_forward(inp, subset=None, want_y=False, exact=False, k=None):
 
     Wt = OrcWeights()
     for i, m in enumerate((ex.gate, ex.up, ex.down)):
+        if m is None:            # gate-less activations: no gate matrix
+            continue
         Wt.fp4[i] = c(m.fp4)
         Wt.e8m0[i] = c(m.e8m0)
         Wt.blk[i] = c(m.blk)
@@ -246,7 +255,9 @@ def layer_forward(inp, subset=None, want_y=False, exact=False, k=None):
     sub = None if subset is None else np.ascontiguousarray(subset, dtype=np.int32)
     tid = None if inp.token_ids is None else np.ascontiguousarray(inp.token_ids, dtype=np.int64)
     bias = None if inp.bias is None else np.ascontiguousarray(inp.bias, dtype=np.float32)
-    lib().orc_layer_forward(T, H, I, E, k, np.ascontiguousarray(inp.x),
+    act = getattr(d, "act", ACT_SWIGLU)
+    assert act != ACT_SWIGLU or ex.gate is not None
+    lib().orc_layer_forward(T, H, I, E, k, act, np.ascontiguousarray(inp.x),
                             np.ascontiguousarray(inp.w_router), _ptr(bias), inp.mode, _ptr(tid),
                             ctypes.byref(Wt), res["ids"], res["w"], res["offsets"],
                             res["sorted_pair"], res["pair_pos"], res["xq"], res["xs"],

@@ -477,11 +477,33 @@ static void expert_linear(const int_matrix* m, const int32_t* xint, const float*
     }
 }
 
+/* The activation between the two expert matmuls.
+ *   ORC_ACT_SWIGLU: h = SiLU(G) * U, SiLU(g) = g / (1 + exp(-g)) (P1 §1.4);
+ *   ORC_ACT_RELU2, ORC_ACT_RELU: the gate-less FFN the pages propose as the
+ *   cheap alternative (P1, the hardware suggestions closing §1: an elementwise
+ *   activation needing neither exponential nor division, and no gate
+ *   projection so that the intermediate can be wider at the same parameter
+ *   count): h = max(U, 0)^2 or h = max(U, 0).  The pages name no function;
+ *   squared ReLU and ReLU are the two taken here. */
+#define ORC_ACT_SWIGLU 0
+#define ORC_ACT_RELU2  1
+#define ORC_ACT_RELU   2
+
+static float activation(int act, double G, double U)
+{
+    switch (act) {
+    case ORC_ACT_RELU2: { const double r = U > 0.0 ? U : 0.0; return (float)(r * r); }
+    case ORC_ACT_RELU: return (float)(U > 0.0 ? U : 0.0);
+    default: return (float)(G / (1.0 + exp(-G)) * U);
+    }
+}
+
 /* One (token, expert) pair: x row already quantised (xq, xs).
- * G, U rounded to fp32; h = fp32(SiLU(G) * U) with SiLU(g) = g/(1+exp(-g));
- * h quantised per 128 channels like x; Y = down(h) in fp64, then either
- * bf16(fp32(Y)) (normal mode) or kept in fp64 (exact mode, y_exact != NULL). */
-static void pair_ffn(int H, int I, const int_matrix* mg, const int_matrix* mu, const int_matrix* md,
+ * G, U rounded to fp32; h = fp32(activation(G, U)) (mg unused by the
+ * gate-less activations); h quantised per 128 channels like x; Y = down(h) in
+ * fp64, then either bf16(fp32(Y)) (normal mode) or kept in fp64 (exact mode,
+ * y_exact != NULL). */
+static void pair_ffn(int act, int H, int I, const int_matrix* mg, const int_matrix* mu, const int_matrix* md,
                      const uint8_t* xq, const float* xs, uint16_t* y_bf16, double* y_exact)
 {
     int32_t* xint = (int32_t*)malloc((size_t)H * sizeof(int32_t));
@@ -494,11 +516,11 @@ static void pair_ffn(int H, int I, const int_matrix* mg, const int_matrix* mu, c
     double* y = (double*)malloc((size_t)H * sizeof(double));
 
     for (int i = 0; i < H; i++) xint[i] = e4m3_int(xq[i]);
-    expert_linear(mg, xint, xs, g);
+    if (act == ORC_ACT_SWIGLU) expert_linear(mg, xint, xs, g);
     expert_linear(mu, xint, xs, u);
     for (int n = 0; n < I; n++) {
-        double G = (double)(float)g[n], U = (double)(float)u[n];
-        h[n] = (float)(G / (1.0 + exp(-G)) * U);
+        double G = act == ORC_ACT_SWIGLU ? (double)(float)g[n] : 0.0, U = (double)(float)u[n];
+        h[n] = activation(act, G, U);
     }
     orc_quant_rows(1, I, h, hq, hs);
     for (int n = 0; n < I; n++) hint[n] = e4m3_int(hq[n]);
@@ -525,9 +547,10 @@ static void pair_ffn(int H, int I, const int_matrix* mg, const int_matrix* mu, c
  *   y   [T*k][H] bf16 bits            expert outputs in pair order p = t*k+j
  *   out [T][H]   bf16 bits            out[t] = bf16(fp32(sum_j w_j * Y[t*k+j]))
  *   out_exact [T][H] fp64            exact mode: no rounding of Y or out
- * Rows of y/out/out_exact that belong to tokens outside the subset are left
- * untouched.  Returns 0. */
-EXPORT int orc_layer_forward(int T, int H, int I, int E, int k,
+ * act selects the activation (ORC_ACT_*); the gate-less ones never read the
+ * gate matrix.  Rows of y/out/out_exact that belong to tokens outside the
+ * subset are left untouched.  Returns 0. */
+EXPORT int orc_layer_forward(int T, int H, int I, int E, int k, int act,
                              const uint16_t* x, const float* wr, const float* bias,
                              int mode, const int64_t* token_ids, const orc_weights* W,
                              int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_pair,
@@ -553,10 +576,11 @@ EXPORT int orc_layer_forward(int T, int H, int I, int E, int k,
         int lo = offsets[e], hi = offsets[e + 1], need = 0;
         for (int r = lo; r < hi; r++) need |= want[sorted_pair[r] / k];
         if (!need) continue;
-        int_matrix mg, mu, md;
+        int_matrix mg = {0}, mu, md;
         size_t so = (size_t)e;
-        make_int_matrix(&mg, I, H, W->fp4[0] + so * I * (H / 2), W->e8m0[0] + so * I * (H / 32),
-                        W->blk[0] + so * (I / 128) * (H / 128));
+        if (act == ORC_ACT_SWIGLU)
+            make_int_matrix(&mg, I, H, W->fp4[0] + so * I * (H / 2), W->e8m0[0] + so * I * (H / 32),
+                            W->blk[0] + so * (I / 128) * (H / 128));
         make_int_matrix(&mu, I, H, W->fp4[1] + so * I * (H / 2), W->e8m0[1] + so * I * (H / 32),
                         W->blk[1] + so * (I / 128) * (H / 128));
         make_int_matrix(&md, H, I, W->fp4[2] + so * H * (I / 2), W->e8m0[2] + so * H * (I / 32),
@@ -565,7 +589,7 @@ EXPORT int orc_layer_forward(int T, int H, int I, int E, int k,
         for (int r = lo; r < hi; r++) {
             int p = sorted_pair[r], t = p / k;
             if (!want[t]) continue;
-            pair_ffn(H, I, &mg, &mu, &md, xq + (size_t)t * H, xs + (size_t)t * (H / 128),
+            pair_ffn(act, H, I, &mg, &mu, &md, xq + (size_t)t * H, xs + (size_t)t * (H / 128),
                      ybuf + (size_t)p * H, yex ? yex + (size_t)p * H : NULL);
         }
         free(mg.wint); free(mu.wint); free(md.wint);

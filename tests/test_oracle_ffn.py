@@ -155,3 +155,66 @@ def test_batch_invariance_oracle():
                             bias=None, token_ids=None, experts=inp.experts)
         alone = oracle.layer_forward(sub)
         assert np.array_equal(alone["out"], full["out"][lo:hi])
+
+
+# ---- the gate-less activations (the pages' cheap alternative to SwiGLU) ------------------
+ACTS = {oracle.ACT_RELU2: lambda u: np.maximum(u, 0.0) ** 2, oracle.ACT_RELU: lambda u: np.maximum(u, 0.0)}
+
+
+def make_gateless(T, H, I, E, k, act, up, down, x=None, mode=0, seed=7):
+    x = inputs.gen_x(seed, T, H) if x is None else x
+    return inputs.Inputs(dims=inputs.Dims(T, H, I, E, k, act), mode=mode, x=x,
+                         w_router=inputs.gen_router(seed, H, E), bias=None, token_ids=None,
+                         experts=inputs.Experts(gate=None, up=up, down=down))
+
+
+def test_closed_form_gateless():
+    """x = 1, every up weight +-1.0 * sg and every down weight 1.0 * sd:
+    U = +-H*sg, h = act(U), and with a constant h row the E4M3 round trip is
+    exact, so Y = I * sd * act(U).  Negative pre-activations give exactly 0."""
+    T, H, I, E = 8, 256, 256, 4
+    sg, sd = 2.0 ** -6, 0.0375
+    x = np.full((T, H), 0x3F80, np.uint16)
+    for act, f in ACTS.items():
+        for code, sign in ((0x2, 1.0), (0xA, -1.0)):
+            inp = make_gateless(T, H, I, E, 2, act, const_matrix(E, I, H, code, 0, sg),
+                                const_matrix(E, H, I, 0x2, 0, sd), x=x)
+            r = oracle.layer_forward(inp, want_y=True)
+            Y = I * sd * f(sign * H * sg)
+            if sign < 0:
+                assert np.all(r["y"] == 0) and np.all(r["out"] == 0)
+            else:
+                np.testing.assert_allclose(bf16_to_f64(r["y"]), Y, rtol=2 ** -8)
+                np.testing.assert_allclose(bf16_to_f64(r["out"]), Y, rtol=2 ** -8)
+
+
+def test_dense_equivalence_gateless():
+    """Every token routed to every expert: the exact-mode output equals the
+    dense per-expert computation act(x W_up^T) quantised, times W_down^T,
+    weighted by the routing weights."""
+    T, H, I, E = 24, 256, 256, 4
+    for act, f in ACTS.items():
+        ex = inputs.gen_experts(13, E, H, I, gated=False)
+        assert ex.gate is None
+        inp = make_gateless(T, H, I, E, E, act, ex.up, ex.down, seed=13)
+        r = oracle.layer_forward(inp, exact=True)
+        xr = quant_real(bf16_to_f64(inp.x).astype(np.float32))
+        ref = np.zeros((T, H))
+        for e in range(E):
+            we = (r["w"].astype(np.float64) * (r["ids"] == e)).sum(1)
+            U = (xr @ real_matrix(ex.up, e).T).astype(np.float32).astype(np.float64)
+            h = f(U).astype(np.float32)
+            ref += we[:, None] * (quant_real(h) @ real_matrix(ex.down, e).T)
+        err = np.abs(r["out_exact"] - ref).max() / np.abs(ref).max()
+        assert err < 1e-12, (act, err)
+        # about half the pre-activations are negative and contribute nothing
+        U0 = xr @ real_matrix(ex.up, 0).T
+        assert 0.3 < np.mean(U0 < 0) < 0.7
+
+
+def test_tiny_gateless_workload_runs():
+    """The tiny_relu2 workload runs end to end with no gate matrix."""
+    inp = inputs.make("tiny_relu2")
+    assert inp.experts.gate is None and inp.dims.act == oracle.ACT_RELU2
+    r = oracle.layer_forward(inp)
+    assert np.abs(bf16_to_f64(r["out"])).max() > 0
