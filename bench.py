@@ -42,14 +42,16 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix
 
 
-def weight_bytes_per_expert(H: int, I: int) -> int:
-    """FP4 codes + E8M0 sub-block scales + fp32 block scales of gate, up and down."""
-    return 3 * (H * I // 2) + 3 * (H * I // 32) + 3 * (H // 128) * (I // 128) * 4
+def weight_bytes_per_expert(H: int, I: int, mats: int = 3) -> int:
+    """FP4 codes + E8M0 sub-block scales + fp32 block scales of gate (SwiGLU
+    only), up and down."""
+    return mats * (H * I // 2 + H * I // 32 + (H // 128) * (I // 128) * 4)
 
 
-def ffn_flops(T: int, k: int, H: int, I: int) -> int:
-    """Two grouped GEMMs: gate and up (2*H*I each) plus down (2*H*I) per token-expert pair."""
-    return 2 * T * k * 3 * H * I
+def ffn_flops(T: int, k: int, H: int, I: int, mats: int = 3) -> int:
+    """Two grouped GEMMs: gate (SwiGLU only) and up (2*H*I each) plus down
+    (2*H*I) per token-expert pair."""
+    return 2 * T * k * mats * H * I
 
 
 def kernel_source_hash() -> str:
@@ -108,13 +110,15 @@ def run_gpu(name, steps, warmup, layer_cache):
     inp = inputs.make(name)
     d = inp.dims
     dev = "cuda:0"
-    key = (d.H, d.I, d.E, d.topk)
+    key = (d.H, d.I, d.E, d.topk, d.act)
     if key not in layer_cache:
+        layer_cache.clear()
+        torch.cuda.empty_cache()
         t0 = time.time()
-        dims = v4moe.dims(d.T, d.H, d.I, d.E, d.topk)
+        dims = v4moe.dims(d.T, d.H, d.I, d.E, d.topk, d.act)
         ex = v4moe.upload_experts(inp.experts, dims, dev)
         layer_cache[key] = v4moe.MoELayer(d.H, d.I, d.E, d.topk, ex,
-                                          torch.from_numpy(inp.w_router).to(dev), dev)
+                                          torch.from_numpy(inp.w_router).to(dev), dev, act=d.act)
         log(f"[bench] uploaded + prepacked weights in {time.time() - t0:.1f}s")
     layer = layer_cache[key]
     x = torch.from_numpy(inp.x.view(np.int16)).to(dev)
@@ -140,9 +144,11 @@ def run_gpu(name, steps, warmup, layer_cache):
     ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     counts = np.diff(off.cpu().numpy())
     n_active = int((counts > 0).sum())
-    wbytes = n_active * weight_bytes_per_expert(d.H, d.I)
-    flops = ffn_flops(d.T, d.topk, d.H, d.I)
-    r = dict(workload=name, T=d.T, H=d.H, I=d.I, E=d.E, topk=d.topk, ms_per_step=ms_step,
+    mats = 3 if d.act == inputs.ACT_SWIGLU else 2
+    wbytes = n_active * weight_bytes_per_expert(d.H, d.I, mats)
+    flops = ffn_flops(d.T, d.topk, d.H, d.I, mats)
+    act = {inputs.ACT_SWIGLU: "swiglu", inputs.ACT_RELU2: "relu2 (gate-less)", inputs.ACT_RELU: "relu (gate-less)"}
+    r = dict(workload=name, T=d.T, H=d.H, I=d.I, E=d.E, topk=d.topk, activation=act[d.act], ms_per_step=ms_step,
              tokens_per_s=d.T / (ms_step / 1e3), ffn_ms=ffn_ms, active_experts=n_active,
              load_max_over_mean=float(counts.max() / counts.mean()), idle_experts=int((counts == 0).sum()),
              weight_bytes=wbytes, ffn_hbm_gbs=wbytes / (ffn_ms / 1e3) / 1e9,
@@ -273,7 +279,8 @@ def main():
         "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": head["workload"], "T": head["T"], "H": head["H"], "I": head["I"],
-                   "E": head["E"], "topk": head["topk"], "weights": "fp4-e2m1/e8m0-32/fp32-128x128",
+                   "E": head["E"], "topk": head["topk"], "activation": head["activation"],
+                   "weights": "fp4-e2m1/e8m0-32/fp32-128x128",
                    "parallelism": "none (one GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -26,7 +26,7 @@ struct DeviceInfo {
     std::once_flag once;
     int ok = 0;          // 1: gfx950
     int cus = 0;
-    int persist_per_cu[2][9] = {};   // [CW == 4][MT]
+    int persist_per_cu[2][2][9] = {};   // [gated][CW == 4][MT]
 };
 DeviceInfo g_dev[kMaxDevices];
 
@@ -41,8 +41,9 @@ DeviceInfo* device_info()
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
         di->ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         di->cus = prop.multiProcessorCount;
-        for (int mt : {1, 2, 4})
-            for (int cw : {2, 4}) di->persist_per_cu[cw == 4][mt] = persistent_blocks_per_cu(mt, cw);
+        for (int g = 0; g < 2; g++)
+            for (int mt : {1, 2, 4})
+                for (int cw : {2, 4}) di->persist_per_cu[g][cw == 4][mt] = persistent_blocks_per_cu(mt, cw, g == 1);
     });
     return di->ok ? di : nullptr;
 }
@@ -62,6 +63,9 @@ bool dims_ok(const v4moe_dims* d)
     // the kernels address activations and intermediates with 32-bit offsets
     if ((int64_t)d->T * d->H >= (1ll << 31)) return false;
     if ((int64_t)d->T * d->topk * d->I >= (1ll << 31)) return false;
+    if (d->act != V4MOE_ACT_SWIGLU && d->act != V4MOE_ACT_RELU2 && d->act != V4MOE_ACT_RELU) return false;
+    // a gate-less linear1 tile spans at least 256 columns of h
+    if (d->act != V4MOE_ACT_SWIGLU && d->I % 256) return false;
     return true;
 }
 
@@ -76,16 +80,20 @@ struct Layout {
 // m-tiles never share a cache line.
 inline int hs_stride(int I) { return ((I / 128) + 31) / 32 * 32; }
 
+inline bool gated(const v4moe_dims* d) { return d->act == V4MOE_ACT_SWIGLU; }
+// linear1 tiles per m-tile: each spans 64*CW columns of h gated, 128*CW gate-less
+inline int nb1(const v4moe_dims* d, int CW) { return d->I / (64 * CW * (gated(d) ? 1 : 2)); }
+
 Layout layout(const v4moe_dims* d)
 {
     Layout L{};
     const size_t T = d->T, H = d->H, I = d->I, E = d->E, P = (size_t)d->T * d->topk;
     L.MT = choose_mt(d->T, d->topk, d->E);
-    L.CW = choose_cw(L.MT, d->H, d->I);
+    L.CW = choose_cw(L.MT, d->H, d->I, gated(d));
     const size_t M = 16 * (size_t)L.MT;
     L.n_mt_bound = (int)(P / M + (P < E ? P : E) + 1);
     L.nblk = (int)((P + kPermChunk - 1) / kPermChunk);
-    const size_t NB1 = I / (64 * L.CW), NB2 = H / (128 * L.CW);
+    const size_t NB1 = nb1(d, L.CW), NB2 = H / (128 * L.CW);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
     L.z = take(T * E * 4);
@@ -118,13 +126,14 @@ FfnArgs ffn_args(const v4moe_dims* d, const Layout& L, uint8_t* ws, const uint8_
                  uint16_t* y)
 {
     FfnArgs a{};
-    a.T = d->T; a.H = d->H; a.I = d->I; a.E = d->E; a.topk = d->topk;
+    a.T = d->T; a.H = d->H; a.I = d->I; a.E = d->E; a.topk = d->topk; a.act = d->act;
     a.n_mt_bound = L.n_mt_bound;
     a.xq = xq; a.xs = xs; a.offsets = offsets; a.sorted_pair = sorted_pair;
     auto mp = [](const v4moe_mat& m) {
         return MatPtr{static_cast<const uint8_t*>(m.fp4), static_cast<const uint8_t*>(m.e8m0), m.blk};
     };
-    a.gate = mp(w->gate); a.up = mp(w->up); a.down = mp(w->down);
+    a.gate = gated(d) ? mp(w->gate) : MatPtr{};
+    a.up = mp(w->up); a.down = mp(w->down);
     a.hq = ws + L.hq;
     a.hs = reinterpret_cast<float*>(ws + L.hs);
     a.hs_stride = hs_stride(d->I);
@@ -142,10 +151,10 @@ thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws, bool persistent,
             DeviceInfo* di, hipStream_t s)
 {
-    const int NB1 = d->I / (64 * L.CW), NB2 = d->H / (128 * L.CW);
+    const int NB1 = nb1(d, L.CW), NB2 = d->H / (128 * L.CW);
     hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
-    int per = di->persist_per_cu[L.CW == 4][L.MT];
+    int per = di->persist_per_cu[gated(d)][L.CW == 4][L.MT];
     int grid = di->cus * (per > 0 ? per : 1);
     // Scheduling lag in waves: enough linear1 tiles between a wave's linear1 and
     // linear2 entries to keep every running block busy meanwhile (estimate from
@@ -265,7 +274,7 @@ __attribute__((visibility("default"))) int moe_expert_ffn(const v4moe_dims* d, c
     if (!dims_ok(d)) return V4MOE_EDIMS;
     if (d->T == 0) return V4MOE_OK;
     if (!xq || !xs || !expert_offsets || !sorted_pair || !w || !y || !workspace) return V4MOE_ENULL;
-    if (!mat_ok(w->gate) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
+    if ((gated(d) && !mat_ok(w->gate)) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
     if (!aligned16(xq) || !aligned16(y) || !aligned16(workspace)) return V4MOE_EALIGN;
     const Layout L = layout(d);
     if (ws_bytes < L.total) return V4MOE_EWORKSPACE;
@@ -306,7 +315,7 @@ __attribute__((visibility("default"))) int moe_layer_forward(
     }
     if (!x || !w || !topk_ids || !topk_w || !out || !workspace) return V4MOE_ENULL;
     if (mode == V4MOE_ROUTE_LEARNED && !w_router) return V4MOE_ENULL;
-    if (!mat_ok(w->gate) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
+    if ((gated(d) && !mat_ok(w->gate)) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
     if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return V4MOE_EALIGN;
     if (mode == V4MOE_ROUTE_LEARNED && !aligned16(w_router)) return V4MOE_EALIGN;
     const Layout L = layout(d);
@@ -346,8 +355,8 @@ __attribute__((visibility("default"))) int moe_prepack_weights(const v4moe_dims*
 {
     if (!dims_ok(d)) return V4MOE_EDIMS;
     if (!canonical || !packed || !workspace) return V4MOE_ENULL;
-    if (!mat_ok(canonical->gate) || !mat_ok(canonical->up) || !mat_ok(canonical->down) ||
-        !mat_ok(packed->gate) || !mat_ok(packed->up) || !mat_ok(packed->down))
+    if ((gated(d) && (!mat_ok(canonical->gate) || !mat_ok(packed->gate))) || !mat_ok(canonical->up) ||
+        !mat_ok(canonical->down) || !mat_ok(packed->up) || !mat_ok(packed->down))
         return V4MOE_ENULL;
     if (!aligned16(workspace)) return V4MOE_EALIGN;
     if (ws_bytes < 256) return V4MOE_EWORKSPACE;
@@ -359,7 +368,7 @@ __attribute__((visibility("default"))) int moe_prepack_weights(const v4moe_dims*
     const v4moe_mat* in[3] = {&canonical->gate, &canonical->up, &canonical->down};
     const v4moe_mat* out[3] = {&packed->gate, &packed->up, &packed->down};
     const int N[3] = {d->I, d->I, d->H}, K[3] = {d->H, d->H, d->I};
-    for (int i = 0; i < 3; i++) {
+    for (int i = gated(d) ? 0 : 1; i < 3; i++) {
         if (launch_prepack(d->E, N[i], K[i], static_cast<const uint8_t*>(in[i]->fp4),
                            static_cast<const uint8_t*>(in[i]->e8m0),
                            static_cast<uint8_t*>(const_cast<void*>(out[i]->fp4)),

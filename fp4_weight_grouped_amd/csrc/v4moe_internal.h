@@ -22,6 +22,7 @@ struct MatPtr {
 // Everything an expert-FFN tile needs.
 struct FfnArgs {
     int T, H, I, E, topk;
+    int act;                   // 0: SwiGLU (gate, up); 1: squared ReLU, 2: ReLU (gate-less, up only)
     int n_mt_bound;            // capacity of the m-tile list
     const uint8_t* xq;         // [T][H]   E4M3
     const float* xs;           // [T][H/128]
@@ -52,7 +53,7 @@ hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue, 
 // two wave rows.
 hipError_t launch_ffn(int phase, int MT, int CW, const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_persistent(int MT, int CW, const FfnArgs& a, int grid, hipStream_t s);
-int persistent_blocks_per_cu(int MT, int CW);
+int persistent_blocks_per_cu(int MT, int CW, bool gated);
 hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* w, uint16_t* out,
                           hipStream_t s);
 hipError_t launch_prepack(int E, int N, int K, const uint8_t* fp4_in, const uint8_t* e8_in,
@@ -66,8 +67,8 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 
 // Rows per m-tile (16 * MT) used for given dimensions.
 int choose_mt(int T, int k, int E);
-// Wave columns per tile: a tile covers 64*CW columns of h in linear1 and
-// 128*CW output columns in linear2.
-int choose_cw(int MT, int H, int I);
+// Wave columns per tile: a tile covers 64*CW columns of h in linear1 (128*CW
+// gate-less) and 128*CW output columns in linear2.
+int choose_cw(int MT, int H, int I, bool gated);
 
 }  // namespace v4moe

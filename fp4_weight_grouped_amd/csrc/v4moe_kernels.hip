@@ -711,11 +711,26 @@ struct TileLayout {
 // SiLU(g) * u in fp32 (the same code in every tile variant).
 __device__ __forceinline__ float swiglu(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
-template <int PHASE, int MT, int RW, int CW>
+// Gate-less activations (the cheap alternative to SwiGLU): squared ReLU, or
+// ReLU; both need neither an exponential nor a division.
+__device__ __forceinline__ float gateless_act(int act, float u)
+{
+    const float r = u > 0.0f ? u : 0.0f;
+    return act == 1 ? r * r : r;
+}
+
+// G: the expert FFN is SwiGLU (gate and up projections); otherwise gate-less
+// (a.act selects the activation).  Phase 2 does not depend on G.
+template <int PHASE, int MT, int RW, int CW, bool G>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8_t* smem)
 {
     using TL = TileLayout<MT, RW, CW>;
     constexpr int M = TL::M, NS = TL::NS, NT = TL::NT, NW = TL::NW, MTW = TL::MTW, RG = TL::RG;
+    // columns of h per linear1 tile: gated, each wave's eight n-tiles pair 64
+    // gate with 64 up columns; gate-less, they are 128 columns of h
+    constexpr int HC1 = G ? TL::HC : 2 * TL::HC;
+    constexpr int SP1 = HC1 + 16;                            // phase-1 staging pitch (bytes)
+    static_assert(M * SP1 <= TL::RING, "phase-1 staging fits the ring");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -739,13 +754,14 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     }
     // The tile's 128x128 block scales for every chunk, staged in LDS (per-chunk
     // global reads would be vector loads whose waits drain the load ring).
-    // Phase 1: [2*hb] gate, [2*hb+1] up of h block hb of the tile; phase 2:
-    // output block cg of the tile.
+    // Phase 1 gated: [2*hb] gate, [2*hb+1] up of h block hb of the tile;
+    // otherwise: output block cg of the tile (linear1 gate-less, linear2).
     float* blkv = reinterpret_cast<float*>(smem + TL::BLK_OFF);
     for (int i = tid; i < CW * C; i += NT) {
         const int h = i / C, c = i % C;
         const float* src = PHASE == 1
-            ? ((h & 1) ? a.up.blk : a.gate.blk) + ((size_t)e * (a.I / 128) + nb * (CW / 2) + (h >> 1)) * C
+            ? (G ? ((h & 1) ? a.up.blk : a.gate.blk) + ((size_t)e * (a.I / 128) + nb * (CW / 2) + (h >> 1)) * C
+                 : a.up.blk + ((size_t)e * (a.I / 128) + nb * CW + h) * C)
             : a.down.blk + ((size_t)e * (a.H / 128) + nb * CW + h) * C;
         blkv[h * 128 + c] = src[c];
     }
@@ -757,20 +773,20 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
 #pragma unroll
     for (int r = 0; r < TL::NBR; r++) {
         const int rr = w * TL::NBR + r;                      // record of the tile, 0 .. 8*CW-1
-        const MatPtr& m = PHASE == 1 ? ((rr & 7) < 4 ? a.gate : a.up) : a.down;
-        const int tile = PHASE == 1 ? nb * 4 * CW + 4 * (rr >> 3) + (rr & 3) : nb * 8 * CW + rr;
+        const MatPtr& m = PHASE == 1 ? (G && (rr & 7) < 4 ? a.gate : a.up) : a.down;
+        const int tile = PHASE == 1 && G ? nb * 4 * CW + 4 * (rr >> 3) + (rr & 3) : nb * 8 * CW + rr;
         bbase[r] = uniform(m.fp4 + ((size_t)e * (N / 16) + tile) * C * 1024);
     }
     const uint8_t* sbase[TL::NSR];
 #pragma unroll
     for (int r = 0; r < TL::NSR; r++) {
         const int ss = w * TL::NSR + r;                      // scale record, 0 .. 2*CW-1
-        const MatPtr& m = PHASE == 1 ? ((ss & 1) ? a.up : a.gate) : a.down;
-        const int quad = PHASE == 1 ? nb * CW + (ss >> 1) : nb * 2 * CW + ss;
+        const MatPtr& m = PHASE == 1 ? (G && (ss & 1) == 0 ? a.gate : a.up) : a.down;
+        const int quad = PHASE == 1 && G ? nb * CW + (ss >> 1) : nb * 2 * CW + ss;
         sbase[r] = uniform(m.e8m0 + ((size_t)e * (N / 64) + quad) * C * 256);
     }
-    const float* blk0 = blkv + (PHASE == 1 ? 2 * (cg >> 1) : cg) * 128;
-    const float* blk1 = blkv + (PHASE == 1 ? 2 * (cg >> 1) + 1 : cg) * 128;
+    const float* blk0 = blkv + (PHASE == 1 && G ? 2 * (cg >> 1) : cg) * 128;
+    const float* blk1 = blkv + (PHASE == 1 && G ? 2 * (cg >> 1) + 1 : cg) * 128;
     const uint8_t* abase = uniform(PHASE == 1 ? a.xq : a.hq);
     uint32_t aoff[TL::AI];
 #pragma unroll
@@ -868,7 +884,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
             const float s1 = xsv[i] * sb1;
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                const float s = (PHASE == 1 && j >= 4) ? s1 : s0;
+                const float s = (PHASE == 1 && G && j >= 4) ? s1 : s0;
 #pragma unroll
                 for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, P[j][q], acc[i][j][q]);
             }
@@ -876,7 +892,48 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     }
     __syncthreads();   // every wave is done with the ring: its first stages become staging space
 
-    if (PHASE == 1) {
+    if (PHASE == 1 && !G) {
+        // h = act(u), then E4M3 per (row, 128 columns of h).  Lane l holds, for
+        // the token l%16 of each token tile, h columns 128cg + 16j + 4(l/16) + q
+        // (j < 8, q < 4): one wave owns a whole 128-column group, so the row
+        // amax is reduced over the lane's 32 values and the four lanes of the
+        // token (xor 16, 32).
+        uint8_t* stage = smem;                                      // [M][SP1]
+        const int g = lane >> 4;
+        const int act = a.act;
+#pragma unroll
+        for (int i = 0; i < MTW; i++) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    acc[i][j][q] = gateless_act(act, acc[i][j][q]);
+                    mx = fmaxf(mx, acc[i][j][q]);                   // h >= 0
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const int r = rg * RG + i * 16 + (lane & 15);
+            const float s = mx > 0.0f ? mx / 448.0f : 1.0f;
+            const float inv = 1.0f / s;
+            if (g == 0 && r < rows)
+                store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * CW + cg, s);
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                *reinterpret_cast<uint32_t*>(stage + r * SP1 + 128 * cg + 16 * j + 4 * g) =
+                    e4m3x2(acc[i][j][0] * inv, acc[i][j][1] * inv) |
+                    (e4m3x2(acc[i][j][2] * inv, acc[i][j][3] * inv) << 16);
+        }
+        __syncthreads();
+        constexpr int SEGS = HC1 / 16;
+        for (int s = tid; s < M * SEGS; s += NT) {
+            const int r = s / SEGS, sg = s % SEGS;
+            if (r < rows)
+                store_coherent(a.hq + (size_t)(row0 + r) * a.I + nb * HC1 + sg * 16,
+                               *reinterpret_cast<const uint4*>(stage + r * SP1 + sg * 16));
+        }
+        __syncthreads();
+    } else if (PHASE == 1) {
         // h = SiLU(g) * u, then E4M3 per (row, 128 columns of h).  Lane l holds,
         // for the token l%16 of each token tile, h columns 64cg + 16j + 4(l/16)
         // + q (j < 4, q < 4): the row amax is reduced over the lane's 16 values,
@@ -914,16 +971,16 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
                 store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * (CW / 2) + (cg >> 1), s);
 #pragma unroll
             for (int j = 0; j < 4; j++)
-                *reinterpret_cast<uint32_t*>(stage + r * TL::SP1 + 64 * cg + 16 * j + 4 * g) =
+                *reinterpret_cast<uint32_t*>(stage + r * SP1 + 64 * cg + 16 * j + 4 * g) =
                     e4m3x2(hv[i][j][0] * inv, hv[i][j][1] * inv) | (e4m3x2(hv[i][j][2] * inv, hv[i][j][3] * inv) << 16);
         }
         __syncthreads();
-        constexpr int SEGS = TL::HC / 16;
+        constexpr int SEGS = HC1 / 16;
         for (int s = tid; s < M * SEGS; s += NT) {
             const int r = s / SEGS, sg = s % SEGS;
             if (r < rows)
-                store_coherent(a.hq + (size_t)(row0 + r) * a.I + nb * TL::HC + sg * 16,
-                               *reinterpret_cast<const uint4*>(stage + r * TL::SP1 + sg * 16));
+                store_coherent(a.hq + (size_t)(row0 + r) * a.I + nb * HC1 + sg * 16,
+                               *reinterpret_cast<const uint4*>(stage + r * SP1 + sg * 16));
         }
         __syncthreads();
     } else {
@@ -955,14 +1012,14 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     }
 }
 
-template <int PHASE, int MT, int RW, int CW>
+template <int PHASE, int MT, int RW, int CW, bool G>
 __global__ __launch_bounds__(64 * RW * CW) void k_ffn(FfnArgs a, int NB)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int mt = blockIdx.x / NB;
     const int nb = blockIdx.x % NB;
     if (mt >= a.ctrl[0]) return;
-    ffn_tile<PHASE, MT, RW, CW>(a, mt, nb, smem);
+    ffn_tile<PHASE, MT, RW, CW, G>(a, mt, nb, smem);
 }
 
 // Persistent, wave-scheduled: blocks take queue entries in order.  A linear2
@@ -970,12 +1027,12 @@ __global__ __launch_bounds__(64 * RW * CW) void k_ffn(FfnArgs a, int NB)
 // earlier in the queue, were taken by running blocks and never wait, so every
 // wait ends.  Counters only signal readiness; no data is accumulated through
 // them, so the numerics are those of the unfused kernels.
-template <int MT, int RW, int CW>
+template <int MT, int RW, int CW, bool G>
 __global__ __launch_bounds__(64 * RW * CW) void k_ffn_persistent(FfnArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ uint32_t item;
-    const int NB1 = a.I / TileLayout<MT, RW, CW>::HC;
+    const int NB1 = a.I / (TileLayout<MT, RW, CW>::HC * (G ? 1 : 2));
     const int total = a.ctrl[2];
     for (;;) {
         __syncthreads();
@@ -992,7 +1049,7 @@ __global__ __launch_bounds__(64 * RW * CW) void k_ffn_persistent(FfnArgs a)
             // h and its scales were written with agent-coherent stores (through
             // this XCD's L2); once every wave has them acknowledged, one counter
             // increment publishes the tile.  No L2 write-back is needed.
-            ffn_tile<1, MT, RW, CW>(a, mt, nb, smem);
+            ffn_tile<1, MT, RW, CW, G>(a, mt, nb, smem);
             wait_vm<0>();
             __syncthreads();
             if (threadIdx.x == 0)
@@ -1004,7 +1061,7 @@ __global__ __launch_bounds__(64 * RW * CW) void k_ffn_persistent(FfnArgs a)
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // drop any stale cached lines
             }
             __syncthreads();
-            ffn_tile<2, MT, RW, CW>(a, mt, nb, smem);
+            ffn_tile<2, MT, RW, CW, G>(a, mt, nb, smem);
         }
     }
 }
@@ -1272,45 +1329,52 @@ static hipError_t allow_lds(F* kernel, size_t bytes, bool& done)
     return r;
 }
 
-template <int PHASE, int MT, int RW, int CW>
+template <int PHASE, int MT, int RW, int CW, bool G>
 static hipError_t launch_ffn_t(const FfnArgs& a, hipStream_t s)
 {
     using TL = TileLayout<MT, RW, CW>;
     static bool lds_ok = false;
-    const int NB = PHASE == 1 ? a.I / TL::HC : a.H / TL::OC;
+    const int NB = PHASE == 1 ? a.I / (TL::HC * (G ? 1 : 2)) : a.H / TL::OC;
     const size_t lds = TL::BYTES;
-    if (allow_lds(k_ffn<PHASE, MT, RW, CW>, lds, lds_ok) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_ffn<PHASE, MT, RW, CW>), dim3((unsigned)a.n_mt_bound * NB), dim3(TL::NT), lds, s, a, NB);
+    if (allow_lds(k_ffn<PHASE, MT, RW, CW, G>, lds, lds_ok) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_ffn<PHASE, MT, RW, CW, G>), dim3((unsigned)a.n_mt_bound * NB), dim3(TL::NT), lds, s, a,
+                       NB);
     return hipGetLastError();
 }
 
-template <int PHASE, int CW>
+template <int PHASE, int CW, bool G>
 static hipError_t launch_ffn_cw(int MT, const FfnArgs& a, hipStream_t s)
 {
     switch (MT) {
-    case 1: return launch_ffn_t<PHASE, 1, 1, CW>(a, s);
-    case 2: return launch_ffn_t<PHASE, 2, 1, CW>(a, s);
-    case 4: return launch_ffn_t<PHASE, 4, 1, CW>(a, s);
-    case 8: return launch_ffn_t<PHASE, 8, 2, CW>(a, s);
+    case 1: return launch_ffn_t<PHASE, 1, 1, CW, G>(a, s);
+    case 2: return launch_ffn_t<PHASE, 2, 1, CW, G>(a, s);
+    case 4: return launch_ffn_t<PHASE, 4, 1, CW, G>(a, s);
+    case 8: return launch_ffn_t<PHASE, 8, 2, CW, G>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
+// Linear2 tiles do not depend on the activation: one instantiation serves both.
 hipError_t launch_ffn(int phase, int MT, int CW, const FfnArgs& a, hipStream_t s)
 {
-    if (CW == 2) return phase == 1 ? launch_ffn_cw<1, 2>(MT, a, s) : launch_ffn_cw<2, 2>(MT, a, s);
-    if (CW == 4) return phase == 1 ? launch_ffn_cw<1, 4>(MT, a, s) : launch_ffn_cw<2, 4>(MT, a, s);
+    const bool g = a.act == 0;
+    if (CW == 2)
+        return phase == 2 ? launch_ffn_cw<2, 2, true>(MT, a, s)
+                          : (g ? launch_ffn_cw<1, 2, true>(MT, a, s) : launch_ffn_cw<1, 2, false>(MT, a, s));
+    if (CW == 4)
+        return phase == 2 ? launch_ffn_cw<2, 4, true>(MT, a, s)
+                          : (g ? launch_ffn_cw<1, 4, true>(MT, a, s) : launch_ffn_cw<1, 4, false>(MT, a, s));
     return hipErrorInvalidValue;
 }
 
-template <int MT, int RW, int CW>
+template <int MT, int RW, int CW, bool G>
 static int persistent_occupancy()
 {
     using TL = TileLayout<MT, RW, CW>;
     static bool lds_ok = false;
-    if (allow_lds(k_ffn_persistent<MT, RW, CW>, TL::BYTES, lds_ok) != hipSuccess) return 1;
+    if (allow_lds(k_ffn_persistent<MT, RW, CW, G>, TL::BYTES, lds_ok) != hipSuccess) return 1;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_ffn_persistent<MT, RW, CW>, TL::NT, TL::BYTES) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_ffn_persistent<MT, RW, CW, G>, TL::NT, TL::BYTES) !=
         hipSuccess)
         n = 1;
     return n < 1 ? 1 : n;
@@ -1318,46 +1382,48 @@ static int persistent_occupancy()
 
 // The persistent kernel serves m-tiles of up to 64 rows (MT <= 4); 128-row
 // m-tiles run as the two launches.
-template <int CW>
+template <int CW, bool G>
 static int persistent_occupancy_cw(int MT)
 {
     switch (MT) {
-    case 1: return persistent_occupancy<1, 1, CW>();
-    case 2: return persistent_occupancy<2, 1, CW>();
-    default: return persistent_occupancy<4, 1, CW>();
+    case 1: return persistent_occupancy<1, 1, CW, G>();
+    case 2: return persistent_occupancy<2, 1, CW, G>();
+    default: return persistent_occupancy<4, 1, CW, G>();
     }
 }
 
-int persistent_blocks_per_cu(int MT, int CW)
+int persistent_blocks_per_cu(int MT, int CW, bool gated)
 {
-    return CW == 4 ? persistent_occupancy_cw<4>(MT) : persistent_occupancy_cw<2>(MT);
+    if (gated) return CW == 4 ? persistent_occupancy_cw<4, true>(MT) : persistent_occupancy_cw<2, true>(MT);
+    return CW == 4 ? persistent_occupancy_cw<4, false>(MT) : persistent_occupancy_cw<2, false>(MT);
 }
 
-template <int MT, int RW, int CW>
+template <int MT, int RW, int CW, bool G>
 static hipError_t launch_persistent_t(const FfnArgs& a, int grid, hipStream_t s)
 {
     using TL = TileLayout<MT, RW, CW>;
     static bool lds_ok = false;
-    if (allow_lds(k_ffn_persistent<MT, RW, CW>, TL::BYTES, lds_ok) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_ffn_persistent<MT, RW, CW>), dim3(grid), dim3(TL::NT), TL::BYTES, s, a);
+    if (allow_lds(k_ffn_persistent<MT, RW, CW, G>, TL::BYTES, lds_ok) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_ffn_persistent<MT, RW, CW, G>), dim3(grid), dim3(TL::NT), TL::BYTES, s, a);
     return hipGetLastError();
 }
 
-template <int CW>
+template <int CW, bool G>
 static hipError_t launch_persistent_cw(int MT, const FfnArgs& a, int grid, hipStream_t s)
 {
     switch (MT) {
-    case 1: return launch_persistent_t<1, 1, CW>(a, grid, s);
-    case 2: return launch_persistent_t<2, 1, CW>(a, grid, s);
-    case 4: return launch_persistent_t<4, 1, CW>(a, grid, s);
+    case 1: return launch_persistent_t<1, 1, CW, G>(a, grid, s);
+    case 2: return launch_persistent_t<2, 1, CW, G>(a, grid, s);
+    case 4: return launch_persistent_t<4, 1, CW, G>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_ffn_persistent(int MT, int CW, const FfnArgs& a, int grid, hipStream_t s)
 {
-    if (CW == 2) return launch_persistent_cw<2>(MT, a, grid, s);
-    if (CW == 4) return launch_persistent_cw<4>(MT, a, grid, s);
+    const bool g = a.act == 0;
+    if (CW == 2) return g ? launch_persistent_cw<2, true>(MT, a, grid, s) : launch_persistent_cw<2, false>(MT, a, grid, s);
+    if (CW == 4) return g ? launch_persistent_cw<4, true>(MT, a, grid, s) : launch_persistent_cw<4, false>(MT, a, grid, s);
     return hipErrorInvalidValue;
 }
 
@@ -1417,12 +1483,13 @@ int choose_mt(int T, int k, int E)
     return 8;
 }
 
-int choose_cw(int MT, int H, int I)
+int choose_cw(int MT, int H, int I, bool gated)
 {
     // Small m-tiles stream weights: two-wave-column tiles keep two blocks per
     // CU.  Large m-tiles are MFMA-bound: four wave columns (and two row groups
-    // at MT = 8, two waves per SIMD) halve the operand traffic per MFMA.
-    return (MT >= 4 && I % 256 == 0 && H % 512 == 0) ? 4 : 2;
+    // at MT = 8, two waves per SIMD) halve the operand traffic per MFMA.  A
+    // linear1 tile spans 64*CW columns of h gated, 128*CW gate-less.
+    return (MT >= 4 && I % (gated ? 256 : 512) == 0 && H % 512 == 0) ? 4 : 2;
 }
 
 }  // namespace v4moe

@@ -24,6 +24,10 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "v4moe.h")
 ROUTE_LEARNED = 0
 ROUTE_HASH = 1
 
+ACT_SWIGLU = 0
+ACT_RELU2 = 1
+ACT_RELU = 2
+
 
 class V4MoeError(RuntimeError):
     def __init__(self, code: int, msg: str):
@@ -33,7 +37,7 @@ class V4MoeError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
-                ("E", ctypes.c_int32), ("topk", ctypes.c_int32)]
+                ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("act", ctypes.c_int32)]
 
 
 class Mat(ctypes.Structure):
@@ -105,8 +109,8 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def dims(T: int, H: int, I: int, E: int, topk: int) -> Dims:
-    return Dims(T, H, I, E, topk)
+def dims(T: int, H: int, I: int, E: int, topk: int, act: int = ACT_SWIGLU) -> Dims:
+    return Dims(T, H, I, E, topk, act)
 
 
 @dataclasses.dataclass
@@ -121,12 +125,12 @@ class DeviceMatrix:
 
 @dataclasses.dataclass
 class DeviceExperts:
-    gate: DeviceMatrix
+    gate: Optional[DeviceMatrix]   # None for the gate-less activations
     up: DeviceMatrix
     down: DeviceMatrix
 
     def c(self) -> ExpertsC:
-        return ExpertsC(self.gate.c(), self.up.c(), self.down.c())
+        return ExpertsC(Mat() if self.gate is None else self.gate.c(), self.up.c(), self.down.c())
 
 
 # ---- the C entry points ------------------------------------------------------------------
@@ -210,10 +214,12 @@ def upload_matrix(m, device="cuda") -> DeviceMatrix:
 
 def prepack(d: Dims, canonical: DeviceExperts) -> DeviceExperts:
     """Canonical -> packed device weights (blk tensors are shared)."""
-    def like(m: DeviceMatrix) -> DeviceMatrix:
+    def like(m: Optional[DeviceMatrix]) -> Optional[DeviceMatrix]:
+        if m is None:
+            return None
         return DeviceMatrix(torch.empty_like(m.fp4), torch.empty_like(m.e8m0), m.blk)
     packed = DeviceExperts(like(canonical.gate), like(canonical.up), like(canonical.down))
-    ws = torch.empty(256, dtype=torch.uint8, device=canonical.gate.fp4.device)
+    ws = torch.empty(256, dtype=torch.uint8, device=canonical.up.fp4.device)
     moe_prepack_weights(d, canonical, packed, ws)
     return packed
 
@@ -221,7 +227,7 @@ def prepack(d: Dims, canonical: DeviceExperts) -> DeviceExperts:
 def upload_experts(ex, d: Dims, device="cuda") -> DeviceExperts:
     """Host canonical weights (objects with gate/up/down, each fp4/e8m0/blk numpy
     arrays) -> packed device weights."""
-    canon = DeviceExperts(upload_matrix(ex.gate, device), upload_matrix(ex.up, device),
+    canon = DeviceExperts(None if ex.gate is None else upload_matrix(ex.gate, device), upload_matrix(ex.up, device),
                           upload_matrix(ex.down, device))
     packed = prepack(d, canon)
     del canon
@@ -232,15 +238,15 @@ class MoELayer:
     """Device-resident layer: packed expert weights, router and a workspace."""
 
     def __init__(self, H: int, I: int, E: int, topk: int, experts: DeviceExperts,
-                 w_router: torch.Tensor, device="cuda"):
-        self.H, self.I, self.E, self.topk = H, I, E, topk
+                 w_router: torch.Tensor, device="cuda", act: int = ACT_SWIGLU):
+        self.H, self.I, self.E, self.topk, self.act = H, I, E, topk, act
         self.experts = experts
         self.w_router = w_router
         self.device = device
         self._ws = None
 
     def dims(self, T: int) -> Dims:
-        return Dims(T, self.H, self.I, self.E, self.topk)
+        return Dims(T, self.H, self.I, self.E, self.topk, self.act)
 
     def workspace(self, T: int) -> torch.Tensor:
         n = moe_workspace_bytes(self.dims(T))

@@ -58,7 +58,19 @@ typedef struct {
     int32_t I;      /* expert intermediate size (linear1 N, linear2 K) */
     int32_t E;      /* routed experts                               */
     int32_t topk;   /* experts per token                            */
+    int32_t act;    /* expert activation, V4MOE_ACT_* (0: SwiGLU)   */
 } v4moe_dims;
+
+/* Expert activations.  SwiGLU (P1 §1.4): h = SiLU(gate x) * (up x).  The
+ * gate-less ones are the cheap alternative the pages recommend (P1, the
+ * hardware suggestions closing §1: an elementwise activation with no
+ * exponential or division, and no gate projection so that the intermediate
+ * can be wider at the same parameter count; the pages name no function):
+ * h = max(up x, 0)^2 or h = max(up x, 0).  Gate-less layers have no gate
+ * matrix (its pointers are ignored) and need I % 256 == 0. */
+#define V4MOE_ACT_SWIGLU 0
+#define V4MOE_ACT_RELU2  1
+#define V4MOE_ACT_RELU   2
 
 /* One expert weight matrix for all E experts: N output rows, K inputs.
  * P1 §4 (FP4 quantisation-aware training): FP4 E2M1 elements with a scale per
@@ -87,8 +99,9 @@ typedef struct {
     const float* blk;
 } v4moe_mat;
 
-/* The SwiGLU expert weights (P1 §1.4: gate, up and down projections).
- * gate, up: N = I, K = H.  down: N = H, K = I. */
+/* The expert weights (P1 §1.4: gate, up and down projections).
+ * gate, up: N = I, K = H.  down: N = H, K = I.  gate is ignored (may be all
+ * NULL) for the gate-less activations. */
 typedef struct {
     v4moe_mat gate;
     v4moe_mat up;

@@ -40,15 +40,15 @@ _layers = {}
 
 def layer_for(inp):
     d = inp.dims
-    key = (d.H, d.I, d.E, d.topk, id(inp.experts))
+    key = (d.H, d.I, d.E, d.topk, d.act, id(inp.experts))
     if key not in _layers:
         if len(_layers) > 2:
             _layers.clear()
             torch.cuda.empty_cache()
-        dims = v4moe.dims(max(d.T, 1), d.H, d.I, d.E, d.topk)
+        dims = v4moe.dims(max(d.T, 1), d.H, d.I, d.E, d.topk, d.act)
         ex = v4moe.upload_experts(inp.experts, dims, DEV)
         _layers[key] = v4moe.MoELayer(d.H, d.I, d.E, d.topk, ex,
-                                      torch.from_numpy(inp.w_router).to(DEV), DEV)
+                                      torch.from_numpy(inp.w_router).to(DEV), DEV, act=d.act)
     return _layers[key]
 
 
@@ -75,9 +75,9 @@ def run_fused(inp):
     return dict(out=out.cpu().numpy(), ids=ids.cpu().numpy(), w=w.cpu().numpy(), offsets=off.cpu().numpy())
 
 
-def custom(T, H, I, E, k, seed=3, mode=0, bias=False):
-    ex = inputs.gen_experts(seed, E, H, I)
-    return inputs.Inputs(dims=inputs.Dims(T, H, I, E, k), mode=mode, x=inputs.gen_x(seed, T, H),
+def custom(T, H, I, E, k, seed=3, mode=0, bias=False, act=inputs.ACT_SWIGLU):
+    ex = inputs.gen_experts(seed, E, H, I, gated=act == inputs.ACT_SWIGLU)
+    return inputs.Inputs(dims=inputs.Dims(T, H, I, E, k, act), mode=mode, x=inputs.gen_x(seed, T, H),
                          w_router=inputs.gen_router(seed, H, E),
                          bias=inputs.zipf_bias(seed, E) if bias else None,
                          token_ids=np.arange(T, dtype=np.int64) * 3 + 1 if mode == 1 else None,
@@ -177,6 +177,26 @@ def test_tiny_full_parity():
 ])
 def test_shapes_full_parity(T, H, I, E, k, mode, bias):
     full_check(custom(T, H, I, E, k, mode=mode, bias=bias), f"T{T}H{H}I{I}E{E}k{k}")
+
+
+RELU2, RELU = inputs.ACT_RELU2, inputs.ACT_RELU
+
+
+def test_tiny_gateless_full_parity():
+    full_check(inputs.make("tiny_relu2"), "tiny_relu2")
+
+
+@pytest.mark.parametrize("T,H,I,E,k,act", [
+    (37, 256, 256, 8, 2, RELU2),        # ragged tail, 16-row tiles, two-wave-column tiles
+    (40, 256, 768, 8, 2, RELU),         # I = 3 linear1 tiles of 256 columns, ReLU
+    (160, 512, 256, 8, 4, RELU2),       # 64-row tiles, persistent, CW = 2
+    (160, 512, 512, 8, 4, RELU),        # 64-row tiles, persistent, CW = 4
+    (600, 512, 512, 4, 2, RELU2),       # 128-row tiles (two launches), CW = 4
+    (300, 256, 256, 16, 3, RELU),       # 64-row tiles, odd k, CW = 2
+    (300, 256, 512, 16, 1, RELU2),      # 32-row tiles, k = 1
+])
+def test_gateless_shapes_full_parity(T, H, I, E, k, act):
+    full_check(custom(T, H, I, E, k, act=act), f"T{T}H{H}I{I}E{E}k{k}act{act}")
 
 
 def test_largest_hidden_and_intermediate():
@@ -298,6 +318,20 @@ def test_prefill_full_size():
     inp = inputs.make("prefill")
     g, f = sampled_check(inp, "prefill", n_sample=10)
     assert np.array_equal(run_fused(inp)["out"], f["out"])
+
+
+@pytest.mark.slow
+def test_decode_gateless_full_size():
+    """Gate-less squared-ReLU experts at I = 3072 (the SwiGLU experts' parameter count)."""
+    inp = inputs.make("decode_relu2")
+    g, f = sampled_check(inp, "decode_relu2", n_sample=16)
+    assert np.array_equal(run_fused(inp)["out"], f["out"])
+
+
+@pytest.mark.slow
+def test_prefill_gateless_full_size():
+    inp = inputs.make("prefill_relu2")
+    sampled_check(inp, "prefill_relu2", n_sample=8)
 
 
 @pytest.mark.slow
