@@ -160,8 +160,9 @@ def run_gpu(name, steps, warmup, layer_cache):
 
 def run_quantizer(E, H, I, reps):
     """FP32 master -> MXFP4 quantisation of every expert's gate, up and down
-    matrices of one layer (moe_quantize_weights, one launch per matrix).
-    Algorithmic bytes per weight: 4 read + 1/2 + 1/32 written (+ 4 per
+    matrices of one layer straight into the packed layout the layer reads
+    (moe_quantize_weights, one launch per matrix: the QAT forward's weight
+    step).  Algorithmic bytes per weight: 4 read + 1/2 + 1/32 written (+ 4 per
     128x128 block)."""
     import torch
     from fp4_weight_grouped_amd import v4moe
@@ -169,13 +170,13 @@ def run_quantizer(E, H, I, reps):
     dev = "cuda:0"
     shapes = [(E, I, H), (E, I, H), (E, H, I)]
     ws = [torch.randn(sh, device=dev) * 0.02 for sh in shapes]
-    outs = [v4moe.quantize_weights(w) for w in ws]
+    outs = [v4moe.quantize_weights(w, packed=True) for w in ws]
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
         for w, o in zip(ws, outs):
-            v4moe.moe_quantize_weights(w, o)
+            v4moe.moe_quantize_weights(w, o, packed=True)
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
@@ -187,7 +188,7 @@ def run_quantizer(E, H, I, reps):
     log(f"[bench] weight quantiser: {ms:.3f} ms for {n / 1e9:.2f} G weights, {gbs:.0f} GB/s")
     return dict(E=E, H=H, I=I, weights=n, ms=ms, algorithmic_bytes=nbytes, bound="hbm", achieved=gbs,
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
-                kernel="k_quantize_weights (fp32 master -> fp4 e2m1 + e8m0 + fp32 block scale)")
+                kernel="k_quantize_weights (fp32 master -> packed fp4 e2m1 + e8m0 + fp32 block scale)")
 
 
 def cpu_baseline(inp, max_tokens=128, min_seconds=10.0, max_reps=8):

@@ -387,8 +387,9 @@ __attribute__((visibility("default"))) int moe_prepack_weights(const v4moe_dims*
 }
 
 __attribute__((visibility("default"))) int moe_quantize_weights(int32_t E, int32_t N, int32_t K,
-                                                                const float* w, const v4moe_mat* out,
-                                                                uint64_t* clamped, void* stream)
+                                                                const float* w, int32_t packed,
+                                                                const v4moe_mat* out, uint64_t* clamped,
+                                                                void* stream)
 {
     if (!w || !out || !mat_ok(*out)) return V4MOE_ENULL;
     if (E < 1 || N < 128 || N % 128 || K < 128 || K % 128) return V4MOE_EDIMS;
@@ -397,7 +398,8 @@ __attribute__((visibility("default"))) int moe_quantize_weights(int32_t E, int32
     if (!di) return V4MOE_EDEVICE;
     if (launch_quantize_weights(E, N, K, w, static_cast<uint8_t*>(const_cast<void*>(out->fp4)),
                                 static_cast<uint8_t*>(const_cast<void*>(out->e8m0)), const_cast<float*>(out->blk),
-                                reinterpret_cast<unsigned long long*>(clamped), as_stream(stream)) != hipSuccess)
+                                reinterpret_cast<unsigned long long*>(clamped), packed ? 1 : 0,
+                                as_stream(stream)) != hipSuccess)
         return V4MOE_ELAUNCH;
     return V4MOE_OK;
 }

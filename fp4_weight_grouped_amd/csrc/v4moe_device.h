@@ -40,6 +40,18 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// Four fp32 values -> four OCP E2M1 codes, a in bits 0-3 ... d in bits 12-15:
+// nearest value, ties to the even code, magnitudes from 6 up saturate to 6, the
+// sign kept (a negative value that rounds to zero gives code 8).  gfx950's
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 does exactly this for every
+// non-NaN fp32 input.
+__device__ __forceinline__ uint32_t e2m1x4(float a, float b, float c, float d)
+{
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c, d, 1.0f, 1);
+    return r & 0xFFFFu;
+}
+
 // SiLU(g) * u with the hardware exp2 and reciprocal (about 2 ulp; the result
 // is requantised to E4M3 right after).
 __device__ __forceinline__ float silu_mul(float g, float u)

@@ -59,7 +59,7 @@ hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* w
 hipError_t launch_prepack(int E, int N, int K, const uint8_t* fp4_in, const uint8_t* e8_in,
                           uint8_t* fp4_out, uint8_t* e8_out, int32_t* bad, hipStream_t s);
 hipError_t launch_quantize_weights(int E, int N, int K, const float* w, uint8_t* fp4, uint8_t* e8, float* blk,
-                                  unsigned long long* clamped, hipStream_t s);
+                                  unsigned long long* clamped, int packed, hipStream_t s);
 hipError_t launch_dequant_export(int N, int K, int expert, const uint8_t* fp4, const uint8_t* e8,
                                  uint8_t* out, hipStream_t s);
 

@@ -27,6 +27,7 @@
 #include "v4moe_internal.h"
 
 #include <limits.h>
+#include <type_traits>
 
 namespace v4moe {
 
@@ -1126,9 +1127,9 @@ __global__ __launch_bounds__(256) void k_prepack(int E, int N, int K, const uint
 
 // FP32 master weights -> MXFP4 under fp32 128x128 block scales (P1 §4 and
 // P4 §4: the QAT forward quantises the FP32 master weights to FP4; format per
-// the OCP MX paper the pages cite).  One block of 256 threads per 128x128
-// block; float4 f = i*256 + tid of the block is row f/32, columns 4*(f%32)..+3,
-// so a 1x32 sub-block is 8 consecutive lanes.
+// the OCP MX paper the pages cite).  256 threads per 128x128 block; float4
+// f = i*256 + tid of the block is row f/32, columns 4*(f%32)..+3, so a 1x32
+// sub-block is 8 consecutive lanes.
 //   s = amax / 384 (fp32; 1 for an all-zero block): the block's largest
 //       magnitude lands on 6 * 2^6, FP4's largest value at the top of the
 //       lossless window;
@@ -1136,67 +1137,146 @@ __global__ __launch_bounds__(256) void k_prepack(int E, int N, int K, const uint
 //       shared exponent, E2M1's largest exponent being 2), raised to -8 below
 //       the window (counted in *clamped), 0 for an all-zero sub-block;
 //   code = nearest E2M1 of v * 2^-b, ties to the even code, saturating at 6,
-//       sign kept.
+//       sign kept (the hardware conversion, e2m1x4).
+// The max of v over each group of 8 consecutive lanes (DPP: swap neighbours,
+// swap pairs, mirror the two quads of the group).
+__device__ __forceinline__ float max8_lanes(float v)
+{
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+    return v;
+}
+
+// LDS staging pitch of the code rows (128 bytes of codes + 16: the 16-byte
+// reads of the packed copy-out, 16 rows apart, fall on distinct banks).
+constexpr int kQuantPitch = 144;
+
+// One 128x128 block: rows r = 8i + tid/32 (i < 16) held as float4 v[i]; the
+// codes (2 bytes per lane per row) and sub-block exponents go to LDS staging
+// rows (f4s: kQuantPitch bytes per row, e8s: 8 bytes per row) at column
+// offset h of the block pair.
+// FAST: v = w/s as RN(w * y) with y = RN(1/s), then two residual corrections
+// r = w - s*q (fma), q += r*y (fma); the first leaves q within one ulp of
+// w/s, so by Markstein's theorem the second gives the correctly rounded
+// quotient.  That needs the residuals exact, which holds for |w| >= 2^-103;
+// the caller takes FAST only when the block's amax >= 2^-84, where a smaller
+// |w| has |w/s| < 2^-10 and so only its sign can reach the output (code 0 or
+// 8, and a sub-block whose max is that small is clamped either way); the sign
+// is restored from w.  Otherwise the IEEE divide.
+template <bool FAST>
+__device__ __forceinline__ int quantize_block_rows(const float4 (&v)[16], float s, uint8_t* f4s, uint8_t* e8s,
+                                                   int h, int tid)
+{
+    const float y = 1.0f / s;
+    auto quot = [&](float x) {
+        if (!FAST) return x / s;
+        float q = x * y;
+        q = __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
+        q = __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
+        return __builtin_copysignf(q, x);
+    };
+    const int c4 = tid & 31;
+    const bool e8_lane = (c4 & 7) == 0;
+    int nclip = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int r = i * 8 + (tid >> 5);
+        const float q0 = quot(v[i].x), q1 = quot(v[i].y), q2 = quot(v[i].z), q3 = quot(v[i].w);
+        const float am = max8_lanes(fmaxf(fmaxf(fabsf(q0), fabsf(q1)), fmaxf(fabsf(q2), fabsf(q3))));
+        // floor(log2 am) - 2 from the exponent field; a subnormal am (field 0)
+        // is far below the window
+        int b = (int)((__float_as_uint(am) >> 23) & 255u) - 129;
+        const bool zero = am == 0.0f;
+        nclip += (!zero && b < -8 && e8_lane) ? 1 : 0;
+        b = zero ? 0 : min(max(b, -8), 6);
+        const float sc = __uint_as_float((uint32_t)(127 - b) << 23);   // 2^-b, exact
+        *reinterpret_cast<uint16_t*>(f4s + r * kQuantPitch + h * 64 + 2 * c4) =
+            (uint16_t)e2m1x4(q0 * sc, q1 * sc, q2 * sc, q3 * sc);
+        if (e8_lane) e8s[r * 8 + h * 4 + (c4 >> 3)] = (uint8_t)(127 + b);
+    }
+    return nclip;
+}
+
+// One workgroup per 128 rows x (up to) 256 columns: two 128x128 blocks in
+// turn, then 16-byte stores from LDS staging: whole 128-byte lines of codes
+// per row (canonical layout), or whole 1 KiB code records and 256-byte scale
+// records (packed layout, the records moe_prepack_weights would write).
 __global__ __launch_bounds__(256) void k_quantize_weights(int N, int K, const float* __restrict__ w,
                                                           uint8_t* __restrict__ fp4, uint8_t* __restrict__ e8,
                                                           float* __restrict__ blk,
-                                                          unsigned long long* __restrict__ clamped)
+                                                          unsigned long long* __restrict__ clamped, int packed)
 {
-    __shared__ float red[4];
-    const int NB = N / 128, KB = K / 128;
-    const int kb = blockIdx.x % KB;
-    const int nb = (blockIdx.x / KB) % NB;
-    const size_t e = blockIdx.x / ((size_t)KB * NB);
+    __shared__ float red[2][4];
+    __shared__ __align__(16) uint8_t f4s[128 * kQuantPitch];
+    __shared__ __align__(16) uint8_t e8s[128 * 8];
+    const int NB = N / 128, KB = K / 128, KP = (KB + 1) / 2;
+    const int kp = blockIdx.x % KP;
+    const int nb = (blockIdx.x / KP) % NB;
+    const size_t e = blockIdx.x / ((size_t)KP * NB);
+    const int nkb = min(2, KB - 2 * kp);                      // 128x128 blocks in this workgroup
     const int tid = threadIdx.x, lane = tid & 63;
     const int c4 = tid & 31;                                 // float4 column in the block row
-    const size_t row0 = e * N + (size_t)nb * 128;
-    float4 v[16];
-    float amax = 0.0f;
+    const size_t rowbase = e * N + (size_t)nb * 128;
+    int nclip = 0;
+    for (int h = 0; h < nkb; h++) {
+        const int kb = 2 * kp + h;
+        const float* wp = w + (rowbase + (tid >> 5)) * K + (size_t)kb * 128 + 4 * c4;
+        float4 v[16];
+        float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const int r = i * 8 + (tid >> 5);
-        v[i] = *reinterpret_cast<const float4*>(w + (row0 + r) * K + (size_t)kb * 128 + 4 * c4);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+        for (int i = 0; i < 16; i++) {
+            v[i] = *reinterpret_cast<const float4*>(wp + (size_t)i * 8 * K);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        if (lane == 0) red[h][tid >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
+        const float s = amax > 0.0f ? amax / 384.0f : 1.0f;
+        if (tid == 0) blk[(e * NB + nb) * KB + kb] = s;
+        nclip += amax >= 0x1p-84f ? quantize_block_rows<true>(v, s, f4s, e8s, h, tid)
+                                  : quantize_block_rows<false>(v, s, f4s, e8s, h, tid);
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if (lane == 0) red[tid >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = amax > 0.0f ? amax / 384.0f : 1.0f;
-    if (tid == 0) blk[(e * NB + nb) * KB + kb] = s;
-    auto code = [](float x) -> uint32_t {
-        const float m = fabsf(x);
-        const uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) +
-                           (m > 5.0f);
-        return c | ((__float_as_uint(x) >> 28) & 8u);
-    };
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const int r = i * 8 + (tid >> 5);
-        const float q[4] = {v[i].x / s, v[i].y / s, v[i].z / s, v[i].w / s};
-        float am = fmaxf(fmaxf(fabsf(q[0]), fabsf(q[1])), fmaxf(fabsf(q[2]), fabsf(q[3])));
-        am = fmaxf(am, __shfl_xor(am, 1));
-        am = fmaxf(am, __shfl_xor(am, 2));
-        am = fmaxf(am, __shfl_xor(am, 4));
-        int b = 0;
-        bool clip = false;
-        if (am > 0.0f) {
-            const int ex = (int)((__float_as_uint(am) >> 23) & 255u);   // 0: subnormal, far below the window
-            b = ex == 0 ? -1000 : ex - 127 - 2;
-            if (b < -8) { b = -8; clip = true; }
-            b = min(b, 6);
+    if (packed) {
+        // code records (n-tile t of the block, chunk 2kp+h): slot sl holds row
+        // 16t + sl%16, elements 32(sl/16)..+31 of the chunk
+        for (int idx = tid; idx < 8 * nkb * 64; idx += 256) {
+            const int t = idx / (nkb * 64), h = (idx / 64) % nkb, sl = idx % 64;
+            *reinterpret_cast<uint4*>(fp4 + ((((e * (N / 16) + nb * 8 + t) * KB + 2 * kp + h) * 64) + sl) * 16) =
+                *reinterpret_cast<const uint4*>(f4s + (t * 16 + (sl & 15)) * kQuantPitch + h * 64 + (sl >> 4) * 16);
         }
-        const float sc = __uint_as_float((uint32_t)(127 - b) << 23);   // 2^-b, exact
-        const uint32_t c0 = code(q[0] * sc), c1 = code(q[1] * sc), c2 = code(q[2] * sc), c3 = code(q[3] * sc);
-        const size_t n = row0 + r;
-        *reinterpret_cast<uint16_t*>(fp4 + n * (K / 2) + ((size_t)kb * 128 + 4 * c4) / 2) =
-            (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-        if ((c4 & 7) == 0) {
-            e8[n * (K / 32) + (size_t)kb * 4 + (c4 >> 3)] = (uint8_t)(127 + b);
-            if (clip && clamped) atomicAdd(clamped, 1ull);
+        // scale records (n-tile quad qd, chunk 2kp+h): byte j of lane sl's
+        // dword = exponent of row (4qd+j)*16 + sl%16, sub-block sl/16
+        for (int idx = tid; idx < 2 * nkb * 64; idx += 256) {
+            const int qd = idx / (nkb * 64), h = (idx / 64) % nkb, sl = idx % 64;
+            uint32_t d = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                d |= (uint32_t)e8s[((qd * 4 + j) * 16 + (sl & 15)) * 8 + h * 4 + (sl >> 4)] << (8 * j);
+            *reinterpret_cast<uint32_t*>(e8 + (((e * (N / 64) + nb * 2 + qd) * KB + 2 * kp + h) * 64 + sl) * 4) = d;
+        }
+    } else {
+        // codes: 128 rows x nkb*64 bytes, 16 bytes per lane
+        const int segs = nkb * 4;
+        for (int idx = tid; idx < 128 * segs; idx += 256) {
+            const int r = idx / segs, sg = idx % segs;
+            *reinterpret_cast<uint4*>(fp4 + (rowbase + r) * (K / 2) + (size_t)kp * 128 + sg * 16) =
+                *reinterpret_cast<const uint4*>(f4s + r * kQuantPitch + sg * 16);
+        }
+        // exponents: 4 bytes per row and block
+        for (int idx = tid; idx < 128 * nkb; idx += 256) {
+            const int r = idx / nkb, h = idx % nkb;
+            *reinterpret_cast<uint32_t*>(e8 + (rowbase + r) * (K / 32) + (size_t)kp * 8 + h * 4) =
+                *reinterpret_cast<const uint32_t*>(e8s + r * 8 + h * 4);
         }
     }
+    if (nclip && clamped) atomicAdd(clamped, (unsigned long long)nclip);
 }
 
 // Test export of the weights exactly as the matrix kernels see them: one wave
@@ -1445,11 +1525,12 @@ hipError_t launch_prepack(int E, int N, int K, const uint8_t* fp4_in, const uint
 }
 
 hipError_t launch_quantize_weights(int E, int N, int K, const float* w, uint8_t* fp4, uint8_t* e8, float* blk,
-                                  unsigned long long* clamped, hipStream_t s)
+                                  unsigned long long* clamped, int packed, hipStream_t s)
 {
-    const size_t blocks = (size_t)E * (N / 128) * (K / 128);
+    const size_t blocks = (size_t)E * (N / 128) * ((K / 128 + 1) / 2);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_quantize_weights, dim3((unsigned)blocks), dim3(256), 0, s, N, K, w, fp4, e8, blk, clamped);
+    hipLaunchKernelGGL(k_quantize_weights, dim3((unsigned)blocks), dim3(256), 0, s, N, K, w, fp4, e8, blk, clamped,
+                       packed);
     return hipGetLastError();
 }
 

@@ -75,7 +75,7 @@ def lib():
         L.moe_prepack_weights.argtypes = [_DP, ctypes.POINTER(ExpertsC), ctypes.POINTER(ExpertsC),
                                           _vp, _sz, _vp]
         L.moe_dequant_fp8.argtypes = [ctypes.POINTER(Mat), _i32, _i32, _i32, _vp, _vp]
-        L.moe_quantize_weights.argtypes = [_i32, _i32, _i32, _vp, ctypes.POINTER(Mat), _vp, _vp]
+        L.moe_quantize_weights.argtypes = [_i32, _i32, _i32, _vp, _i32, ctypes.POINTER(Mat), _vp, _vp]
         L.moe_time_next_ffn.argtypes = [_vp, _vp]
         L.moe_time_next_ffn.restype = None
         for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
@@ -178,23 +178,25 @@ def moe_dequant_fp8(m: DeviceMatrix, N: int, K: int, expert: int, out):
     _check(lib().moe_dequant_fp8(ctypes.byref(mc), N, K, expert, _p(out), _stream()))
 
 
-def moe_quantize_weights(w, out: DeviceMatrix, clamped=None):
-    """w: fp32 [E][N][K] on the device -> out (canonical fp4 [E][N][K/2], e8m0
-    [E][N][K/32], blk [E][N/128][K/128]); clamped: int64 [1] device tensor the
-    number of clamped sub-blocks is added to, or None."""
+def moe_quantize_weights(w, out: DeviceMatrix, clamped=None, packed: bool = False):
+    """w: fp32 [E][N][K] on the device -> out (fp4 and e8m0 in the canonical
+    or the packed layout, blk [E][N/128][K/128]); clamped: int64 [1] device
+    tensor the number of clamped sub-blocks is added to, or None."""
     E, N, K = w.shape
     oc = out.c()
-    _check(lib().moe_quantize_weights(E, N, K, _p(w), ctypes.byref(oc), _p(clamped), _stream()))
+    _check(lib().moe_quantize_weights(E, N, K, _p(w), 1 if packed else 0, ctypes.byref(oc), _p(clamped),
+                                      _stream()))
 
 
-def quantize_weights(w, clamped=None) -> DeviceMatrix:
-    """Allocating convenience around moe_quantize_weights."""
+def quantize_weights(w, clamped=None, packed: bool = False) -> DeviceMatrix:
+    """Allocating convenience around moe_quantize_weights (the packed layout
+    has the same byte counts as the canonical one)."""
     E, N, K = w.shape
     dev = w.device
     out = DeviceMatrix(fp4=torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev),
                        e8m0=torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev),
                        blk=torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev))
-    moe_quantize_weights(w, out, clamped)
+    moe_quantize_weights(w, out, clamped, packed)
     return out
 
 

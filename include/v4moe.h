@@ -192,14 +192,18 @@ int moe_layer_forward(const v4moe_dims* d, const uint16_t* x, const float* w_rou
                       int32_t* expert_offsets, uint16_t* out,
                       void* workspace, size_t ws_bytes, void* stream);
 
-/* FP32 master weights -> CANONICAL FP4 weights (P1 §4 and P4 §4: FP4
- * quantisation-aware training quantises the FP32 master weights to FP4 in the
- * forward pass; element format and shared-exponent rule per the OCP MX
- * specification the pages cite).
+/* FP32 master weights -> FP4 weights (P1 §4 and P4 §4: FP4 quantisation-aware
+ * training quantises the FP32 master weights to FP4 in the forward pass;
+ * element format and shared-exponent rule per the OCP MX specification the
+ * pages cite).
  *   w: device fp32 [E][N][K], row-major, finite values; N % 128 == 0,
  *      K % 128 == 0; 16-byte aligned.
- *   out: device CANONICAL matrix (fp4 [E][N][K/2], e8m0 [E][N][K/32],
- *      blk [E][N/128][K/128]), written in full.
+ *   packed: 0 writes the CANONICAL layout (fp4 [E][N][K/2], e8m0
+ *      [E][N][K/32]); non-zero writes the PACKED layout the matrix kernels
+ *      read, byte for byte what moe_prepack_weights makes of the canonical
+ *      output (so a training step needs no separate prepack).
+ *   out: device matrix in that layout plus blk [E][N/128][K/128], written in
+ *      full.
  * Per 128x128 block, s = max|w| / 384 in fp32 (1 for an all-zero block), so
  * the block's largest magnitude maps to 6 * 2^6, FP4's largest value at the
  * top of the lossless window.  Per 1x32 sub-block of a row, v = w / s in fp32,
@@ -210,7 +214,7 @@ int moe_layer_forward(const v4moe_dims* d, const uint16_t* x, const float* w_rou
  * clamped: device uint64 to which the number of clamped sub-blocks is added
  * (the caller clears it), or NULL.  Asynchronous on `stream`; allocates
  * nothing.  The output passes moe_prepack_weights' window check. */
-int moe_quantize_weights(int32_t E, int32_t N, int32_t K, const float* w,
+int moe_quantize_weights(int32_t E, int32_t N, int32_t K, const float* w, int32_t packed,
                          const v4moe_mat* out, uint64_t* clamped, void* stream);
 
 /* Offline: canonical -> packed weight layout (both device buffers of equal

@@ -72,9 +72,9 @@ def test_error_paths_without_device():
     assert L.moe_dequant_fp8(ctypes.byref(m), 15, 128, 0, p, None) == -2
     assert L.moe_dequant_fp8(ctypes.byref(m), 16, 100, 0, p, None) == -2
     assert L.moe_prepack_weights(ctypes.byref(d), ctypes.byref(ex), ctypes.byref(ex), p, 8, None) == -4
-    assert L.moe_quantize_weights(1, 100, 128, p, ctypes.byref(m), None, None) == -2
-    assert L.moe_quantize_weights(1, 128, 64, p, ctypes.byref(m), None, None) == -2
-    assert L.moe_quantize_weights(0, 128, 128, p, ctypes.byref(m), None, None) == -2
-    assert L.moe_quantize_weights(1, 128, 128, None, ctypes.byref(m), None, None) == -1
-    assert L.moe_quantize_weights(1, 128, 128, mis, ctypes.byref(m), None, None) == -3
-    assert L.moe_quantize_weights(1, 128, 128, p, ctypes.byref(v4moe.Mat(4096, 0, 4096)), None, None) == -1
+    assert L.moe_quantize_weights(1, 100, 128, p, 0, ctypes.byref(m), None, None) == -2
+    assert L.moe_quantize_weights(1, 128, 64, p, 0, ctypes.byref(m), None, None) == -2
+    assert L.moe_quantize_weights(0, 128, 128, p, 1, ctypes.byref(m), None, None) == -2
+    assert L.moe_quantize_weights(1, 128, 128, None, 0, ctypes.byref(m), None, None) == -1
+    assert L.moe_quantize_weights(1, 128, 128, mis, 0, ctypes.byref(m), None, None) == -3
+    assert L.moe_quantize_weights(1, 128, 128, p, 0, ctypes.byref(v4moe.Mat(4096, 0, 4096)), None, None) == -1

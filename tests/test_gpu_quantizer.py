@@ -18,8 +18,9 @@ DEV = "cuda:0"
 def master_weights(rng, E, N, K):
     """Normal weights with a per-row log-normal magnitude, plus the cases the
     method has: an all-zero block, an all-zero sub-block, sub-blocks far below
-    their block (clamped), fp32 subnormals, signed zeros, exact E2M1 ties and
-    values that saturate at 6."""
+    their block (clamped), fp32 subnormals, signed zeros, exact E2M1 ties,
+    values that saturate at 6, and blocks of tiny magnitude (both ways of
+    forming w / s)."""
     w = (rng.standard_normal((E, N, K)) * np.exp(rng.standard_normal((E, N, 1)))).astype(np.float32)
     if N >= 256 and K >= 256:
         w[0, :128, :128] = 0.0                                # all-zero block: s = 1
@@ -27,6 +28,13 @@ def master_weights(rng, E, N, K):
         w[0, 129, 128:160] = -0.0                             # signed zeros keep code 8
         w[0, 130, 160:192] *= np.float32(1e-9)                # below the window: clamped
         w[0, 131, 192:224] = np.float32(1e-41) * rng.standard_normal(32).astype(np.float32)  # subnormals
+    if N >= 384 and K >= 256:
+        w[0, 256:384, :128] *= np.float32(1e-30)            # block max below 2^-84: the divide path
+        tiny = w[0, 256:384, 128:256]                         # block max just above 2^-84 ...
+        tiny *= np.float32(2.0 ** -80)
+        tiny[5, :32] = np.float32(1e-38) * rng.standard_normal(32).astype(np.float32)   # ... with w < 2^-103
+        tiny[6, 32:48] = np.float32(3e-44)                   # subnormal weights
+        tiny[6, 48:64] = -np.float32(3e-44)
     # ties: a block whose max is 384 (s = 1) and a sub-block with max 4 (b = 0)
     # holding every E2M1 midpoint and both signs
     kb = 2 if K >= 384 else 0
@@ -105,3 +113,22 @@ def test_quantized_weights_feed_the_layer():
             torch.cuda.synchronize()
             want = oracle.dequant_matrix(fp4[e], e8[e])
             assert np.array_equal(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("E,H,I,seed", [(2, 256, 384, 3), (1, 512, 128, 4)])
+def test_packed_output_equals_prepacked_canonical(E, H, I, seed):
+    """packed=1 writes byte for byte what moe_prepack_weights makes of the
+    canonical output (gate/up: N = I, K = H; down: N = H, K = I, so both an
+    odd and an even number of 128-wide chunks occur)."""
+    print(f"quantize packed E={E} H={H} I={I}", flush=True)
+    rng = np.random.default_rng(seed)
+    wg = torch.from_numpy(master_weights(rng, E, I, H)).to(DEV)
+    wd = torch.from_numpy(master_weights(rng, E, H, I)).to(DEV)
+    canon = v4moe.DeviceExperts(v4moe.quantize_weights(wg), v4moe.quantize_weights(wg), v4moe.quantize_weights(wd))
+    ref = v4moe.prepack(v4moe.dims(1, H, I, E, 1), canon)
+    pg, pd = v4moe.quantize_weights(wg, packed=True), v4moe.quantize_weights(wd, packed=True)
+    torch.cuda.synchronize()
+    for got, want in ((pg, ref.gate), (pd, ref.down)):
+        assert torch.equal(got.fp4, want.fp4)
+        assert torch.equal(got.e8m0, want.e8m0)
+        assert torch.equal(got.blk, want.blk)
