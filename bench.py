@@ -19,7 +19,13 @@ the same counters' reading for a plain copy kernel of known size); it is
 reported only while the kernel sources hash to the value recorded with it.
 The CPU baseline is the C oracle (test infrastructure) timed on the host cores.
 The weight quantiser (FP32 master -> MXFP4, one layer's experts) is reported
-as a side record against the HBM peak.
+as a side record against the HBM peak.  Each workload record also carries the
+per-step device time (median, p10, p90 of HIP events around each step), the
+device time of each step of the layer through the separate entry points
+(route, permute, expert_ffn, combine), and board power and shader clock
+sampled from the amdgpu sysfs files during about a second of back-to-back
+steps outside the timed region.  The weights of the large workloads (3.4 GB)
+are 13x the 256 MB last-level cache, so every step streams them from HBM.
 
 `--copy-bytes N` runs only a plain device copy of N bytes (the calibration
 kernel for those counters) and prints what it did.
@@ -103,6 +109,95 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def pct(v, q):
+    return float(np.percentile(np.asarray(v, np.float64), q))
+
+
+def attribution(layer, x, bias, mode, tid, reps=10):
+    """Device time of each step of the layer, through the separate entry
+    points (moe_route, moe_permute = x quantisation + permutation,
+    moe_expert_ffn, moe_combine) with events between them; medians in ms."""
+    import torch
+    from fp4_weight_grouped_amd import v4moe
+    T = x.shape[0]
+    d = layer.dims(T)
+    dev = layer.device
+    P = T * layer.topk
+    ids = torch.empty((T, layer.topk), dtype=torch.int32, device=dev)
+    w = torch.empty((T, layer.topk), dtype=torch.float32, device=dev)
+    off = torch.empty(layer.E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(P, dtype=torch.int32, device=dev)
+    pp = torch.empty(P, dtype=torch.int32, device=dev)
+    xq = torch.empty((T, layer.H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, layer.H // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((P, layer.H), dtype=torch.int16, device=dev)
+    out = torch.empty((T, layer.H), dtype=torch.int16, device=dev)
+    ws = layer.workspace(T)
+    steps = [
+        ("route", lambda: v4moe.moe_route(d, x, layer.w_router, bias, mode, tid, ids, w, ws)),
+        ("permute", lambda: v4moe.moe_permute(d, x, ids, off, sp, pp, xq, xs, ws)),
+        ("expert_ffn", lambda: v4moe.moe_expert_ffn(d, xq, xs, off, sp, layer.experts, y, ws)),
+        ("combine", lambda: v4moe.moe_combine(d, y, w, out)),
+    ]
+    times = {k: [] for k, _ in steps}
+    for rep in range(reps + 2):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
+        evs[0].record()
+        for i, (_, f) in enumerate(steps):
+            f()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        if rep >= 2:
+            for i, (k, _) in enumerate(steps):
+                times[k].append(evs[i].elapsed_time(evs[i + 1]))
+    return {k: float(np.median(v)) for k, v in times.items()}
+
+
+def read_sysfs_power_clock():
+    """Best effort: average board power (W) and current shader clock (MHz) from
+    the amdgpu sysfs files of the first card that has them."""
+    pw = clk = None
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            f = glob.glob(dev + "/hwmon/hwmon*/power1_average") + glob.glob(dev + "/hwmon/hwmon*/power1_input")
+            if f and pw is None:
+                pw = int(open(f[0]).read()) / 1e6
+            if clk is None and os.path.exists(dev + "/pp_dpm_sclk"):
+                for line in open(dev + "/pp_dpm_sclk"):
+                    if line.strip().endswith("*"):
+                        clk = float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+    return pw, clk
+
+
+def sustained_power_clock(fn, seconds=1.0):
+    """Run fn back to back for about `seconds` (not timed for the metric) and
+    sample power and clock every 20 ms on a host thread."""
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            samples.append(read_sysfs_power_clock())
+            time.sleep(0.02)
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    pw = [p for p, _ in samples if p is not None]
+    ck = [c for _, c in samples if c is not None]
+    return dict(power_w_mean=float(np.mean(pw)) if pw else None, power_w_max=float(np.max(pw)) if pw else None,
+                sclk_mhz_mean=float(np.mean(ck)) if ck else None, samples=len(samples),
+                source="amdgpu sysfs (hwmon power1_average, pp_dpm_sclk), sampled every 20 ms")
+
+
 def run_gpu(name, steps, warmup, layer_cache):
     import torch
     from fp4_weight_grouped_amd import inputs, v4moe
@@ -130,18 +225,25 @@ def run_gpu(name, steps, warmup, layer_cache):
         layer.forward(x, bias, inp.mode, tid, out=out)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:          # torch creates the HIP event on first record
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev + sev:    # torch creates the HIP event on first record
         a.record()
         b.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        sev[i][0].record()
         v4moe.moe_time_next_ffn(*ev[i])
         _, ids, _, off = layer.forward(x, bias, inp.mode, tid, out=out)
+        sev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ffn_all = [a.elapsed_time(b) for a, b in ev]
+    step_all = [a.elapsed_time(b) for a, b in sev]
+    ffn_ms = float(np.mean(ffn_all))
+    attr = attribution(layer, x, bias, inp.mode, tid)
+    pc = sustained_power_clock(lambda: layer.forward(x, bias, inp.mode, tid, out=out))
     counts = np.diff(off.cpu().numpy())
     n_active = int((counts > 0).sum())
     mats = 3 if d.act == inputs.ACT_SWIGLU else 2
@@ -152,9 +254,15 @@ def run_gpu(name, steps, warmup, layer_cache):
              tokens_per_s=d.T / (ms_step / 1e3), ffn_ms=ffn_ms, active_experts=n_active,
              load_max_over_mean=float(counts.max() / counts.mean()), idle_experts=int((counts == 0).sum()),
              weight_bytes=wbytes, ffn_hbm_gbs=wbytes / (ffn_ms / 1e3) / 1e9,
-             ffn_tflops=flops / (ffn_ms / 1e3) / 1e12)
+             ffn_tflops=flops / (ffn_ms / 1e3) / 1e12,
+             step_device_ms=dict(median=float(np.median(step_all)), p10=pct(step_all, 10), p90=pct(step_all, 90)),
+             ffn_device_ms=dict(median=float(np.median(ffn_all)), p10=pct(ffn_all, 10), p90=pct(ffn_all, 90)),
+             attribution_ms=attr, power_clock=pc)
     log(f"[bench] {name}: {ms_step:.3f} ms/step, ffn {ffn_ms:.3f} ms, "
         f"{r['ffn_hbm_gbs']:.0f} GB/s, {r['ffn_tflops']:.0f} TFLOP/s, active {n_active}")
+    log(f"[bench] {name}: step device ms median {r['step_device_ms']['median']:.3f} "
+        f"(p10 {r['step_device_ms']['p10']:.3f}, p90 {r['step_device_ms']['p90']:.3f}); "
+        f"attribution {', '.join(f'{k} {v:.3f}' for k, v in attr.items())}; power/clock {pc}")
     return r, inp
 
 
@@ -204,8 +312,16 @@ def cpu_baseline(inp, max_tokens=128, min_seconds=10.0, max_reps=8):
         oracle.layer_forward(inp, subset=sub)
         dt += time.perf_counter() - t0
         reps += 1
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=reps * n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                seconds=dt, repetitions=reps,
+                seconds=dt, repetitions=reps, cpu_model=cpu_model,
                 sample=(f"whole layer forward of all {T} tokens of the workload, {reps} times" if sub is None else
                         f"routing/quantisation/permutation of all {T} tokens, expert FFN + combine "
                         f"of the first {n} tokens, {reps} times; rate = those tokens / wall time"))
