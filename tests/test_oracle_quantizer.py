@@ -155,3 +155,62 @@ def test_quantised_weights_dequantise_losslessly():
     got = np.vectorize(oracle.e4m3_value)(q.astype(np.int64))
     want = e2m1_values(unpack_codes(fp4)[0]) * np.ldexp(1.0, np.repeat(e8[0].astype(np.int64) - 127, 32, axis=1))
     assert np.array_equal(got, want)
+
+
+def test_reconstruction_error_within_e2m1_half_step():
+    """|w - blk * e2m1(code) * 2^b| <= blk * 2^b * (half the E2M1 spacing at
+    |v| 2^-b), or the saturation excess above 6, for every element: the
+    quantiser picks the nearest representable value under its own scales."""
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((2, 256, 384)) * np.exp(2 * rng.standard_normal((2, 256, 1)))).astype(np.float32)
+    fp4, e8, s, clamped = oracle.quantize_weights(w)
+    codes = unpack_codes(fp4)
+    b = np.repeat(e8.astype(np.int64) - 127, 32, axis=2)
+    blk = np.repeat(np.repeat(s.astype(np.float64), 128, 1), 128, 2)
+    deq = e2m1_values(codes) * np.ldexp(1.0, b) * blk
+    m = np.abs(w.astype(np.float64) / blk) * np.ldexp(1.0, -b)        # |v| 2^-b (fp64)
+    spacing = np.where(m < 2, 0.5, np.where(m < 4, 1.0, 2.0))
+    bound = np.where(m <= 6, spacing / 2, m - 6) * np.ldexp(1.0, b) * blk
+    err = np.abs(w - deq)
+    assert np.all(err <= bound * (1 + 1e-6) + 1e-30), np.max(err / np.maximum(bound, 1e-300))
+    # on these weights the MXFP4 map keeps about 88% of the signal
+    assert np.linalg.norm(w - deq) / np.linalg.norm(w) < 0.15
+
+
+def test_layer_from_fp32_master_weights():
+    """Dense equivalence starting from FP32 master weights: quantise with the
+    oracle, run the layer with every token routed to every expert (exact
+    mode), and compare with a dense SwiGLU FFN on the same master weights in
+    fp64.  The only differences are the FP4 weight and FP8 activation
+    quantisation: about 12% relative error per MXFP4 matrix on Gaussian
+    weights, about 21% through the three matrices and SwiGLU here, far below
+    what a wrong scale or transposition gives (> 100%)."""
+    from fp4_weight_grouped_amd import inputs
+    T, H, I, E = 16, 256, 128, 4
+    rng = np.random.default_rng(5)
+    wg, wu = (rng.standard_normal((E, I, H)).astype(np.float32) * np.float32(0.05) for _ in range(2))
+    wd = rng.standard_normal((E, H, I)).astype(np.float32) * np.float32(0.05)
+    mats = []
+    for wm in (wg, wu, wd):
+        fp4, e8, s, clamped = oracle.quantize_weights(wm)
+        assert clamped == 0
+        mats.append(inputs.Matrix(fp4=fp4, e8m0=e8, blk=s))
+    x = inputs.gen_x(5, T, H)
+    inp = inputs.Inputs(dims=inputs.Dims(T, H, I, E, E), mode=1, x=x, w_router=inputs.gen_router(5, H, E),
+                        bias=None, token_ids=None, experts=inputs.Experts(*mats))
+    r = oracle.layer_forward(inp, exact=True)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = np.zeros((T, H))
+    for e in range(E):
+        G = xf @ wg[e].T.astype(np.float64)
+        U = xf @ wu[e].T.astype(np.float64)
+        ref += (1.0 / E) * ((G / (1 + np.exp(-G)) * U) @ wd[e].T.astype(np.float64))
+    rel = np.linalg.norm(r["out_exact"] - ref) / np.linalg.norm(ref)
+    assert rel < 0.3, rel
+    # a transposed down matrix or a dropped block scale is far off
+    bad = np.zeros((T, H))
+    for e in range(E):
+        G = xf @ wg[e].T.astype(np.float64)
+        U = xf @ wu[e].T.astype(np.float64)
+        bad += (1.0 / E) * ((G / (1 + np.exp(-G)) * U) @ wd[e].reshape(I, H).astype(np.float64))
+    assert np.linalg.norm(r["out_exact"] - bad) / np.linalg.norm(ref) > 1.0
