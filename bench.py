@@ -198,7 +198,7 @@ def sustained_power_clock(fn, seconds=1.0):
                 source="amdgpu sysfs (hwmon power1_average, pp_dpm_sclk), sampled every 20 ms")
 
 
-def run_gpu(name, steps, warmup, layer_cache):
+def run_gpu(name, steps, warmup, layer_cache, extras=True):
     import torch
     from fp4_weight_grouped_amd import inputs, v4moe
 
@@ -242,8 +242,8 @@ def run_gpu(name, steps, warmup, layer_cache):
     ffn_all = [a.elapsed_time(b) for a, b in ev]
     step_all = [a.elapsed_time(b) for a, b in sev]
     ffn_ms = float(np.mean(ffn_all))
-    attr = attribution(layer, x, bias, inp.mode, tid)
-    pc = sustained_power_clock(lambda: layer.forward(x, bias, inp.mode, tid, out=out))
+    attr = attribution(layer, x, bias, inp.mode, tid) if extras else None
+    pc = sustained_power_clock(lambda: layer.forward(x, bias, inp.mode, tid, out=out)) if extras else None
     counts = np.diff(off.cpu().numpy())
     n_active = int((counts > 0).sum())
     mats = 3 if d.act == inputs.ACT_SWIGLU else 2
@@ -261,8 +261,9 @@ def run_gpu(name, steps, warmup, layer_cache):
     log(f"[bench] {name}: {ms_step:.3f} ms/step, ffn {ffn_ms:.3f} ms, "
         f"{r['ffn_hbm_gbs']:.0f} GB/s, {r['ffn_tflops']:.0f} TFLOP/s, active {n_active}")
     log(f"[bench] {name}: step device ms median {r['step_device_ms']['median']:.3f} "
-        f"(p10 {r['step_device_ms']['p10']:.3f}, p90 {r['step_device_ms']['p90']:.3f}); "
-        f"attribution {', '.join(f'{k} {v:.3f}' for k, v in attr.items())}; power/clock {pc}")
+        f"(p10 {r['step_device_ms']['p10']:.3f}, p90 {r['step_device_ms']['p90']:.3f})")
+    if extras:
+        log(f"[bench] {name}: attribution {', '.join(f'{k} {v:.3f}' for k, v in attr.items())}; power/clock {pc}")
     return r, inp
 
 
@@ -337,6 +338,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true", help="skip the weight-quantiser side report")
     ap.add_argument("--copy-bytes", type=int, default=0, help="only run the counter-calibration copy")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-entry-point attribution and the power/clock sampling")
+    ap.add_argument("--only-quantizer", action="store_true",
+                    help="only time the weight quantiser on the workload's layer shape and print its record")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -349,11 +354,16 @@ def main():
     if args.copy_bytes:
         copy_calibration(args.copy_bytes, args.steps)
         return
+    if args.only_quantizer:
+        from fp4_weight_grouped_amd import inputs
+        d = inputs.WORKLOADS[args.workload].dims
+        print(json.dumps({"weight_quantizer": run_quantizer(d.E, d.H, d.I, args.steps)}), flush=True)
+        return
     cache = {}
-    head, inp = run_gpu(args.workload, args.steps, args.warmup, cache)
+    head, inp = run_gpu(args.workload, args.steps, args.warmup, cache, not args.no_extras)
     side = None
     if not args.no_prefill and args.workload != "prefill":
-        side, _ = run_gpu("prefill", max(5, args.steps // 2), max(2, args.warmup // 2), cache)
+        side, _ = run_gpu("prefill", max(5, args.steps // 2), max(2, args.warmup // 2), cache, not args.no_extras)
 
     quant = None
     if not args.no_quantizer:
