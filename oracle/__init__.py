@@ -90,6 +90,9 @@ def lib():
                                         ctypes.POINTER(OrcWeights), i32p, f32p, i32p, i32p, i32p,
                                         u8p, f32p, vp, vp, vp, vp, ci]
         L.orc_layer_forward.restype = ci
+        L.orc_layer_backward.argtypes = [ci, ci, ci, ci, ci, ci, u16p, f32p, vp, ci, vp,
+                                         ctypes.POINTER(OrcWeights), u16p, vp, vp, vp, vp, vp, vp, ci, vp, ci]
+        L.orc_layer_backward.restype = ci
         _lib = L
     return _lib
 
@@ -267,4 +270,50 @@ def layer_forward(inp, subset=None, want_y=False, exact=False, k=None):
         res["y"] = y
     if exact:
         res["out_exact"] = oex
+    return res
+
+
+def layer_backward(inp, dout, tokens=None, experts=None, want_dw=True):
+    """Gradients of sum(dout * out) for the layer on ``inp`` (straight-through
+    quantisation, the router not differentiated).  ``dout``: bf16 bits [T][H].
+
+    Returns dict(dx [T][H] f64, dw [T][k] f64, dWg / dWu [n][I][H] and
+    dWd [n][H][I] f64 for the listed experts (all experts if None; dWg is
+    absent for the gate-less activations)).  With ``tokens`` only those rows
+    of dx / dw are computed (others are zero)."""
+    d = inp.dims
+    T, H, I, E, k = d.T, d.H, d.I, d.E, d.topk
+    act = getattr(d, "act", ACT_SWIGLU)
+    ex = inp.experts
+    keep = []
+
+    def c(a):
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return a.ctypes.data_as(ctypes.c_void_p)
+
+    Wt = OrcWeights()
+    for i, m in enumerate((ex.gate, ex.up, ex.down)):
+        if m is None:
+            continue
+        Wt.fp4[i] = c(m.fp4)
+        Wt.e8m0[i] = c(m.e8m0)
+        Wt.blk[i] = c(m.blk)
+    elist = None if experts is None else np.ascontiguousarray(experts, dtype=np.int32)
+    nE = E if elist is None else len(elist)
+    res = dict(dx=np.zeros((T, H)), dw=np.zeros((T, k)))
+    if want_dw:
+        if act == ACT_SWIGLU:
+            res["dWg"] = np.zeros((nE, I, H))
+        res["dWu"] = np.zeros((nE, I, H))
+        res["dWd"] = np.zeros((nE, H, I))
+    tl = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    tid = None if inp.token_ids is None else np.ascontiguousarray(inp.token_ids, dtype=np.int64)
+    bias = None if inp.bias is None else np.ascontiguousarray(inp.bias, dtype=np.float32)
+    lib().orc_layer_backward(T, H, I, E, k, act, np.ascontiguousarray(inp.x),
+                             np.ascontiguousarray(inp.w_router), _ptr(bias), inp.mode, _ptr(tid),
+                             ctypes.byref(Wt), np.ascontiguousarray(dout, dtype=np.uint16),
+                             _ptr(res["dx"]), _ptr(res["dw"]), _ptr(res.get("dWg")), _ptr(res.get("dWu")),
+                             _ptr(res.get("dWd")), _ptr(tl), 0 if tl is None else len(tl),
+                             _ptr(elist), nE if elist is not None else 0)
     return res

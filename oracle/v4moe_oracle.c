@@ -504,7 +504,8 @@ static float activation(int act, double G, double U)
  * fp64, then either bf16(fp32(Y)) (normal mode) or kept in fp64 (exact mode,
  * y_exact != NULL). */
 static void pair_ffn(int act, int H, int I, const int_matrix* mg, const int_matrix* mu, const int_matrix* md,
-                     const uint8_t* xq, const float* xs, uint16_t* y_bf16, double* y_exact)
+                     const uint8_t* xq, const float* xs, uint16_t* y_bf16, double* y_exact,
+                     double* G_out, double* U_out, uint8_t* hq_out, float* hs_out)
 {
     int32_t* xint = (int32_t*)malloc((size_t)H * sizeof(int32_t));
     double* g = (double*)malloc((size_t)I * sizeof(double));
@@ -521,8 +522,12 @@ static void pair_ffn(int act, int H, int I, const int_matrix* mg, const int_matr
     for (int n = 0; n < I; n++) {
         double G = act == ORC_ACT_SWIGLU ? (double)(float)g[n] : 0.0, U = (double)(float)u[n];
         h[n] = activation(act, G, U);
+        if (G_out) G_out[n] = G;
+        if (U_out) U_out[n] = U;
     }
     orc_quant_rows(1, I, h, hq, hs);
+    if (hq_out) memcpy(hq_out, hq, (size_t)I);
+    if (hs_out) memcpy(hs_out, hs, (size_t)(I / 128) * sizeof(float));
     for (int n = 0; n < I; n++) hint[n] = e4m3_int(hq[n]);
     expert_linear(md, hint, hs, y);
     for (int n = 0; n < H; n++) {
@@ -590,7 +595,7 @@ EXPORT int orc_layer_forward(int T, int H, int I, int E, int k, int act,
             int p = sorted_pair[r], t = p / k;
             if (!want[t]) continue;
             pair_ffn(act, H, I, &mg, &mu, &md, xq + (size_t)t * H, xs + (size_t)t * (H / 128),
-                     ybuf + (size_t)p * H, yex ? yex + (size_t)p * H : NULL);
+                     ybuf + (size_t)p * H, yex ? yex + (size_t)p * H : NULL, NULL, NULL, NULL, NULL);
         }
         free(mg.wint); free(mu.wint); free(md.wint);
     }
@@ -617,5 +622,199 @@ EXPORT int orc_layer_forward(int T, int H, int I, int E, int k, int act,
     free(want);
     free(ybuf);
     free(yex);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the layer                                                     */
+/* (P1 §3 and P4 §3: the MoE backward accumulates in a fixed, token-ordered   */
+/* sequence, no atomics; P1 §4 and P4 §4: gradients are computed with the     */
+/* forward's FP8 weights and passed straight to the FP32 master weights, i.e. */
+/* the straight-through estimator for every quantisation step, and the        */
+/* transposed weights are the same FP8 values, never requantised.)            */
+/* ------------------------------------------------------------------------ */
+
+/* Real value of weight (n, k) of an expert matrix: E4M3 value x block scale. */
+static double wreal(const int_matrix* m, int n, int k)
+{
+    return ldexp((double)m->wint[(size_t)n * m->K + k], -9) *
+           (double)m->blk[(size_t)(n / 128) * (m->K / 128) + k / 128];
+}
+
+/* Derivatives of the activations at (G, U): dh/dG and dh/dU. */
+static void activation_grad(int act, double G, double U, double* dG, double* dU)
+{
+    switch (act) {
+    case ORC_ACT_RELU2: *dG = 0.0; *dU = U > 0.0 ? 2.0 * U : 0.0; return;
+    case ORC_ACT_RELU: *dG = 0.0; *dU = U > 0.0 ? 1.0 : 0.0; return;
+    default: {
+        const double sg = 1.0 / (1.0 + exp(-G));          /* sigmoid */
+        *dG = U * sg * (1.0 + G * (1.0 - sg));            /* d/dG [G sigmoid(G) U] */
+        *dU = G * sg;                                     /* SiLU(G) */
+    }
+    }
+}
+
+/* Gradients of L = sum(dout * out) for the layer forward above, in fp64.
+ * The forward is recomputed exactly as orc_layer_forward does it; then, per
+ * (token, expert) pair p = t*k + j of expert e with routing weight w_p:
+ *   dY_p = w_p * dout_t                        (out = sum_j w_j Y_j)
+ *   dw_p = <dout_t, Y_p>, Y_p the bf16 expert output the combine used
+ *   dh_p = Wd_e^T dY_p                         (real FP8 weight values)
+ *   dG_p, dU_p = dh_p * dh/dG, dh_p * dh/dU at the forward's fp32 G, U
+ *   dx_p = Wg_e^T dG_p + Wu_e^T dU_p,   dx_t = sum over j ascending of dx_{t,j}
+ *   dWd_e = sum_p dY_p hq_p^T,  dWg_e = sum_p dG_p xq_p^T,  dWu_e = sum_p dU_p xq_p^T
+ * where xq_p, hq_p are the forward's quantised activations (E4M3 value x fp32
+ * scale) and the sums over p run over the expert's rows in their sorted
+ * (token) order.  The quantisations are straight-through: their gradient is
+ * the identity, so dx and the dW's are the gradients with respect to x and to
+ * the FP32 master weights.  The router is not differentiated (dw is returned
+ * for it).  For the gate-less activations the gate terms vanish.
+ * Outputs (each may be NULL): dx [T][H], dw [T][k], dWg, dWu [E][I][H],
+ * dWd [E][H][I].  tok / n_tok restrict dx and dw to the listed tokens (their
+ * rows are written; others are left untouched); ex / n_ex restrict the dW's to
+ * the listed experts, whose gradients are then stored in the order of the list
+ * (dWg [n_ex][I][H] ...).  Returns 0. */
+EXPORT int orc_layer_backward(int T, int H, int I, int E, int k, int act,
+                              const uint16_t* x, const float* wr, const float* bias,
+                              int mode, const int64_t* token_ids, const orc_weights* W,
+                              const uint16_t* dout, double* dx, double* dw,
+                              double* dWg, double* dWu, double* dWd,
+                              const int32_t* tok, int n_tok, const int32_t* ex, int n_ex)
+{
+    const int P = T * k;
+    int32_t* ids = (int32_t*)malloc((size_t)(P > 0 ? P : 1) * sizeof(int32_t));
+    float* w = (float*)malloc((size_t)(P > 0 ? P : 1) * sizeof(float));
+    int32_t* offsets = (int32_t*)malloc((size_t)(E + 1) * sizeof(int32_t));
+    int32_t* sorted_pair = (int32_t*)malloc((size_t)(P > 0 ? P : 1) * sizeof(int32_t));
+    int32_t* pair_pos = (int32_t*)malloc((size_t)(P > 0 ? P : 1) * sizeof(int32_t));
+    uint8_t* xq = (uint8_t*)malloc((size_t)(T > 0 ? T : 1) * H);
+    float* xs = (float*)malloc((size_t)(T > 0 ? T : 1) * (H / 128) * sizeof(float));
+    orc_route(T, H, E, k, x, wr, bias, mode, token_ids, ids, w);
+    orc_quant_x(T, H, x, xq, xs);
+    orc_permute(T, k, E, ids, offsets, sorted_pair, pair_pos);
+
+    char* want_t = (char*)calloc((size_t)(T > 0 ? T : 1), 1);
+    char* want_e = (char*)calloc((size_t)E, 1);
+    int* slot_e = (int*)malloc((size_t)E * sizeof(int));        /* output slot of each wanted expert */
+    if (tok) { for (int i = 0; i < n_tok; i++) want_t[tok[i]] = 1; } else memset(want_t, 1, (size_t)T);
+    for (int e = 0; e < E; e++) slot_e[e] = e;
+    if (ex) { for (int i = 0; i < n_ex; i++) { want_e[ex[i]] = 1; slot_e[ex[i]] = i; } }
+    else memset(want_e, 1, (size_t)E);
+    double* dxp = (double*)calloc((size_t)(P > 0 ? P : 1) * H, sizeof(double));   /* dx per pair */
+
+    for (int e = 0; e < E; e++) {
+        const int lo = offsets[e], hi = offsets[e + 1], R = hi - lo;
+        int need_t = 0;
+        for (int r = lo; r < hi; r++) need_t |= want_t[sorted_pair[r] / k];
+        const int need_w = want_e[e] && (dWg || dWu || dWd);
+        if (!need_t && !need_w) continue;
+        int_matrix mg = {0}, mu, md;
+        const size_t so = (size_t)e;
+        if (act == ORC_ACT_SWIGLU)
+            make_int_matrix(&mg, I, H, W->fp4[0] + so * I * (H / 2), W->e8m0[0] + so * I * (H / 32),
+                            W->blk[0] + so * (I / 128) * (H / 128));
+        make_int_matrix(&mu, I, H, W->fp4[1] + so * I * (H / 2), W->e8m0[1] + so * I * (H / 32),
+                        W->blk[1] + so * (I / 128) * (H / 128));
+        make_int_matrix(&md, H, I, W->fp4[2] + so * H * (I / 2), W->e8m0[2] + so * H * (I / 32),
+                        W->blk[2] + so * (H / 128) * (I / 128));
+        /* per row of the expert: dY, dG, dU, and the quantised activations */
+        double* dY = (double*)malloc((size_t)(R > 0 ? R : 1) * H * sizeof(double));
+        double* dGr = (double*)malloc((size_t)(R > 0 ? R : 1) * I * sizeof(double));
+        double* dUr = (double*)malloc((size_t)(R > 0 ? R : 1) * I * sizeof(double));
+        double* hr = (double*)malloc((size_t)(R > 0 ? R : 1) * I * sizeof(double));
+        char* done = (char*)calloc((size_t)(R > 0 ? R : 1), 1);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int r = lo; r < hi; r++) {
+            const int p = sorted_pair[r], t = p / k, rr = r - lo;
+            if (!need_w && !want_t[t]) continue;
+            double* G = (double*)malloc((size_t)I * sizeof(double));
+            double* U = (double*)malloc((size_t)I * sizeof(double));
+            uint8_t* hq = (uint8_t*)malloc((size_t)I);
+            float* hs = (float*)malloc((size_t)(I / 128) * sizeof(float));
+            uint16_t* y = (uint16_t*)malloc((size_t)H * sizeof(uint16_t));
+            double* dh = (double*)malloc((size_t)I * sizeof(double));
+            pair_ffn(act, H, I, &mg, &mu, &md, xq + (size_t)t * H, xs + (size_t)t * (H / 128), y, NULL,
+                     G, U, hq, hs);
+            double* dYr = dY + (size_t)rr * H;
+            double dwp = 0.0;
+            for (int n = 0; n < H; n++) {
+                const double g = (double)orc_bf16_value(dout[(size_t)t * H + n]);
+                dYr[n] = (double)w[p] * g;
+                dwp += g * (double)orc_bf16_value(y[n]);
+            }
+            if (dw && want_t[t]) dw[p] = dwp;
+            for (int i = 0; i < I; i++) {
+                double a = 0.0;
+                for (int n = 0; n < H; n++) a += dYr[n] * wreal(&md, n, i);
+                dh[i] = a;
+            }
+            for (int i = 0; i < I; i++) {
+                double gG, gU;
+                activation_grad(act, G[i], U[i], &gG, &gU);
+                dGr[(size_t)rr * I + i] = dh[i] * gG;
+                dUr[(size_t)rr * I + i] = dh[i] * gU;
+                hr[(size_t)rr * I + i] = orc_e4m3_value(hq[i]) * (double)hs[i / 128];
+            }
+            if (want_t[t]) {
+                double* d = dxp + (size_t)p * H;
+                for (int h = 0; h < H; h++) {
+                    double a = 0.0;
+                    for (int i = 0; i < I; i++) {
+                        if (act == ORC_ACT_SWIGLU) a += dGr[(size_t)rr * I + i] * wreal(&mg, i, h);
+                        a += dUr[(size_t)rr * I + i] * wreal(&mu, i, h);
+                    }
+                    d[h] = a;
+                }
+            }
+            done[rr] = 1;
+            free(G); free(U); free(hq); free(hs); free(y); free(dh);
+        }
+        if (need_w) {
+            /* weight gradients: rows accumulated in sorted order, one output
+             * element per iteration (parallel over outputs, never over rows) */
+            if (dWd) {
+                double* o = dWd + (size_t)slot_e[e] * H * I;
+#pragma omp parallel for schedule(static)
+                for (int n = 0; n < H; n++)
+                    for (int i = 0; i < I; i++) {
+                        double a = 0.0;
+                        for (int rr = 0; rr < R; rr++) a += dY[(size_t)rr * H + n] * hr[(size_t)rr * I + i];
+                        o[(size_t)n * I + i] = a;
+                    }
+            }
+            for (int m = 0; m < 2; m++) {
+                double* o = m == 0 ? dWg : dWu;
+                const double* d = m == 0 ? dGr : dUr;
+                if (!o || (m == 0 && act != ORC_ACT_SWIGLU)) continue;
+                o += (size_t)slot_e[e] * I * H;
+#pragma omp parallel for schedule(static)
+                for (int i = 0; i < I; i++)
+                    for (int h = 0; h < H; h++) {
+                        double a = 0.0;
+                        for (int rr = 0; rr < R; rr++) {
+                            const int t = sorted_pair[lo + rr] / k;
+                            a += d[(size_t)rr * I + i] * orc_e4m3_value(xq[(size_t)t * H + h]) *
+                                 (double)xs[(size_t)t * (H / 128) + h / 128];
+                        }
+                        o[(size_t)i * H + h] = a;
+                    }
+            }
+        }
+        free(dY); free(dGr); free(dUr); free(hr); free(done);
+        free(mg.wint); free(mu.wint); free(md.wint);
+    }
+    if (dx)
+#pragma omp parallel for schedule(static)
+        for (int t = 0; t < T; t++) {
+            if (!want_t[t]) continue;
+            for (int h = 0; h < H; h++) {
+                double a = 0.0;
+                for (int j = 0; j < k; j++) a += dxp[((size_t)t * k + j) * H + h];
+                dx[(size_t)t * H + h] = a;
+            }
+        }
+    free(ids); free(w); free(offsets); free(sorted_pair); free(pair_pos); free(xq); free(xs);
+    free(want_t); free(want_e); free(slot_e); free(dxp);
     return 0;
 }
