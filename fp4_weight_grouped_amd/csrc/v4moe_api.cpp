@@ -146,6 +146,46 @@ FfnArgs ffn_args(const v4moe_dims* d, const Layout& L, uint8_t* ws, const uint8_
     return a;
 }
 
+// Backward workspace: the forward's layout, then the backward's buffers.
+struct BwdLayout {
+    Layout F;
+    size_t ids, w, off, g, u, dys, dgu, dxs, padoff, bmt_expert, bmt_row0, bctrl, bdone1, dyT, dguT, xT, hT;
+    size_t total;
+    int n_mt4, ldd, gI;
+};
+
+BwdLayout bwd_layout(const v4moe_dims* d)
+{
+    BwdLayout B{};
+    B.F = layout(d);
+    size_t o = B.F.total;
+    auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
+    const size_t T = d->T, H = d->H, I = d->I, E = d->E, P = (size_t)d->T * d->topk;
+    B.gI = d->act == V4MOE_ACT_SWIGLU ? 2 * d->I : d->I;
+    B.n_mt4 = (int)(P / 64 + (P < E ? P : E) + 1);
+    B.ldd = (int)((P + 32 * E + 63) / 64 * 64);
+    B.ids = take(P * 4);
+    B.w = take(P * 4);
+    B.off = take((E + 1) * 4);
+    B.g = take(d->act == V4MOE_ACT_SWIGLU ? P * I * 4 : 0);
+    B.u = take(P * I * 4);
+    B.dys = take(P * H * 2);
+    B.dgu = take(P * B.gI * 2);
+    B.dxs = take(P * H * 4);
+    B.padoff = take((E + 1) * 4);
+    B.bmt_expert = take((size_t)B.n_mt4 * 4);
+    B.bmt_row0 = take((size_t)B.n_mt4 * 4);
+    B.bctrl = take(16 * 4);
+    B.bdone1 = take((size_t)B.n_mt4 * 4);
+    B.dyT = take(H * B.ldd * 2);
+    B.dguT = take((size_t)B.gI * B.ldd * 2);
+    B.xT = take(H * B.ldd * 2);
+    B.hT = take(I * B.ldd * 2);
+    (void)T;
+    B.total = o;
+    return B;
+}
+
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
 int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws, bool persistent,
@@ -416,6 +456,157 @@ __attribute__((visibility("default"))) int moe_dequant_fp8(const v4moe_mat* m, i
     if (launch_dequant_export(N, K, expert, static_cast<const uint8_t*>(m->fp4),
                               static_cast<const uint8_t*>(m->e8m0), out, as_stream(stream)) != hipSuccess)
         return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+__attribute__((visibility("default"))) size_t moe_backward_workspace_bytes(const v4moe_dims* d)
+{
+    if (!dims_ok(d)) return 0;
+    return bwd_layout(d).total;
+}
+
+__attribute__((visibility("default"))) int moe_transpose_weights(const v4moe_dims* d, const v4moe_experts* w,
+                                                                 uint16_t* wt_gu, uint16_t* wt_d, void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (!w || !wt_gu || !wt_d) return V4MOE_ENULL;
+    if ((gated(d) && !mat_ok(w->gate)) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
+    if (!aligned16(wt_gu) || !aligned16(wt_d)) return V4MOE_EALIGN;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    hipStream_t s = as_stream(stream);
+    const int E = d->E, H = d->H, I = d->I, gI = gated(d) ? 2 * I : I;
+    auto fp = [](const v4moe_mat& m) { return static_cast<const uint8_t*>(m.fp4); };
+    auto ep = [](const v4moe_mat& m) { return static_cast<const uint8_t*>(m.e8m0); };
+    if (gated(d) && launch_weights_t(E, I, H, fp(w->gate), ep(w->gate), wt_gu, gI, 0, (size_t)H * gI, s) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    if (launch_weights_t(E, I, H, fp(w->up), ep(w->up), wt_gu, gI, gated(d) ? I : 0, (size_t)H * gI, s) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    if (launch_weights_t(E, H, I, fp(w->down), ep(w->down), wt_d, H, 0, (size_t)I * H, s) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+__attribute__((visibility("default"))) int moe_layer_backward(
+    const v4moe_dims* d, const uint16_t* x, const float* w_router, const float* bias, int32_t mode,
+    const int64_t* token_ids, const v4moe_experts* w, const uint16_t* wt_gu, const uint16_t* wt_d,
+    const uint16_t* dout, float* dx, float* dw, float* dWg, float* dWu, float* dWd, void* workspace,
+    size_t ws_bytes, void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (mode != V4MOE_ROUTE_LEARNED && mode != V4MOE_ROUTE_HASH) return V4MOE_EDIMS;
+    if (!w || !wt_gu || !wt_d || !dWu || !dWd || !workspace || (gated(d) && !dWg)) return V4MOE_ENULL;
+    if ((gated(d) && !mat_ok(w->gate)) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
+    if (d->T > 0 && (!x || !dout || !dx || !dw || (mode == V4MOE_ROUTE_LEARNED && !w_router))) return V4MOE_ENULL;
+    for (const void* p : {(const void*)x, (const void*)dout, (const void*)dx, (const void*)wt_gu, (const void*)wt_d,
+                          (const void*)dWu, (const void*)dWd, (const void*)dWg, (const void*)workspace})
+        if (p && !aligned16(p)) return V4MOE_EALIGN;
+    if (mode == V4MOE_ROUTE_LEARNED && d->T > 0 && !aligned16(w_router)) return V4MOE_EALIGN;
+    const BwdLayout B = bwd_layout(d);
+    if (ws_bytes < B.total) return V4MOE_EWORKSPACE;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    hipStream_t s = as_stream(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const Layout& L = B.F;
+    const int T = d->T, H = d->H, I = d->I, E = d->E, k = d->topk, gI = B.gI;
+    auto at = [&](size_t off) { return ws + off; };
+    int32_t* ids = reinterpret_cast<int32_t*>(at(B.ids));
+    float* wts = reinterpret_cast<float*>(at(B.w));
+    int32_t* offsets = reinterpret_cast<int32_t*>(at(B.off));
+    uint8_t* xq = at(L.xq);
+    float* xs = reinterpret_cast<float*>(at(L.xs));
+    int32_t* sp = reinterpret_cast<int32_t*>(at(L.sorted_pair));
+    int32_t* pp = reinterpret_cast<int32_t*>(at(L.pair_pos));
+    int32_t* padoff = reinterpret_cast<int32_t*>(at(B.padoff));
+    if (T > 0) {
+        // the forward again, keeping what the backward needs (G, U; hq, hs; Y)
+        if (launch_route(T, H, E, k, x, w_router, bias, mode, token_ids, ids, wts,
+                         reinterpret_cast<float*>(at(L.z)), s) != hipSuccess)
+            return V4MOE_ELAUNCH;
+        if (launch_quant_x(T, H, x, xq, xs, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_permute(T, k, E, ids, offsets, sp, pp, reinterpret_cast<int32_t*>(at(L.hist)), s) != hipSuccess)
+            return V4MOE_ELAUNCH;
+        uint16_t* y = reinterpret_cast<uint16_t*>(at(L.y));
+        FfnArgs a = ffn_args(d, L, ws, xq, xs, offsets, sp, w, y);
+        a.g_out = gated(d) ? reinterpret_cast<float*>(at(B.g)) : nullptr;
+        a.u_out = reinterpret_cast<float*>(at(B.u));
+        int rc = run_ffn(d, L, a, ws, false, di, s);
+        if (rc) return rc;
+        uint16_t* dys = reinterpret_cast<uint16_t*>(at(B.dys));
+        if (launch_bwd_combine(T, H, k, dout, wts, y, pp, dys, dw, s) != hipSuccess) return V4MOE_ELAUNCH;
+        // 64-row m-tiles of the experts' row segments
+        FfnArgs b = a;
+        b.ctrl = reinterpret_cast<int32_t*>(at(B.bctrl));
+        b.done1 = reinterpret_cast<int32_t*>(at(B.bdone1));
+        int32_t* bmte = reinterpret_cast<int32_t*>(at(B.bmt_expert));
+        int32_t* bmtr = reinterpret_cast<int32_t*>(at(B.bmt_row0));
+        if (launch_build_tiles(E, 4, 1, 1, 0, 1, b, bmte, bmtr, nullptr, s) != hipSuccess) return V4MOE_ELAUNCH;
+        BgemmArgs g{};
+        g.I = I; g.H = H; g.act = d->act;
+        g.mt_expert = bmte; g.mt_row0 = bmtr; g.ctrl = b.ctrl; g.offsets = offsets;
+        g.g = a.g_out; g.u = a.u_out;
+        uint16_t* dgu = reinterpret_cast<uint16_t*>(at(B.dgu));
+        g.dgu = dgu;
+        float* dxs = reinterpret_cast<float*>(at(B.dxs));
+        g.dxs = dxs;
+        // dh = Wd^T dY, activation derivative -> dG, dU
+        g.N = I; g.K = H; g.A = dys; g.lda = H; g.B = wt_d; g.ldb = H; g.b_expert = (size_t)I * H;
+        g.blk0 = w->down.blk;
+        if (launch_bgemm(BG_DGRAD2, g, B.n_mt4, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        // dx per row = [Wg Wu]^T [dG dU]
+        g.N = H; g.K = gI; g.A = dgu; g.lda = gI; g.B = wt_gu; g.ldb = gI; g.b_expert = (size_t)H * gI;
+        g.blk0 = gated(d) ? w->gate.blk : w->up.blk;
+        g.blk1 = w->up.blk;
+        if (launch_bgemm(BG_DGRAD1, g, B.n_mt4, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bwd_unpermute(T, H, k, pp, dxs, dx, s) != hipSuccess) return V4MOE_ELAUNCH;
+        // transposed operands of the weight gradients
+        if (launch_pad_offsets(E, offsets, padoff, s) != hipSuccess) return V4MOE_ELAUNCH;
+        const int P = T * k, maxc = P + 32 * E;
+        uint16_t* dyT = reinterpret_cast<uint16_t*>(at(B.dyT));
+        uint16_t* dguT = reinterpret_cast<uint16_t*>(at(B.dguT));
+        uint16_t* xT = reinterpret_cast<uint16_t*>(at(B.xT));
+        uint16_t* hT = reinterpret_cast<uint16_t*>(at(B.hT));
+        if (launch_bwd_transpose(0, H, E, k, maxc, offsets, padoff, sp, dys, nullptr, nullptr, 0, dyT, B.ldd, s) !=
+                hipSuccess ||
+            launch_bwd_transpose(0, gI, E, k, maxc, offsets, padoff, sp, dgu, nullptr, nullptr, 0, dguT, B.ldd, s) !=
+                hipSuccess ||
+            launch_bwd_transpose(1, H, E, k, maxc, offsets, padoff, sp, nullptr, xq, xs, H / 128, xT, B.ldd, s) !=
+                hipSuccess ||
+            launch_bwd_transpose(2, I, E, k, maxc, offsets, padoff, sp, nullptr, at(L.hq),
+                                 reinterpret_cast<const float*>(at(L.hs)), hs_stride(I), hT, B.ldd, s) != hipSuccess)
+            return V4MOE_ELAUNCH;
+        BgemmArgs wg{};
+        wg.offsets = offsets; wg.padoff = padoff;
+        wg.lda = wg.ldb = B.ldd;
+        wg.M = H; wg.N = I; wg.A = dyT; wg.B = hT; wg.dW = dWd;
+        if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        wg.M = I; wg.N = H; wg.B = xT;
+        if (gated(d)) {
+            wg.A = dguT; wg.dW = dWg;
+            if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        }
+        wg.A = dguT + (gated(d) ? (size_t)I * B.ldd : 0); wg.dW = dWu;
+        if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+    } else {
+        // no tokens: every weight gradient is zero
+        if (launch_fill_i32(offsets, 0, E + 1, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_pad_offsets(E, offsets, padoff, s) != hipSuccess) return V4MOE_ELAUNCH;
+        uint16_t* dyT = reinterpret_cast<uint16_t*>(at(B.dyT));
+        BgemmArgs wg{};
+        wg.offsets = offsets; wg.padoff = padoff;
+        wg.lda = wg.ldb = B.ldd;
+        wg.A = dyT; wg.B = dyT;
+        wg.M = H; wg.N = I; wg.dW = dWd;
+        if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        wg.M = I; wg.N = H;
+        if (gated(d)) {
+            wg.dW = dWg;
+            if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        }
+        wg.dW = dWu;
+        if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+    }
     return V4MOE_OK;
 }
 

@@ -1,0 +1,453 @@
+// libv4moe -- backward of the MoE layer on gfx950.
+//
+// Sources (the pages; cited by short tag and section):
+//   P1 = "DeepSeek-V4揭秘：细粒度专家并行隐藏通信时延，FP4量化与TileLang协同优化百万Token上下文"
+//   P4 = "DeepSeek-V4 的暗线之二：训练一台不会失控的万亿参数机器"
+// P1 §3 / P4 §3: the MoE backward must accumulate in a fixed order (the pages
+// order tokens before accumulation and isolate buffers instead of racing on
+// atomics).  P1 §4 / P4 §4: gradients are computed with the forward's FP8
+// weights and passed straight to the FP32 master weights (straight-through
+// quantisation), and since FP4 -> FP8 is lossless the transposed weights are
+// the same FP8 values, never requantised.
+//
+// With L = sum(dout * out), per (token t, expert e) pair p = t*k + j of weight
+// w_p, in expert-sorted row order r:
+//   dY_r  = w_p dout_t                          (k_bwd_combine; also dw_p = <dout_t, Y_p>)
+//   dh_r  = Wd_e^T dY_r, then dG_r, dU_r        (k_bgemm<DGRAD2>, activation derivative fused)
+//   dx_r  = [Wg_e; Wu_e]^T [dG_r; dU_r]         (k_bgemm<DGRAD1>)
+//   dx_t  = sum_j dx_{t,j}, j ascending         (k_bwd_unpermute)
+//   dW_e  = sum_r (row gradient) (forward activation)^T over the expert's rows
+//           in sorted order                     (k_bwd_transpose + k_bgemm<WGRAD>)
+// Every matrix product runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16)
+// with fp32 accumulation: FP8 weight values, FP8 activation codes and E4M3
+// values are exact in bf16; the incoming gradients are rounded to bf16, and
+// so are the activations of the weight gradients (E4M3 code times its fp32
+// scale).  The weights' 128x128 block scales multiply each 128-wide K chunk's
+// partial sum (as in the forward).  No atomics: every output element is
+// written once by one thread, in a fixed reduction order.
+#include "v4moe_device.h"
+#include "v4moe_internal.h"
+
+#include <hip/hip_runtime.h>
+
+namespace v4moe {
+
+namespace {
+
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t bf16_bits(float f)
+{
+    return (uint16_t)bf16x2(f, 0.0f);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b)
+{
+    // E4M3FN: bias 7, subnormals at exponent field 0; never NaN here
+    const uint32_t s = (b & 0x80u) << 24, e = (b >> 3) & 15u, m = b & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Combine backward: dY in sorted row order (bf16) and the routing-weight
+// gradients.  One block per pair; the dot product is reduced in a fixed tree.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_combine(int H, int k, const uint16_t* __restrict__ dout,
+                                                     const float* __restrict__ w, const uint16_t* __restrict__ y,
+                                                     const int32_t* __restrict__ pair_pos,
+                                                     uint16_t* __restrict__ dys, float* __restrict__ dw)
+{
+    __shared__ float red[256];
+    const int p = blockIdx.x, t = p / k, tid = threadIdx.x;
+    const float wp = w[p];
+    const size_t row = (size_t)pair_pos[p];
+    float acc = 0.0f;
+    for (int n = tid * 8; n < H; n += 2048) {
+        const uint4 g = *reinterpret_cast<const uint4*>(dout + (size_t)t * H + n);
+        const uint4 yy = *reinterpret_cast<const uint4*>(y + (size_t)p * H + n);
+        const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, yw[4] = {yy.x, yy.y, yy.z, yy.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const float g0 = __uint_as_float(gw[q] << 16), g1 = __uint_as_float(gw[q] & 0xFFFF0000u);
+            const float y0 = __uint_as_float(yw[q] << 16), y1 = __uint_as_float(yw[q] & 0xFFFF0000u);
+            acc = __builtin_fmaf(g0, y0, acc);
+            acc = __builtin_fmaf(g1, y1, acc);
+            o[q] = bf16x2(wp * g0, wp * g1);
+        }
+        *reinterpret_cast<uint4*>(dys + row * H + n) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    red[tid] = acc;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    if (tid == 0) dw[p] = red[0];
+}
+
+// ---------------------------------------------------------------------------
+// Transposed FP8 weight values in bf16: packed matrix (N rows, K inputs) ->
+// out[e][kk][nofs + n] = e2m1(code) * 2^b for kk < K, n < N, row pitch ldo
+// (so gate and up can share one [H][2I] buffer).  One block per (expert,
+// 64-row quad, 128-wide chunk); the quad is transposed through LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_weights_t(int N, int K, const uint8_t* __restrict__ fp4,
+                                                   const uint8_t* __restrict__ e8, uint16_t* __restrict__ out,
+                                                   int ldo, int nofs, size_t out_expert_stride)
+{
+    __shared__ uint16_t tr[128][64 + 8];
+    const int C = K / 128;
+    const int c = blockIdx.x % C;
+    const int qd = (blockIdx.x / C) % (N / 64);
+    const size_t e = blockIdx.x / ((size_t)C * (N / 64));
+    const int tid = threadIdx.x, tq = tid >> 6, sl = tid & 63;
+    const int tile = qd * 4 + tq;
+    const uint4 codes = *reinterpret_cast<const uint4*>(fp4 + (((e * (N / 16) + tile) * C + c) * 64 + sl) * 16);
+    const int b = (int)e8[((e * (N / 64) + qd) * C + c) * 256 + sl * 4 + tq] - 127;
+    const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
+    const int nl = tq * 16 + (sl & 15), kl = (sl >> 4) * 32;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+        const uint32_t code = (cw[i >> 3] >> (4 * (i & 7))) & 15u;
+        const uint32_t e2 = (code >> 1) & 3u, m = code & 1u;
+        // e2m1 magnitude as fp32 bits, times 2^b (exact), to bf16 bits (exact)
+        const float mag = e2 ? __uint_as_float(((e2 + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
+        const float v = ldexpf(mag, b);
+        tr[kl + i][nl] = (uint16_t)((__float_as_uint(v) >> 16) | ((code & 8u) << 12));
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 128 * 8; idx += 256) {
+        const int kk = idx >> 3, seg = idx & 7;
+        *reinterpret_cast<uint4*>(out + e * out_expert_stride + (size_t)(c * 128 + kk) * ldo + nofs + qd * 64 +
+                                  seg * 8) = *reinterpret_cast<const uint4*>(&tr[kk][seg * 8]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Padded column offsets of the experts' row segments (multiples of 32) for the
+// transposed activation buffers; one block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_pad_offsets(int E, const int32_t* __restrict__ off,
+                                                      int32_t* __restrict__ padoff)
+{
+    __shared__ int s[1024];
+    const int tid = threadIdx.x;
+    const int cnt = tid < E ? off[tid + 1] - off[tid] : 0;
+    s[tid] = (cnt + 31) & ~31;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int v = tid >= d ? s[tid - d] : 0;
+        __syncthreads();
+        s[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) padoff[tid + 1] = s[tid];
+    if (tid == 0) padoff[0] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Transpose of sorted-row activations into [channel][padded column] bf16,
+// zeros in each expert's padding.  MODE 0: bf16 rows src[r][C] (row pitch
+// C); MODE 1: the forward's x payload, E4M3 code x scale of token
+// sorted_pair[r]/k; MODE 2: the forward's h payload, hq[r] x hs[r].
+// One block per (64 padded columns, 64 channels).
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(256) void k_bwd_transpose(int C, int E, int k, const int32_t* __restrict__ off,
+                                                       const int32_t* __restrict__ padoff,
+                                                       const int32_t* __restrict__ sorted_pair,
+                                                       const uint16_t* __restrict__ src16,
+                                                       const uint8_t* __restrict__ q8, const float* __restrict__ qs,
+                                                       int qs_stride, uint16_t* __restrict__ dst, int ldd)
+{
+    __shared__ uint16_t tile[64][64 + 2];
+    const int pc0 = blockIdx.x * 64, ch0 = blockIdx.y * 64;
+    const int total = padoff[E];
+    if (pc0 >= total) return;
+    const int tid = threadIdx.x;
+    // each thread loads 16 channels of one padded column
+    {
+        const int col = tid >> 2, cseg = (tid & 3) * 16;
+        const int pc = pc0 + col;
+        int lo = 0, hi = E;                       // expert of pc: padoff[e] <= pc < padoff[e+1]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (padoff[mid] <= pc) lo = mid; else hi = mid;
+        }
+        const int e = lo;
+        const int r = off[e] + (pc - padoff[e]);
+        const bool valid = pc < total && r < off[e + 1];
+        uint16_t v[16];
+        if (!valid) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = 0;
+        } else if (MODE == 0) {
+            const uint4 a = *reinterpret_cast<const uint4*>(src16 + (size_t)r * C + ch0 + cseg);
+            const uint4 b = *reinterpret_cast<const uint4*>(src16 + (size_t)r * C + ch0 + cseg + 8);
+            const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 8; i++) { v[2 * i] = (uint16_t)wv[i]; v[2 * i + 1] = (uint16_t)(wv[i] >> 16); }
+        } else {
+            const size_t qrow = MODE == 1 ? (size_t)(sorted_pair[r] / k) : (size_t)r;
+            const uint4 a = *reinterpret_cast<const uint4*>(q8 + qrow * C + ch0 + cseg);
+            const float sc = qs[qrow * qs_stride + (ch0 + cseg) / 128];
+            const uint32_t wv[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = bf16_bits(e4m3_to_f32((wv[i >> 2] >> (8 * (i & 3))) & 255u) * sc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i++) tile[cseg + i][col] = v[i];
+    }
+    __syncthreads();
+    // write 64 channel rows of 64 columns (128 bytes), 16 bytes per thread
+    for (int idx = tid; idx < 64 * 8; idx += 256) {
+        const int ch = idx >> 3, seg = idx & 7;
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            o[i] = (uint32_t)tile[ch][seg * 8 + 2 * i] | ((uint32_t)tile[ch][seg * 8 + 2 * i + 1] << 16);
+        *reinterpret_cast<uint4*>(dst + (size_t)(ch0 + ch) * ldd + pc0 + seg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dx_t = sum_j dx_{t,j} in j order (fp32).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_unpermute(int T, int H, int k, const int32_t* __restrict__ pair_pos,
+                                                       const float* __restrict__ dxs, float* __restrict__ dx)
+{
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;       // float4 index
+    if (idx >= (size_t)T * H / 4) return;
+    const size_t t = idx / (H / 4), c = (idx % (H / 4)) * 4;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; j++) {
+        const float4 v = *reinterpret_cast<const float4*>(dxs + (size_t)pair_pos[t * k + j] * H + c);
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    *reinterpret_cast<float4*>(dx + t * H + c) = a;
+}
+
+// ---------------------------------------------------------------------------
+// Grouped bf16 NT GEMM: C[m][n] = sum over 128-wide K chunks c of
+// s(c) * sum_{kk in c} A[m][kk] * B[n][kk], fp32.  Block tile 64 (m) x 128
+// (n), four waves of 64 x 32; LDS rows padded to 272 bytes.
+//   DGRAD2: m = rows of an m-tile of one expert (tile list), A = dY (sorted
+//     rows, K = H), B = Wd^T of the expert ([I][H]), s = down block scale;
+//     epilogue: the activation derivative at the forward's G, U -> dG, dU
+//     (bf16, [rows][2I] or [rows][I] gate-less).
+//   DGRAD1: A = [dG dU] (K = 2I, or I), B = [Wg Wu]^T ([H][2I]), s = gate or
+//     up block scale; epilogue: dx per sorted row (fp32).
+//   WGRAD: blockIdx.z = expert; m over the weight rows, n over its inputs,
+//     K = the expert's padded row segment of the transposed buffers, s = 1;
+//     epilogue: dW[e] (fp32, master layout).
+// ---------------------------------------------------------------------------
+enum { DGRAD2 = BG_DGRAD2, DGRAD1 = BG_DGRAD1, WGRAD = BG_WGRAD };
+
+constexpr int kBgPitch = 136;   // bf16 elements per LDS row (128 + 8)
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
+{
+    __shared__ __align__(16) uint16_t As[64 * kBgPitch];
+    __shared__ __align__(16) uint16_t Bs[128 * kBgPitch];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int e, row0, rows, kbeg, kend;
+    const int nb = blockIdx.x % NB;
+    const int n0 = nb * 128;
+    int m0 = 0;
+    if (MODE == WGRAD) {
+        e = blockIdx.z;
+        m0 = (blockIdx.x / NB) * 64;
+        row0 = 0;
+        rows = 64;
+        kbeg = a.padoff[e];
+        kend = kbeg + ((a.offsets[e + 1] - a.offsets[e] + 31) & ~31);
+    } else {
+        const int mt = blockIdx.x / NB;
+        if (mt >= a.ctrl[0]) return;
+        e = a.mt_expert[mt];
+        row0 = a.mt_row0[mt];
+        rows = min(64, a.offsets[e + 1] - row0);
+        kbeg = 0;
+        kend = a.K;
+    }
+    const uint16_t* Bb = a.B + (size_t)e * a.b_expert;
+    v4f acc[4][2], part[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = kbeg; k0 < kend; k0 += 128) {
+        const int kn = min(128, kend - k0);          // multiple of 32
+        __syncthreads();
+        // A: 64 rows x 128, B: 128 rows x 128 (16 bytes per load; rows past
+        // the end of a DGRAD m-tile repeat its last row, never stored)
+        for (int idx = tid; idx < 64 * 16; idx += 256) {
+            const int r = idx >> 4, sg = idx & 15;
+            const int ar = MODE == WGRAD ? m0 + r : row0 + min(r, rows - 1);
+            *reinterpret_cast<uint4*>(&As[r * kBgPitch + sg * 8]) =
+                sg * 8 < kn ? *reinterpret_cast<const uint4*>(a.A + (size_t)ar * a.lda + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
+        }
+        for (int idx = tid; idx < 128 * 16; idx += 256) {
+            const int r = idx >> 4, sg = idx & 15;
+            *reinterpret_cast<uint4*>(&Bs[r * kBgPitch + sg * 8]) =
+                sg * 8 < kn ? *reinterpret_cast<const uint4*>(Bb + (size_t)(n0 + r) * a.ldb + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < kn; ks += 32) {
+            bf8 bfr[2];
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                bfr[j] = *reinterpret_cast<const bf8*>(&Bs[(w * 32 + j * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const bf8 afr = *reinterpret_cast<const bf8*>(&As[(i * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], part[i][j], 0, 0, 0);
+            }
+        }
+        float s = 1.0f;
+        if (MODE == DGRAD2) s = a.blk0[((size_t)e * (a.H / 128) + k0 / 128) * (a.I / 128) + n0 / 128];
+        if (MODE == DGRAD1) {
+            const int c = k0 / 128, ci = a.I / 128;
+            s = c < ci ? a.blk0[((size_t)e * ci + c) * (a.H / 128) + n0 / 128]
+                       : a.blk1[((size_t)e * ci + (c - ci)) * (a.H / 128) + n0 / 128];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, part[i][j][q], acc[i][j][q]);
+    }
+    // stage the 64 x 128 fp32 tile through LDS (As/Bs reused)
+    __syncthreads();
+    float* cs = reinterpret_cast<float*>(Bs);                 // [64][132]
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                cs[(i * 16 + 4 * (lane >> 4) + q) * 132 + w * 32 + j * 16 + (lane & 15)] = acc[i][j][q];
+    __syncthreads();
+    for (int idx = tid; idx < 64 * 32; idx += 256) {
+        const int r = idx >> 5, c4 = (idx & 31) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(&cs[r * 132 + c4]);
+        if (MODE == WGRAD) {
+            *reinterpret_cast<float4*>(a.dW + ((size_t)e * a.M + m0 + r) * a.N + n0 + c4) = v;
+        } else if (r < rows) {
+            const size_t row = (size_t)row0 + r;
+            if (MODE == DGRAD1) {
+                *reinterpret_cast<float4*>(a.dxs + row * a.H + n0 + c4) = v;
+            } else {
+                const float dh[4] = {v.x, v.y, v.z, v.w};
+                const float4 U = *reinterpret_cast<const float4*>(a.u + row * a.I + n0 + c4);
+                const float uu[4] = {U.x, U.y, U.z, U.w};
+                float dg[4], du[4];
+                if (a.act == 0) {
+                    const float4 G = *reinterpret_cast<const float4*>(a.g + row * a.I + n0 + c4);
+                    const float gg[4] = {G.x, G.y, G.z, G.w};
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const float sg = 1.0f / (1.0f + expf(-gg[q]));
+                        dg[q] = dh[q] * uu[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+                        du[q] = dh[q] * gg[q] * sg;
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        dg[q] = 0.0f;
+                        du[q] = uu[q] > 0.0f ? (a.act == 1 ? 2.0f * uu[q] * dh[q] : dh[q]) : 0.0f;
+                    }
+                }
+                const int ld = a.act == 0 ? 2 * a.I : a.I;
+                uint16_t* d = a.dgu + row * ld + n0 + c4;
+                if (a.act == 0) {
+                    *reinterpret_cast<uint2*>(d) = make_uint2(bf16x2(dg[0], dg[1]), bf16x2(dg[2], dg[3]));
+                    d += a.I;
+                }
+                *reinterpret_cast<uint2*>(d) = make_uint2(bf16x2(du[0], du[1]), bf16x2(du[2], du[3]));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_bwd_combine(int T, int H, int k, const uint16_t* dout, const float* w, const uint16_t* y,
+                              const int32_t* pair_pos, uint16_t* dys, float* dw, hipStream_t s)
+{
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)(T * k)), dim3(256), 0, s, H, k, dout, w, y, pair_pos, dys, dw);
+    return hipGetLastError();
+}
+
+hipError_t launch_weights_t(int E, int N, int K, const uint8_t* fp4, const uint8_t* e8, uint16_t* out, int ldo,
+                            int nofs, size_t out_expert_stride, hipStream_t s)
+{
+    const size_t blocks = (size_t)E * (N / 64) * (K / 128);
+    hipLaunchKernelGGL(k_weights_t, dim3((unsigned)blocks), dim3(256), 0, s, N, K, fp4, e8, out, ldo, nofs,
+                       out_expert_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(int E, const int32_t* off, int32_t* padoff, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, s, E, off, padoff);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_transpose(int mode, int C, int E, int k, int max_cols, const int32_t* off,
+                                const int32_t* padoff, const int32_t* sorted_pair, const uint16_t* src16,
+                                const uint8_t* q8, const float* qs, int qs_stride, uint16_t* dst, int ldd,
+                                hipStream_t s)
+{
+    const dim3 grid((unsigned)((max_cols + 63) / 64), (unsigned)(C / 64));
+    if (mode == 0)
+        hipLaunchKernelGGL(k_bwd_transpose<0>, grid, dim3(256), 0, s, C, E, k, off, padoff, sorted_pair, src16, q8,
+                           qs, qs_stride, dst, ldd);
+    else if (mode == 1)
+        hipLaunchKernelGGL(k_bwd_transpose<1>, grid, dim3(256), 0, s, C, E, k, off, padoff, sorted_pair, src16, q8,
+                           qs, qs_stride, dst, ldd);
+    else
+        hipLaunchKernelGGL(k_bwd_transpose<2>, grid, dim3(256), 0, s, C, E, k, off, padoff, sorted_pair, src16, q8,
+                           qs, qs_stride, dst, ldd);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_unpermute(int T, int H, int k, const int32_t* pair_pos, const float* dxs, float* dx,
+                                hipStream_t s)
+{
+    const size_t n = (size_t)T * H / 4;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_bwd_unpermute, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, H, k, pair_pos, dxs, dx);
+    return hipGetLastError();
+}
+
+hipError_t launch_bgemm(int mode, const BgemmArgs& a, int n_mt_bound, int E, hipStream_t s)
+{
+    const int NB = a.N / 128;
+    if (mode == WGRAD) {
+        if (E == 0) return hipSuccess;
+        hipLaunchKernelGGL(k_bgemm<WGRAD>, dim3((unsigned)((a.M / 64) * NB), 1, (unsigned)E), dim3(256), 0, s, a, NB);
+    } else {
+        const dim3 grid((unsigned)(n_mt_bound * NB));
+        if (mode == DGRAD2) hipLaunchKernelGGL(k_bgemm<DGRAD2>, grid, dim3(256), 0, s, a, NB);
+        else hipLaunchKernelGGL(k_bgemm<DGRAD1>, grid, dim3(256), 0, s, a, NB);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace v4moe

@@ -38,6 +38,8 @@ struct FfnArgs {
     int32_t* ctrl;             // [0] number of m-tiles, [1] queue head, [2] queue length
     int32_t* done1;            // [n_mt_bound] finished linear1 tiles per m-tile
     const uint32_t* queue;     // persistent schedule
+    float* g_out;              // optional [T*topk][I]: linear1 gate outputs (fp32, sorted rows), or null
+    float* u_out;              // optional [T*topk][I]: linear1 up outputs, or null
 };
 
 hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
@@ -67,6 +69,35 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 
 // Rows per m-tile (16 * MT) used for given dimensions.
 int choose_mt(int T, int k, int E);
+
+// ---- backward (v4moe_bwd.hip) ----
+enum { BG_DGRAD2 = 0, BG_DGRAD1 = 1, BG_WGRAD = 2 };
+// Arguments of the grouped bf16 GEMM k_bgemm (C = sum over 128-wide K chunks
+// of scale * A B^T, both operands K-contiguous).
+struct BgemmArgs {
+    int M, N, K;                 // WGRAD: rows, cols of dW; DGRAD: N outputs, K contraction
+    int I, H, act;
+    const uint16_t* A; int lda;
+    const uint16_t* B; int ldb; size_t b_expert;   // B element (e, n, k) at B + e*b_expert + n*ldb + k
+    const float* blk0; const float* blk1;           // block scales (DGRAD2: down; DGRAD1: gate, up)
+    const int32_t* mt_expert; const int32_t* mt_row0; const int32_t* ctrl; const int32_t* offsets;
+    const int32_t* padoff;
+    const float* g; const float* u;                 // forward's linear1 outputs (sorted rows, [P][I])
+    uint16_t* dgu; float* dxs; float* dW;
+};
+hipError_t launch_bwd_combine(int T, int H, int k, const uint16_t* dout, const float* w, const uint16_t* y,
+                              const int32_t* pair_pos, uint16_t* dys, float* dw, hipStream_t s);
+hipError_t launch_weights_t(int E, int N, int K, const uint8_t* fp4, const uint8_t* e8, uint16_t* out, int ldo,
+                            int nofs, size_t out_expert_stride, hipStream_t s);
+hipError_t launch_pad_offsets(int E, const int32_t* off, int32_t* padoff, hipStream_t s);
+hipError_t launch_bwd_transpose(int mode, int C, int E, int k, int max_cols, const int32_t* off,
+                                const int32_t* padoff, const int32_t* sorted_pair, const uint16_t* src16,
+                                const uint8_t* q8, const float* qs, int qs_stride, uint16_t* dst, int ldd,
+                                hipStream_t s);
+hipError_t launch_bwd_unpermute(int T, int H, int k, const int32_t* pair_pos, const float* dxs, float* dx,
+                                hipStream_t s);
+// DGRAD modes: grid over n_mt_bound m-tiles of 64 rows x N/128; WGRAD: E x (M/64) x (N/128).
+hipError_t launch_bgemm(int mode, const BgemmArgs& a, int n_mt_bound, int E, hipStream_t s);
 // Wave columns per tile: a tile covers 64*CW columns of h in linear1 (128*CW
 // gate-less) and 128*CW output columns in linear2.
 int choose_cw(int MT, int H, int I, bool gated);

@@ -720,6 +720,28 @@ __device__ __forceinline__ float gateless_act(int act, float u)
     return act == 1 ? r * r : r;
 }
 
+// Optional export of the linear1 outputs before the activation (fp32, sorted
+// rows; the backward recomputes them this way): lane l of a wave holds, for
+// the token l%16 of each token tile i, four consecutive columns
+// col0 + 16j + 4(l/16) .. +3 in acc[i][j0 + j], j < NJ.
+template <int MTW>
+__device__ __forceinline__ void store_linear1(float* out, const FfnArgs& a, int row0, int rows, int rbase, int col0,
+                                              const v4f (&acc)[MTW][8], int j0, int nj = 8)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < MTW; i++) {
+        const int r = rbase + i * 16 + (lane & 15);
+        if (r >= rows) continue;
+        float* dst = out + (size_t)(row0 + r) * a.I + col0 + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if (j < nj)
+                *reinterpret_cast<float4*>(dst + 16 * j) =
+                    make_float4(acc[i][j0 + j][0], acc[i][j0 + j][1], acc[i][j0 + j][2], acc[i][j0 + j][3]);
+    }
+}
+
 // G: the expert FFN is SwiGLU (gate and up projections); otherwise gate-less
 // (a.act selects the activation).  Phase 2 does not depend on G.
 template <int PHASE, int MT, int RW, int CW, bool G>
@@ -902,6 +924,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         uint8_t* stage = smem;                                      // [M][SP1]
         const int g = lane >> 4;
         const int act = a.act;
+        if (a.u_out) store_linear1(a.u_out, a, row0, rows, rg * RG, nb * HC1 + 128 * cg, acc, 0);
 #pragma unroll
         for (int i = 0; i < MTW; i++) {
             float mx = 0.0f;
@@ -943,6 +966,10 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         uint8_t* stage = smem;                                      // [M][SP1]
         float* red = reinterpret_cast<float*>(smem + TL::STAGE);    // [NW][RG], ring stage 1
         const int g = lane >> 4;
+        if (a.g_out) {
+            store_linear1(a.g_out, a, row0, rows, rg * RG, nb * HC1 + 64 * cg, acc, 0, 4);
+            store_linear1(a.u_out, a, row0, rows, rg * RG, nb * HC1 + 64 * cg, acc, 4, 4);
+        }
         float hv[MTW][4][4];
 #pragma unroll
         for (int i = 0; i < MTW; i++) {

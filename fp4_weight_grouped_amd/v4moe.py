@@ -76,10 +76,16 @@ def lib():
                                           _vp, _sz, _vp]
         L.moe_dequant_fp8.argtypes = [ctypes.POINTER(Mat), _i32, _i32, _i32, _vp, _vp]
         L.moe_quantize_weights.argtypes = [_i32, _i32, _i32, _vp, _i32, ctypes.POINTER(Mat), _vp, _vp]
+        L.moe_backward_workspace_bytes.argtypes = [_DP]
+        L.moe_backward_workspace_bytes.restype = _sz
+        L.moe_transpose_weights.argtypes = [_DP, ctypes.POINTER(ExpertsC), _vp, _vp, _vp]
+        L.moe_layer_backward.argtypes = [_DP, _vp, _vp, _vp, _i32, _vp, ctypes.POINTER(ExpertsC), _vp, _vp,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_time_next_ffn.argtypes = [_vp, _vp]
         L.moe_time_next_ffn.restype = None
         for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-                  "moe_prepack_weights", "moe_dequant_fp8", "moe_quantize_weights"):
+                  "moe_prepack_weights", "moe_dequant_fp8", "moe_quantize_weights", "moe_transpose_weights",
+                  "moe_layer_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -200,6 +206,23 @@ def quantize_weights(w, clamped=None, packed: bool = False) -> DeviceMatrix:
     return out
 
 
+def moe_backward_workspace_bytes(d: Dims) -> int:
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(d)))
+
+
+def moe_transpose_weights(d: Dims, experts: DeviceExperts, wt_gu, wt_d):
+    ex = experts.c()
+    _check(lib().moe_transpose_weights(ctypes.byref(d), ctypes.byref(ex), _p(wt_gu), _p(wt_d), _stream()))
+
+
+def moe_layer_backward(d: Dims, x, w_router, bias, mode, token_ids, experts: DeviceExperts, wt_gu, wt_d, dout,
+                       dx, dw, dWg, dWu, dWd, workspace):
+    ex = experts.c()
+    _check(lib().moe_layer_backward(ctypes.byref(d), _p(x), _p(w_router), _p(bias), mode, _p(token_ids),
+                                    ctypes.byref(ex), _p(wt_gu), _p(wt_d), _p(dout), _p(dx), _p(dw), _p(dWg),
+                                    _p(dWu), _p(dWd), _p(workspace), workspace.numel(), _stream()))
+
+
 def moe_time_next_ffn(start_event, stop_event):
     """start/stop: torch.cuda.Event(enable_timing=True) objects, or None."""
     a = None if start_event is None else ctypes.c_void_p(start_event.cuda_event)
@@ -270,6 +293,39 @@ class MoELayer:
         moe_layer_forward(d, x, self.w_router, bias, mode, token_ids, self.experts, ids, w, off, out,
                           self.workspace(T))
         return out, ids, w, off
+
+    def transposed_weights(self):
+        """The bf16 transposed FP8 weight values the backward reads (made once)."""
+        if getattr(self, "_wt", None) is None:
+            d = self.dims(1)
+            gI = 2 * self.I if self.act == ACT_SWIGLU else self.I
+            wt_gu = torch.empty((self.E, self.H, gI), dtype=torch.int16, device=self.device)
+            wt_d = torch.empty((self.E, self.I, self.H), dtype=torch.int16, device=self.device)
+            moe_transpose_weights(d, self.experts, wt_gu, wt_d)
+            self._wt = (wt_gu, wt_d)
+        return self._wt
+
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, bias=None, mode=ROUTE_LEARNED, token_ids=None,
+                 grads=None):
+        """Gradients of sum(dout * out): dict(dx [T][H], dw [T][k], dWg / dWu [E][I][H], dWd [E][H][I])
+        (fp32; dWg absent gate-less).  ``grads`` may hold preallocated outputs."""
+        T = x.shape[0]
+        d = self.dims(T)
+        dev = self.device
+        gated = self.act == ACT_SWIGLU
+        g = grads or dict(
+            dx=torch.empty((T, self.H), dtype=torch.float32, device=dev),
+            dw=torch.empty((T, self.topk), dtype=torch.float32, device=dev),
+            dWu=torch.empty((self.E, self.I, self.H), dtype=torch.float32, device=dev),
+            dWd=torch.empty((self.E, self.H, self.I), dtype=torch.float32, device=dev),
+            **({"dWg": torch.empty((self.E, self.I, self.H), dtype=torch.float32, device=dev)} if gated else {}))
+        n = moe_backward_workspace_bytes(d)
+        if getattr(self, "_bws", None) is None or self._bws.numel() < n:
+            self._bws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        wt_gu, wt_d = self.transposed_weights()
+        moe_layer_backward(d, x, self.w_router, bias, mode, token_ids, self.experts, wt_gu, wt_d, dout,
+                           g["dx"], g["dw"], g.get("dWg"), g["dWu"], g["dWd"], self._bws)
+        return g
 
     def forward_unfused(self, x: torch.Tensor, bias=None, mode=ROUTE_LEARNED, token_ids=None):
         """The same layer through the four separate entry points."""

@@ -236,6 +236,49 @@ int moe_prepack_weights(const v4moe_dims* d, const v4moe_experts* canonical,
 int moe_dequant_fp8(const v4moe_mat* m, int32_t N, int32_t K, int32_t expert,
                     uint8_t* out, void* stream);
 
+/* ---- Backward (P1 §3 and P4 §3: the MoE backward accumulates in a fixed,
+ * token-ordered sequence with no atomics; P1 §4 and P4 §4: gradients are
+ * computed with the forward's FP8 weights and go straight to the FP32 master
+ * weights, and the transposed weights are the same FP8 values) ---- */
+
+/* Workspace bytes of moe_layer_backward (host-only, pure; 0 for invalid dims).
+ * Device memory owned by the caller, 16-byte aligned, no initialisation. */
+size_t moe_backward_workspace_bytes(const v4moe_dims* d);
+
+/* The PACKED expert weights as transposed FP8 values in bf16 (exact: every
+ * E2M1 code times its power-of-two sub-block scale is a bf16 value; the fp32
+ * 128x128 block scales are not applied and stay in w):
+ *   wt_gu: [E][H][2I] with [e][h][i] = gate(e, i, h), [e][h][I + i] = up(e, i, h)
+ *          (gate-less: [E][H][I] of up);
+ *   wt_d:  [E][I][H] with [e][i][h] = down(e, h, i).
+ * Computed once per weight version and passed to moe_layer_backward.
+ * Asynchronous on `stream`; 16-byte aligned outputs. */
+int moe_transpose_weights(const v4moe_dims* d, const v4moe_experts* w, uint16_t* wt_gu,
+                          uint16_t* wt_d, void* stream);
+
+/* Gradients of L = sum(dout * out) for the layer forward moe_layer_forward
+ * computes on the same inputs (routing, quantisation and the FFN are
+ * recomputed here).  The quantisation steps are straight-through, so
+ *   dx  [T][H] fp32   = dL/dx (through the FP8 dispatch payload),
+ *   dw  [T][topk] fp32 = dL/d(routing weight) = <dout_t, Y_p> (the router
+ *                       itself is not differentiated),
+ *   dWg, dWu [E][I][H], dWd [E][H][I] fp32 = dL/d(master weights): the
+ *                       gradients with respect to the FP8 weight values
+ *                       (dWg unused and may be NULL gate-less).
+ * Every gradient is written in full (zeros for experts without tokens), by
+ * one thread per element, in a fixed order: the result is bitwise
+ * deterministic.  Products run on bf16 matrix cores with fp32 accumulation;
+ * dout and the row gradients are rounded to bf16 before each product, as are
+ * the forward activations (E4M3 code x scale) in the weight gradients.
+ *   w: PACKED weights; wt_gu, wt_d: from moe_transpose_weights;
+ *   dout: bf16 bits [T][H]; workspace: moe_backward_workspace_bytes(d).
+ * Pointers 16-byte aligned. */
+int moe_layer_backward(const v4moe_dims* d, const uint16_t* x, const float* w_router,
+                       const float* bias, int32_t mode, const int64_t* token_ids,
+                       const v4moe_experts* w, const uint16_t* wt_gu, const uint16_t* wt_d,
+                       const uint16_t* dout, float* dx, float* dw, float* dWg, float* dWu,
+                       float* dWd, void* workspace, size_t ws_bytes, void* stream);
+
 /* Profiling hook (no effect on results).  start/stop are hipEvent_t handles
  * created by the caller (or NULL to clear).  The next moe_expert_ffn or
  * moe_layer_forward call made by this host thread records `start` on its

@@ -12,7 +12,8 @@ def test_exports_every_declared_function():
     names = v4moe.declared_functions()
     assert set(names) >= {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
                           "moe_layer_forward", "moe_workspace_bytes", "moe_prepack_weights",
-                          "moe_dequant_fp8", "moe_quantize_weights", "moe_strerror"}
+                          "moe_dequant_fp8", "moe_quantize_weights", "moe_strerror", "moe_transpose_weights",
+                          "moe_layer_backward", "moe_backward_workspace_bytes"}
     L = v4moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -72,6 +73,20 @@ def test_error_paths_without_device():
     assert L.moe_dequant_fp8(ctypes.byref(m), 15, 128, 0, p, None) == -2
     assert L.moe_dequant_fp8(ctypes.byref(m), 16, 100, 0, p, None) == -2
     assert L.moe_prepack_weights(ctypes.byref(d), ctypes.byref(ex), ctypes.byref(ex), p, 8, None) == -4
+    assert L.moe_backward_workspace_bytes(ctypes.byref(bd)) == 0
+    assert L.moe_backward_workspace_bytes(ctypes.byref(d)) > L.moe_workspace_bytes(ctypes.byref(d))
+    assert L.moe_transpose_weights(ctypes.byref(bd), ctypes.byref(ex), p, p, None) == -2
+    assert L.moe_transpose_weights(ctypes.byref(d), ctypes.byref(ex), None, p, None) == -1
+    assert L.moe_transpose_weights(ctypes.byref(d), ctypes.byref(ex), mis, p, None) == -3
+    nb = L.moe_backward_workspace_bytes(ctypes.byref(d))
+    assert L.moe_layer_backward(ctypes.byref(d), p, p, None, 0, None, ctypes.byref(ex), p, p, p, p, p, p, p, p, p,
+                                nb - 1, None) == -4
+    assert L.moe_layer_backward(ctypes.byref(d), p, p, None, 0, None, ctypes.byref(ex), p, p, p, p, p, None, p, p,
+                                p, nb, None) == -1
+    assert L.moe_layer_backward(ctypes.byref(d), p, p, None, 3, None, ctypes.byref(ex), p, p, p, p, p, p, p, p, p,
+                                nb, None) == -2
+    assert L.moe_layer_backward(ctypes.byref(d), mis, p, None, 0, None, ctypes.byref(ex), p, p, p, p, p, p, p, p, p,
+                                nb, None) == -3
     assert L.moe_quantize_weights(1, 100, 128, p, 0, ctypes.byref(m), None, None) == -2
     assert L.moe_quantize_weights(1, 128, 64, p, 0, ctypes.byref(m), None, None) == -2
     assert L.moe_quantize_weights(0, 128, 128, p, 1, ctypes.byref(m), None, None) == -2
