@@ -300,6 +300,69 @@ def run_quantizer(E, H, I, reps):
                 kernel="k_quantize_weights (fp32 master -> packed fp4 e2m1 + e8m0 + fp32 block scale)")
 
 
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
+
+
+def run_backward(name, steps, warmup, layer_cache):
+    """One backward step = moe_layer_backward (forward recompute, combine
+    backward, dgrad, activation derivative, un-permute, weight gradients) on
+    the workload's layer, inputs and dout resident in HBM.  Reported against
+    HBM (decode: forward weight bytes + bf16 transposed weights of the active
+    experts read, fp32 weight gradients of all experts written) or the dense
+    bf16 matrix peak (prefill: 4 * T*k*mats*H*I FLOP of dgrad and wgrad)."""
+    import torch
+    from fp4_weight_grouped_amd import inputs, v4moe
+    inp = inputs.make(name)
+    d = inp.dims
+    dev = "cuda:0"
+    key = (d.H, d.I, d.E, d.topk, d.act)
+    if key not in layer_cache:
+        layer_cache.clear()
+        torch.cuda.empty_cache()
+        dims = v4moe.dims(d.T, d.H, d.I, d.E, d.topk, d.act)
+        ex = v4moe.upload_experts(inp.experts, dims, dev)
+        layer_cache[key] = v4moe.MoELayer(d.H, d.I, d.E, d.topk, ex,
+                                          torch.from_numpy(inp.w_router).to(dev), dev, act=d.act)
+    layer = layer_cache[key]
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev)
+    r = np.random.default_rng(9)
+    dout = torch.from_numpy(inputs.to_bf16_bits(r.standard_normal((d.T, d.H)).astype(np.float32)).view(np.int16)).to(dev)
+    grads = layer.backward(x, dout)
+    for _ in range(warmup):
+        layer.backward(x, dout, grads=grads)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        layer.backward(x, dout, grads=grads)
+        b.record()
+    torch.cuda.synchronize()
+    ms_all = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.median(ms_all))
+    off = torch.diff(layer.forward(x)[3]).cpu().numpy()
+    n_active = int((off > 0).sum())
+    mats = 3 if d.act == inputs.ACT_SWIGLU else 2
+    hi = d.H * d.I
+    nbytes = n_active * (weight_bytes_per_expert(d.H, d.I, mats) + mats * hi * 2) + d.E * mats * hi * 4
+    flops = 4 * d.T * d.topk * mats * hi
+    rec = dict(workload=name, T=d.T, ms=ms, p10=pct(ms_all, 10), p90=pct(ms_all, 90), tokens_per_s=d.T / (ms / 1e3),
+               algorithmic_bytes=nbytes, bf16_flops=flops)
+    if d.T <= 1024:
+        a = nbytes / (ms / 1e3) / 1e9
+        rec.update(bound="hbm", achieved=a, peak=HBM_PEAK_GBS, unit="GB/s", frac=a / HBM_PEAK_GBS)
+    else:
+        a = flops / (ms / 1e3) / 1e12
+        rec.update(bound="mfma (bf16)", achieved=a, peak=BF16_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
+                   frac=a / BF16_DENSE_PEAK_TFLOPS)
+    log(f"[bench] backward {name}: {ms:.3f} ms (p10 {rec['p10']:.3f}, p90 {rec['p90']:.3f}), "
+        f"{rec['achieved']:.0f} {rec['unit']} = {rec['frac']:.3f} of peak")
+    return rec
+
+
 def cpu_baseline(inp, max_tokens=128, min_seconds=10.0, max_reps=8):
     """The oracle's layer forward on the same inputs, repeated until about
     min_seconds of CPU work have been timed."""
@@ -337,6 +400,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill side report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true", help="skip the weight-quantiser side report")
+    ap.add_argument("--no-backward", action="store_true", help="skip the layer-backward side report")
+    ap.add_argument("--only-backward", default=None, metavar="WORKLOAD",
+                    help="only time the layer backward on this workload and print its record")
     ap.add_argument("--copy-bytes", type=int, default=0, help="only run the counter-calibration copy")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-entry-point attribution and the power/clock sampling")
@@ -354,6 +420,9 @@ def main():
     if args.copy_bytes:
         copy_calibration(args.copy_bytes, args.steps)
         return
+    if args.only_backward:
+        print(json.dumps({"backward": [run_backward(args.only_backward, args.steps, args.warmup, {})]}), flush=True)
+        return
     if args.only_quantizer:
         from fp4_weight_grouped_amd import inputs
         d = inputs.WORKLOADS[args.workload].dims
@@ -364,6 +433,10 @@ def main():
     side = None
     if not args.no_prefill and args.workload != "prefill":
         side, _ = run_gpu("prefill", max(5, args.steps // 2), max(2, args.warmup // 2), cache, not args.no_extras)
+
+    bwd = None
+    if not args.no_backward:
+        bwd = [run_backward(w, max(3, args.steps // 4), 2, cache) for w in ("decode", "prefill")]
 
     quant = None
     if not args.no_quantizer:
@@ -417,6 +490,8 @@ def main():
         rec["prefill"] = dict(side, roofline=roofline(side))
     if quant is not None:
         rec["weight_quantizer"] = quant
+    if bwd is not None:
+        rec["backward"] = bwd
     print(json.dumps(rec), flush=True)
 
 

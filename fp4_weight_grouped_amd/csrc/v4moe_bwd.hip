@@ -282,27 +282,49 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 #pragma unroll
         for (int j = 0; j < 2; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Each thread moves 4 A and 8 B 16-byte pieces per 128-wide chunk: piece
+    // q of the A tile is row (tid + 256q) / 16, columns 8 * (tid % 16)...; the
+    // next chunk's pieces are loaded into registers while this one computes.
+    // Rows past the end of a DGRAD m-tile repeat its last row (never stored);
+    // columns past the chunk's end read as zero.
+    uint4 ra[4], rb[8];
+    auto load = [&](int k0) {
+        const int kn = min(128, kend - k0);
+        const int sg = tid & 15;
+        const bool in = sg * 8 < kn;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int r = (tid >> 4) + 16 * q;
+            const int ar = MODE == WGRAD ? m0 + r : row0 + min(r, rows - 1);
+            ra[q] = in ? *reinterpret_cast<const uint4*>(a.A + (size_t)ar * a.lda + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const int r = (tid >> 4) + 16 * q;
+            rb[q] = in ? *reinterpret_cast<const uint4*>(Bb + (size_t)(n0 + r) * a.ldb + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    if (kbeg < kend) load(kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += 128) {
         const int kn = min(128, kend - k0);          // multiple of 32
-        __syncthreads();
-        // A: 64 rows x 128, B: 128 rows x 128 (16 bytes per load; rows past
-        // the end of a DGRAD m-tile repeat its last row, never stored)
-        for (int idx = tid; idx < 64 * 16; idx += 256) {
-            const int r = idx >> 4, sg = idx & 15;
-            const int ar = MODE == WGRAD ? m0 + r : row0 + min(r, rows - 1);
-            *reinterpret_cast<uint4*>(&As[r * kBgPitch + sg * 8]) =
-                sg * 8 < kn ? *reinterpret_cast<const uint4*>(a.A + (size_t)ar * a.lda + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
-        }
-        for (int idx = tid; idx < 128 * 16; idx += 256) {
-            const int r = idx >> 4, sg = idx & 15;
-            *reinterpret_cast<uint4*>(&Bs[r * kBgPitch + sg * 8]) =
-                sg * 8 < kn ? *reinterpret_cast<const uint4*>(Bb + (size_t)(n0 + r) * a.ldb + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
+        __syncthreads();                             // the previous chunk's LDS reads are done
+        {
+            const int sg = tid & 15;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                *reinterpret_cast<uint4*>(&As[((tid >> 4) + 16 * q) * kBgPitch + sg * 8]) = ra[q];
+#pragma unroll
+            for (int q = 0; q < 8; q++)
+                *reinterpret_cast<uint4*>(&Bs[((tid >> 4) + 16 * q) * kBgPitch + sg * 8]) = rb[q];
         }
         __syncthreads();
+        if (k0 + 128 < kend) load(k0 + 128);
+        if (MODE != WGRAD) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+            for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < 2; j++) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
         for (int ks = 0; ks < kn; ks += 32) {
             bf8 bfr[2];
 #pragma unroll
@@ -312,23 +334,27 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
             for (int i = 0; i < 4; i++) {
                 const bf8 afr = *reinterpret_cast<const bf8*>(&As[(i * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-                    part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], part[i][j], 0, 0, 0);
+                for (int j = 0; j < 2; j++) {
+                    if (MODE == WGRAD) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+                    else part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], part[i][j], 0, 0, 0);
+                }
             }
         }
-        float s = 1.0f;
-        if (MODE == DGRAD2) s = a.blk0[((size_t)e * (a.H / 128) + k0 / 128) * (a.I / 128) + n0 / 128];
-        if (MODE == DGRAD1) {
-            const int c = k0 / 128, ci = a.I / 128;
-            s = c < ci ? a.blk0[((size_t)e * ci + c) * (a.H / 128) + n0 / 128]
-                       : a.blk1[((size_t)e * ci + (c - ci)) * (a.H / 128) + n0 / 128];
+        if (MODE != WGRAD) {
+            float s = 1.0f;
+            if (MODE == DGRAD2) s = a.blk0[((size_t)e * (a.H / 128) + k0 / 128) * (a.I / 128) + n0 / 128];
+            if (MODE == DGRAD1) {
+                const int c = k0 / 128, ci = a.I / 128;
+                s = c < ci ? a.blk0[((size_t)e * ci + c) * (a.H / 128) + n0 / 128]
+                           : a.blk1[((size_t)e * ci + (c - ci)) * (a.H / 128) + n0 / 128];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, part[i][j][q], acc[i][j][q]);
         }
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, part[i][j][q], acc[i][j][q]);
     }
     // stage the 64 x 128 fp32 tile through LDS (As/Bs reused)
     __syncthreads();
