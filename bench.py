@@ -394,8 +394,8 @@ def cpu_baseline(inp, max_tokens=128, min_seconds=10.0, max_reps=8):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill side report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -432,15 +432,15 @@ def main():
     head, inp = run_gpu(args.workload, args.steps, args.warmup, cache, not args.no_extras)
     side = None
     if not args.no_prefill and args.workload != "prefill":
-        side, _ = run_gpu("prefill", max(5, args.steps // 2), max(2, args.warmup // 2), cache, not args.no_extras)
+        side, _ = run_gpu("prefill", max(5, min(20, args.steps)), max(2, args.warmup // 2), cache, not args.no_extras)
 
     bwd = None
     if not args.no_backward:
-        bwd = [run_backward(w, max(3, args.steps // 4), 2, cache) for w in ("decode", "prefill")]
+        bwd = [run_backward(w, max(3, min(10, args.steps // 4)), 2, cache) for w in ("decode", "prefill")]
 
     quant = None
     if not args.no_quantizer:
-        quant = run_quantizer(head["E"], head["H"], head["I"], max(3, args.steps // 4))
+        quant = run_quantizer(head["E"], head["H"], head["I"], max(3, min(10, args.steps // 4)))
 
     def roofline(r):
         if r["T"] <= 1024:

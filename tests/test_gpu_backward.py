@@ -149,5 +149,10 @@ def test_backward_decode_full_size():
 
 
 @pytest.mark.slow
+def test_backward_decode_gateless_full_size():
+    sampled("decode_relu2", 4, 2)
+
+
+@pytest.mark.slow
 def test_backward_prefill_full_size():
     sampled("prefill", 3, 1)
