@@ -151,7 +151,7 @@ struct BwdLayout {
     Layout F;
     size_t ids, w, off, g, u, dys, dgu, dxs, padoff, bmt_expert, bmt_row0, bctrl, bdone1, dyT, dguT, xT, hT;
     size_t total;
-    int n_mt4, ldd, gI;
+    int n_mt4, ldd, gI, bm;
 };
 
 BwdLayout bwd_layout(const v4moe_dims* d)
@@ -162,7 +162,8 @@ BwdLayout bwd_layout(const v4moe_dims* d)
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
     const size_t T = d->T, H = d->H, I = d->I, E = d->E, P = (size_t)d->T * d->topk;
     B.gI = d->act == V4MOE_ACT_SWIGLU ? 2 * d->I : d->I;
-    B.n_mt4 = (int)(P / 64 + (P < E ? P : E) + 1);
+    B.bm = bwd_tile_rows(d->T, d->topk, d->E);
+    B.n_mt4 = (int)(P / B.bm + (P < E ? P : E) + 1);    // m-tiles of the dgrad GEMMs
     B.ldd = (int)((P + 32 * E + 63) / 64 * 64);
     B.ids = take(P * 4);
     B.w = take(P * 4);
@@ -535,13 +536,14 @@ __attribute__((visibility("default"))) int moe_layer_backward(
         if (rc) return rc;
         uint16_t* dys = reinterpret_cast<uint16_t*>(at(B.dys));
         if (launch_bwd_combine(T, H, k, dout, wts, y, pp, dys, dw, s) != hipSuccess) return V4MOE_ELAUNCH;
-        // 64-row m-tiles of the experts' row segments
+        // m-tiles of B.bm rows over the experts' row segments
         FfnArgs b = a;
         b.ctrl = reinterpret_cast<int32_t*>(at(B.bctrl));
         b.done1 = reinterpret_cast<int32_t*>(at(B.bdone1));
         int32_t* bmte = reinterpret_cast<int32_t*>(at(B.bmt_expert));
         int32_t* bmtr = reinterpret_cast<int32_t*>(at(B.bmt_row0));
-        if (launch_build_tiles(E, 4, 1, 1, 0, 1, b, bmte, bmtr, nullptr, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_build_tiles(E, B.bm / 16, 1, 1, 0, 1, b, bmte, bmtr, nullptr, s) != hipSuccess)
+            return V4MOE_ELAUNCH;
         BgemmArgs g{};
         g.I = I; g.H = H; g.act = d->act;
         g.mt_expert = bmte; g.mt_row0 = bmtr; g.ctrl = b.ctrl; g.offsets = offsets;
@@ -553,12 +555,12 @@ __attribute__((visibility("default"))) int moe_layer_backward(
         // dh = Wd^T dY, activation derivative -> dG, dU
         g.N = I; g.K = H; g.A = dys; g.lda = H; g.B = wt_d; g.ldb = H; g.b_expert = (size_t)I * H;
         g.blk0 = w->down.blk;
-        if (launch_bgemm(BG_DGRAD2, g, B.n_mt4, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bgemm(BG_DGRAD2, B.bm, g, B.n_mt4, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         // dx per row = [Wg Wu]^T [dG dU]
         g.N = H; g.K = gI; g.A = dgu; g.lda = gI; g.B = wt_gu; g.ldb = gI; g.b_expert = (size_t)H * gI;
         g.blk0 = gated(d) ? w->gate.blk : w->up.blk;
         g.blk1 = w->up.blk;
-        if (launch_bgemm(BG_DGRAD1, g, B.n_mt4, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bgemm(BG_DGRAD1, B.bm, g, B.n_mt4, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         if (launch_bwd_unpermute(T, H, k, pp, dxs, dx, s) != hipSuccess) return V4MOE_ELAUNCH;
         // transposed operands of the weight gradients
         if (launch_pad_offsets(E, offsets, padoff, s) != hipSuccess) return V4MOE_ELAUNCH;
@@ -580,14 +582,14 @@ __attribute__((visibility("default"))) int moe_layer_backward(
         wg.offsets = offsets; wg.padoff = padoff;
         wg.lda = wg.ldb = B.ldd;
         wg.M = H; wg.N = I; wg.A = dyT; wg.B = hT; wg.dW = dWd;
-        if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         wg.M = I; wg.N = H; wg.B = xT;
         if (gated(d)) {
             wg.A = dguT; wg.dW = dWg;
-            if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+            if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         }
         wg.A = dguT + (gated(d) ? (size_t)I * B.ldd : 0); wg.dW = dWu;
-        if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
     } else {
         // no tokens: every weight gradient is zero
         if (launch_fill_i32(offsets, 0, E + 1, s) != hipSuccess) return V4MOE_ELAUNCH;
@@ -598,14 +600,14 @@ __attribute__((visibility("default"))) int moe_layer_backward(
         wg.lda = wg.ldb = B.ldd;
         wg.A = dyT; wg.B = dyT;
         wg.M = H; wg.N = I; wg.dW = dWd;
-        if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         wg.M = I; wg.N = H;
         if (gated(d)) {
             wg.dW = dWg;
-            if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+            if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         }
         wg.dW = dWu;
-        if (launch_bgemm(BG_WGRAD, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
     }
     return V4MOE_OK;
 }

@@ -233,8 +233,12 @@ __global__ __launch_bounds__(256) void k_bwd_unpermute(int T, int H, int k, cons
 
 // ---------------------------------------------------------------------------
 // Grouped bf16 NT GEMM: C[m][n] = sum over 128-wide K chunks c of
-// s(c) * sum_{kk in c} A[m][kk] * B[n][kk], fp32.  Block tile 64 (m) x 128
-// (n), four waves of 64 x 32; LDS rows padded to 272 bytes.
+// s(c) * sum_{kk in c} A[m][kk] * B[n][kk], fp32.  Block tile BM (m) x 128
+// (n) with four waves of 64 x (BM/2): BM = 128 (2 x 2 waves) for the dgrads
+// of large batches (each expert's weights are read once per 128 rows, where
+// 64-row tiles made these GEMMs HBM-bound on weight re-reads), BM = 64 (1 x 4
+// waves) for small batches and the weight gradients.  Operands staged K-contiguous in LDS (272-byte rows); the
+// next 128-wide chunk is loaded into registers while this one computes.
 //   DGRAD2: m = rows of an m-tile of one expert (tile list), A = dY (sorted
 //     rows, K = H), B = Wd^T of the expert ([I][H]), s = down block scale;
 //     epilogue: the activation derivative at the forward's G, U -> dG, dU
@@ -247,23 +251,34 @@ __global__ __launch_bounds__(256) void k_bwd_unpermute(int T, int H, int k, cons
 // ---------------------------------------------------------------------------
 enum { DGRAD2 = BG_DGRAD2, DGRAD1 = BG_DGRAD1, WGRAD = BG_WGRAD };
 
-constexpr int kBgPitch = 136;   // bf16 elements per LDS row (128 + 8)
-
-template <int MODE>
+constexpr int kBgPitch = 136;                      // bf16 elements per LDS row (128 + 8)
+template <int BM>
+struct BgTile {
+    static constexpr int WR = BM / 64;             // wave rows
+    static constexpr int WC = 4 / WR;              // wave columns
+    static constexpr int NJ = 128 / WC / 16;       // 16-column n-tiles per wave
+    static constexpr int LDS = (BM + 128) * kBgPitch * 2;
+    static_assert(BM * 132 * 4 <= LDS, "epilogue staging fits");
+};
+template <int MODE, int BM>
 __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 {
-    __shared__ __align__(16) uint16_t As[64 * kBgPitch];
-    __shared__ __align__(16) uint16_t Bs[128 * kBgPitch];
+    using TL = BgTile<BM>;
+    constexpr int NJ = TL::NJ;
+    extern __shared__ __align__(16) uint16_t smem_bg[];
+    uint16_t* As = smem_bg;
+    uint16_t* Bs = smem_bg + BM * kBgPitch;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wr = w / TL::WC, wc = w % TL::WC;
     int e, row0, rows, kbeg, kend;
     const int nb = blockIdx.x % NB;
     const int n0 = nb * 128;
     int m0 = 0;
     if (MODE == WGRAD) {
         e = blockIdx.z;
-        m0 = (blockIdx.x / NB) * 64;
+        m0 = (blockIdx.x / NB) * BM;
         row0 = 0;
-        rows = 64;
+        rows = BM;
         kbeg = a.padoff[e];
         kend = kbeg + ((a.offsets[e + 1] - a.offsets[e] + 31) & ~31);
     } else {
@@ -271,29 +286,30 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
         if (mt >= a.ctrl[0]) return;
         e = a.mt_expert[mt];
         row0 = a.mt_row0[mt];
-        rows = min(64, a.offsets[e + 1] - row0);
+        rows = min(BM, a.offsets[e + 1] - row0);
         kbeg = 0;
         kend = a.K;
     }
     const uint16_t* Bb = a.B + (size_t)e * a.b_expert;
-    v4f acc[4][2], part[4][2];
+    v4f acc[4][NJ], part[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Each thread moves 4 A and 8 B 16-byte pieces per 128-wide chunk: piece
-    // q of the A tile is row (tid + 256q) / 16, columns 8 * (tid % 16)...; the
-    // next chunk's pieces are loaded into registers while this one computes.
-    // Rows past the end of a DGRAD m-tile repeat its last row (never stored);
+    // Each thread moves BM/16 A and 8 B 16-byte pieces per 128-wide chunk:
+    // piece q is row (tid / 16) + 16q, columns 8 * (tid % 16)...; the next
+    // chunk's pieces are loaded into registers while this one computes.  Rows
+    // past the end of a DGRAD m-tile repeat its last row (never stored);
     // columns past the chunk's end read as zero.
-    uint4 ra[4], rb[8];
+    constexpr int QA = BM / 16;
+    uint4 ra[QA], rb[8];
     auto load = [&](int k0) {
         const int kn = min(128, kend - k0);
         const int sg = tid & 15;
         const bool in = sg * 8 < kn;
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
+        for (int q = 0; q < QA; q++) {
             const int r = (tid >> 4) + 16 * q;
             const int ar = MODE == WGRAD ? m0 + r : row0 + min(r, rows - 1);
             ra[q] = in ? *reinterpret_cast<const uint4*>(a.A + (size_t)ar * a.lda + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
@@ -301,7 +317,8 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 #pragma unroll
         for (int q = 0; q < 8; q++) {
             const int r = (tid >> 4) + 16 * q;
-            rb[q] = in ? *reinterpret_cast<const uint4*>(Bb + (size_t)(n0 + r) * a.ldb + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
+            rb[q] = in ? *reinterpret_cast<const uint4*>(Bb + (size_t)(n0 + r) * a.ldb + k0 + sg * 8)
+                       : make_uint4(0, 0, 0, 0);
         }
     };
     if (kbeg < kend) load(kbeg);
@@ -311,7 +328,7 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
         {
             const int sg = tid & 15;
 #pragma unroll
-            for (int q = 0; q < 4; q++)
+            for (int q = 0; q < QA; q++)
                 *reinterpret_cast<uint4*>(&As[((tid >> 4) + 16 * q) * kBgPitch + sg * 8]) = ra[q];
 #pragma unroll
             for (int q = 0; q < 8; q++)
@@ -323,18 +340,20 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 2; j++) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < NJ; j++) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
         }
         for (int ks = 0; ks < kn; ks += 32) {
-            bf8 bfr[2];
+            bf8 bfr[NJ];
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-                bfr[j] = *reinterpret_cast<const bf8*>(&Bs[(w * 32 + j * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
+            for (int j = 0; j < NJ; j++)
+                bfr[j] = *reinterpret_cast<const bf8*>(
+                    &Bs[(wc * NJ * 16 + j * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const bf8 afr = *reinterpret_cast<const bf8*>(&As[(i * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
+                const bf8 afr = *reinterpret_cast<const bf8*>(
+                    &As[(wr * 64 + i * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
+                for (int j = 0; j < NJ; j++) {
                     if (MODE == WGRAD) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
                     else part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], part[i][j], 0, 0, 0);
                 }
@@ -351,23 +370,23 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 2; j++)
+                for (int j = 0; j < NJ; j++)
 #pragma unroll
                     for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, part[i][j][q], acc[i][j][q]);
         }
     }
-    // stage the 64 x 128 fp32 tile through LDS (As/Bs reused)
+    // stage the BM x 128 fp32 tile through LDS (the operand buffers reused)
     __syncthreads();
-    float* cs = reinterpret_cast<float*>(Bs);                 // [64][132]
+    float* cs = reinterpret_cast<float*>(smem_bg);            // [BM][132]
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < NJ; j++)
 #pragma unroll
             for (int q = 0; q < 4; q++)
-                cs[(i * 16 + 4 * (lane >> 4) + q) * 132 + w * 32 + j * 16 + (lane & 15)] = acc[i][j][q];
+                cs[(wr * 64 + i * 16 + 4 * (lane >> 4) + q) * 132 + wc * NJ * 16 + j * 16 + (lane & 15)] = acc[i][j][q];
     __syncthreads();
-    for (int idx = tid; idx < 64 * 32; idx += 256) {
+    for (int idx = tid; idx < BM * 32; idx += 256) {
         const int r = idx >> 5, c4 = (idx & 31) * 4;
         const float4 v = *reinterpret_cast<const float4*>(&cs[r * 132 + c4]);
         if (MODE == WGRAD) {
@@ -462,18 +481,33 @@ hipError_t launch_bwd_unpermute(int T, int H, int k, const int32_t* pair_pos, co
     return hipGetLastError();
 }
 
-hipError_t launch_bgemm(int mode, const BgemmArgs& a, int n_mt_bound, int E, hipStream_t s)
+template <int MODE, int BM>
+static hipError_t launch_bgemm_t(const BgemmArgs& a, dim3 grid, int NB, hipStream_t s)
+{
+    constexpr int LDS = BgTile<BM>::LDS;
+    static bool lds_ok = false;
+    if (!lds_ok) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_bgemm<MODE, BM>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS) != hipSuccess)
+            return hipErrorInvalidValue;
+        lds_ok = true;
+    }
+    hipLaunchKernelGGL((k_bgemm<MODE, BM>), grid, dim3(256), LDS, s, a, NB);
+    return hipGetLastError();
+}
+
+// DGRAD modes: bm (64 or 128) is the row count of the m-tiles in the list.
+hipError_t launch_bgemm(int mode, int bm, const BgemmArgs& a, int n_mt_bound, int E, hipStream_t s)
 {
     const int NB = a.N / 128;
     if (mode == WGRAD) {
         if (E == 0) return hipSuccess;
-        hipLaunchKernelGGL(k_bgemm<WGRAD>, dim3((unsigned)((a.M / 64) * NB), 1, (unsigned)E), dim3(256), 0, s, a, NB);
-    } else {
-        const dim3 grid((unsigned)(n_mt_bound * NB));
-        if (mode == DGRAD2) hipLaunchKernelGGL(k_bgemm<DGRAD2>, grid, dim3(256), 0, s, a, NB);
-        else hipLaunchKernelGGL(k_bgemm<DGRAD1>, grid, dim3(256), 0, s, a, NB);
+        return launch_bgemm_t<WGRAD, 64>(a, dim3((unsigned)((a.M / 64) * NB), 1, (unsigned)E), NB, s);
     }
-    return hipGetLastError();
+    const dim3 grid((unsigned)(n_mt_bound * NB));
+    if (bm == 128)
+        return mode == DGRAD2 ? launch_bgemm_t<DGRAD2, 128>(a, grid, NB, s) : launch_bgemm_t<DGRAD1, 128>(a, grid, NB, s);
+    return mode == DGRAD2 ? launch_bgemm_t<DGRAD2, 64>(a, grid, NB, s) : launch_bgemm_t<DGRAD1, 64>(a, grid, NB, s);
 }
 
 }  // namespace v4moe

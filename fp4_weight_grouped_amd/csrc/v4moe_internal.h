@@ -96,8 +96,11 @@ hipError_t launch_bwd_transpose(int mode, int C, int E, int k, int max_cols, con
                                 hipStream_t s);
 hipError_t launch_bwd_unpermute(int T, int H, int k, const int32_t* pair_pos, const float* dxs, float* dx,
                                 hipStream_t s);
-// DGRAD modes: grid over n_mt_bound m-tiles of 64 rows x N/128; WGRAD: E x (M/64) x (N/128).
-hipError_t launch_bgemm(int mode, const BgemmArgs& a, int n_mt_bound, int E, hipStream_t s);
+// DGRAD modes: grid over n_mt_bound m-tiles of bm (64 or 128) rows x N/128;
+// WGRAD: E x (M/64) x (N/128).
+hipError_t launch_bgemm(int mode, int bm, const BgemmArgs& a, int n_mt_bound, int E, hipStream_t s);
+// Rows per dgrad m-tile of the backward: 128 once experts average 64 rows or more.
+inline int bwd_tile_rows(int T, int k, int E) { return (long long)T * k >= 64LL * E ? 128 : 64; }
 // Wave columns per tile: a tile covers 64*CW columns of h in linear1 (128*CW
 // gate-less) and 128*CW output columns in linear2.
 int choose_cw(int MT, int H, int I, bool gated);
