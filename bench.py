@@ -18,8 +18,9 @@ TCC counter summary (FETCH_SIZE + WRITE_SIZE per FFN, scaled by
 the same counters' reading for a plain copy kernel of known size); it is
 reported only while the kernel sources hash to the value recorded with it.
 The CPU baseline is the C oracle (test infrastructure) timed on the host cores.
-The weight quantiser (FP32 master -> MXFP4, one layer's experts) is reported
-as a side record against the HBM peak.  Each workload record also carries the
+The weight quantiser (FP32 master -> MXFP4, one layer's experts), the layer
+backward (decode and prefill) and the gate-less squared-ReLU layer at the same
+parameter count (I=3072) are reported as side records.  Each workload record also carries the
 per-step device time (median, p10, p90 of HIP events around each step), the
 device time of each step of the layer through the separate entry points
 (route, permute, expert_ffn, combine), and board power and shader clock
@@ -401,6 +402,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true", help="skip the weight-quantiser side report")
     ap.add_argument("--no-backward", action="store_true", help="skip the layer-backward side report")
+    ap.add_argument("--no-gateless", action="store_true", help="skip the gate-less (squared ReLU) side report")
     ap.add_argument("--only-backward", default=None, metavar="WORKLOAD",
                     help="only time the layer backward on this workload and print its record")
     ap.add_argument("--copy-bytes", type=int, default=0, help="only run the counter-calibration copy")
@@ -460,6 +462,13 @@ def main():
 
     roof = roofline(head)
 
+    gateless = None
+    if not args.no_gateless and args.workload in ("decode", "prefill"):
+        gateless = []
+        for w in ("decode_relu2", "prefill_relu2"):
+            r, _ = run_gpu(w, max(5, min(20, args.steps)), max(2, args.warmup // 2), cache, False)
+            gateless.append(dict(r, roofline=roofline(r)))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -492,6 +501,8 @@ def main():
         rec["weight_quantizer"] = quant
     if bwd is not None:
         rec["backward"] = bwd
+    if gateless is not None:
+        rec["gateless"] = gateless
     print(json.dumps(rec), flush=True)
 
 
