@@ -365,3 +365,32 @@ def test_ragged_batch_invariance_and_determinism():
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), f["out"][lo:hi]), f"request {r} differs alone vs batch"
         assert np.array_equal(ids.cpu().numpy(), f["ids"][lo:hi])
+
+
+@pytest.mark.parametrize("T,H,E,k", [
+    (32, 256, 8, 3),        # small-batch router
+    (50, 256, 6, 2),        # E % 4 != 0: the generic router
+    (4096, 512, 256, 8),    # one token per lane, two experts per lane
+    (8192, 256, 256, 8),    # two tokens x eight experts per lane
+])
+def test_routing_exact_ties(T, H, E, k):
+    """Logits that collide exactly (x in {-1, 0, 1}, W_r columns drawn from
+    three dyadic columns): ids, ranked with ties to the lower expert id, are
+    bit-exact against the oracle in every router variant."""
+    rng = np.random.default_rng(T + E)
+    x = inputs.to_bf16_bits(rng.choice([-1.0, 0.0, 1.0], size=(T, H)).astype(np.float32))
+    base = rng.choice([0.0, 0.5, 1.0], size=(H, 3)).astype(np.float32)
+    wr = np.ascontiguousarray(base[:, rng.integers(0, 3, E)])
+    ids_ref, w_ref = oracle.route(x, wr, k)
+    d = v4moe.dims(T, H, 128, E, k)
+    xd = torch.from_numpy(x.view(np.int16)).to(DEV)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    ws = torch.empty(v4moe.moe_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    v4moe.moe_route(d, xd, torch.from_numpy(wr).to(DEV), None, 0, None, ids, w, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=1e-6, atol=0)
+    z = oracle.router_logits(x, wr)
+    ties = sum(int(np.sum(z[t, ids_ref[t, -1]] == z[t])) > 1 for t in range(0, T, max(1, T // 64)))
+    assert ties > 0
