@@ -532,7 +532,7 @@ __attribute__((visibility("default"))) int moe_layer_backward(
         FfnArgs a = ffn_args(d, L, ws, xq, xs, offsets, sp, w, y);
         a.g_out = gated(d) ? reinterpret_cast<float*>(at(B.g)) : nullptr;
         a.u_out = reinterpret_cast<float*>(at(B.u));
-        int rc = run_ffn(d, L, a, ws, false, di, s);
+        int rc = run_ffn(d, L, a, ws, L.MT < 8, di, s);   // as in moe_layer_forward
         if (rc) return rc;
         uint16_t* dys = reinterpret_cast<uint16_t*>(at(B.dys));
         if (launch_bwd_combine(T, H, k, dout, wts, y, pp, dys, dw, s) != hipSuccess) return V4MOE_ELAUNCH;
