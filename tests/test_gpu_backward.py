@@ -156,3 +156,10 @@ def test_backward_decode_gateless_full_size():
 @pytest.mark.slow
 def test_backward_prefill_full_size():
     sampled("prefill", 3, 1)
+
+
+@pytest.mark.slow
+def test_backward_largest_hidden_and_intermediate():
+    """H = I = 16384: 256 chunks in the [dG dU] contraction, the largest
+    transposes and weight gradients; every token to both experts."""
+    full_check(make(2, 16384, 16384, 2, 2, seed=35), "T2H16384I16384E2k2", runs=1)
