@@ -163,3 +163,33 @@ def test_backward_largest_hidden_and_intermediate():
     """H = I = 16384: 256 chunks in the [dG dU] contraction, the largest
     transposes and weight gradients; every token to both experts."""
     full_check(make(2, 16384, 16384, 2, 2, seed=35), "T2H16384I16384E2k2", runs=1)
+
+
+def test_qat_step_from_fp32_master_weights():
+    """One QAT step end to end: FP32 master weights -> moe_quantize_weights
+    straight into the packed layout -> layer forward and backward on the GPU;
+    the gradients (straight through to the master weights) match the oracle's
+    backward on the oracle's own quantisation of the same master weights."""
+    T, H, I, E, k = 48, 256, 256, 4, 2
+    rng = np.random.default_rng(41)
+    masters = [rng.standard_normal((E, I, H)).astype(np.float32) * np.float32(0.05),
+               rng.standard_normal((E, I, H)).astype(np.float32) * np.float32(0.05),
+               rng.standard_normal((E, H, I)).astype(np.float32) * np.float32(0.05)]
+    mats = []
+    for m in masters:
+        fp4, e8, blk, _ = oracle.quantize_weights(m)
+        mats.append(inputs.Matrix(fp4=fp4, e8m0=e8, blk=blk))
+    inp = inputs.Inputs(dims=inputs.Dims(T, H, I, E, k), mode=0, x=inputs.gen_x(41, T, H),
+                        w_router=inputs.gen_router(41, H, E), bias=None, token_ids=None,
+                        experts=inputs.Experts(*mats))
+    dout = dout_for(inp)
+    ref = oracle.layer_backward(inp, dout)
+    packed = v4moe.DeviceExperts(*[v4moe.quantize_weights(torch.from_numpy(m).to(DEV), packed=True)
+                                   for m in masters])
+    layer = v4moe.MoELayer(H, I, E, k, packed, torch.from_numpy(inp.w_router).to(DEV), DEV)
+    g = gpu_backward(layer, inp, dout)
+    check(g["dx"], ref["dx"], "qat dx")
+    check(g["dw"], ref["dw"], "qat dw")
+    for key in ("dWg", "dWu", "dWd"):
+        check(g[key], ref[key], f"qat {key}")
+        assert g[key].shape == masters[("dWg", "dWu", "dWd").index(key)].shape
