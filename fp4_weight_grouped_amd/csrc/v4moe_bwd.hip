@@ -251,23 +251,30 @@ __global__ __launch_bounds__(256) void k_bwd_unpermute(int T, int H, int k, cons
 // ---------------------------------------------------------------------------
 enum { DGRAD2 = BG_DGRAD2, DGRAD1 = BG_DGRAD1, WGRAD = BG_WGRAD };
 
-constexpr int kBgPitch = 136;                      // bf16 elements per LDS row (128 + 8)
-template <int BM>
+// KS: K per LDS stage (128; 64 for the weight gradients, whose K loops are
+// short: half the LDS and prefetch registers, more blocks per CU to hide each
+// tile's load latency).  Rows are padded by 8 elements against bank conflicts.
+template <int BM, int KS>
 struct BgTile {
     static constexpr int WR = BM / 64;             // wave rows
     static constexpr int WC = 4 / WR;              // wave columns
     static constexpr int NJ = 128 / WC / 16;       // 16-column n-tiles per wave
-    static constexpr int LDS = (BM + 128) * kBgPitch * 2;
-    static_assert(BM * 132 * 4 <= LDS, "epilogue staging fits");
+    static constexpr int PITCH = KS + 8;           // bf16 elements per LDS row
+    static constexpr int SEGS = KS / 8;            // 16-byte segments per row and stage
+    static constexpr int QA = BM * SEGS / 256;     // A pieces per thread per stage
+    static constexpr int QB = 128 * SEGS / 256;    // B pieces per thread per stage
+    static constexpr int OPS_BYTES = (BM + 128) * PITCH * 2;
+    static constexpr int LDS = OPS_BYTES > BM * 132 * 4 ? OPS_BYTES : BM * 132 * 4;
 };
-template <int MODE, int BM>
+template <int MODE, int BM, int KS>
 __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 {
-    using TL = BgTile<BM>;
-    constexpr int NJ = TL::NJ;
+    using TL = BgTile<BM, KS>;
+    constexpr int NJ = TL::NJ, PITCH = TL::PITCH, SEGS = TL::SEGS;
+    static_assert(MODE == WGRAD || KS == 128, "the dgrads promote once per 128-wide stage");
     extern __shared__ __align__(16) uint16_t smem_bg[];
     uint16_t* As = smem_bg;
-    uint16_t* Bs = smem_bg + BM * kBgPitch;
+    uint16_t* Bs = smem_bg + BM * PITCH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wr = w / TL::WC, wc = w % TL::WC;
     int e, row0, rows, kbeg, kend;
@@ -297,45 +304,45 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 #pragma unroll
         for (int j = 0; j < NJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Each thread moves BM/16 A and 8 B 16-byte pieces per 128-wide chunk:
-    // piece q is row (tid / 16) + 16q, columns 8 * (tid % 16)...; the next
-    // chunk's pieces are loaded into registers while this one computes.  Rows
+    // Each thread moves QA A and QB B 16-byte pieces per stage: piece q is
+    // row (tid / SEGS) + (256 / SEGS) q, columns 8 * (tid % SEGS)...; the next
+    // stage's pieces are loaded into registers while this one computes.  Rows
     // past the end of a DGRAD m-tile repeat its last row (never stored);
-    // columns past the chunk's end read as zero.
-    constexpr int QA = BM / 16;
-    uint4 ra[QA], rb[8];
+    // columns past the stage's end read as zero.
+    constexpr int RSTEP = 256 / SEGS;
+    uint4 ra[TL::QA], rb[TL::QB];
     auto load = [&](int k0) {
-        const int kn = min(128, kend - k0);
-        const int sg = tid & 15;
+        const int kn = min(KS, kend - k0);
+        const int sg = tid % SEGS;
         const bool in = sg * 8 < kn;
 #pragma unroll
-        for (int q = 0; q < QA; q++) {
-            const int r = (tid >> 4) + 16 * q;
+        for (int q = 0; q < TL::QA; q++) {
+            const int r = tid / SEGS + RSTEP * q;
             const int ar = MODE == WGRAD ? m0 + r : row0 + min(r, rows - 1);
             ra[q] = in ? *reinterpret_cast<const uint4*>(a.A + (size_t)ar * a.lda + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-            const int r = (tid >> 4) + 16 * q;
+        for (int q = 0; q < TL::QB; q++) {
+            const int r = tid / SEGS + RSTEP * q;
             rb[q] = in ? *reinterpret_cast<const uint4*>(Bb + (size_t)(n0 + r) * a.ldb + k0 + sg * 8)
                        : make_uint4(0, 0, 0, 0);
         }
     };
     if (kbeg < kend) load(kbeg);
-    for (int k0 = kbeg; k0 < kend; k0 += 128) {
-        const int kn = min(128, kend - k0);          // multiple of 32
-        __syncthreads();                             // the previous chunk's LDS reads are done
+    for (int k0 = kbeg; k0 < kend; k0 += KS) {
+        const int kn = min(KS, kend - k0);           // multiple of 32
+        __syncthreads();                             // the previous stage's LDS reads are done
         {
-            const int sg = tid & 15;
+            const int sg = tid % SEGS;
 #pragma unroll
-            for (int q = 0; q < QA; q++)
-                *reinterpret_cast<uint4*>(&As[((tid >> 4) + 16 * q) * kBgPitch + sg * 8]) = ra[q];
+            for (int q = 0; q < TL::QA; q++)
+                *reinterpret_cast<uint4*>(&As[(tid / SEGS + RSTEP * q) * PITCH + sg * 8]) = ra[q];
 #pragma unroll
-            for (int q = 0; q < 8; q++)
-                *reinterpret_cast<uint4*>(&Bs[((tid >> 4) + 16 * q) * kBgPitch + sg * 8]) = rb[q];
+            for (int q = 0; q < TL::QB; q++)
+                *reinterpret_cast<uint4*>(&Bs[(tid / SEGS + RSTEP * q) * PITCH + sg * 8]) = rb[q];
         }
         __syncthreads();
-        if (k0 + 128 < kend) load(k0 + 128);
+        if (k0 + KS < kend) load(k0 + KS);
         if (MODE != WGRAD) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
@@ -347,11 +354,11 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 #pragma unroll
             for (int j = 0; j < NJ; j++)
                 bfr[j] = *reinterpret_cast<const bf8*>(
-                    &Bs[(wc * NJ * 16 + j * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
+                    &Bs[(wc * NJ * 16 + j * 16 + (lane & 15)) * PITCH + ks + 8 * (lane >> 4)]);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const bf8 afr = *reinterpret_cast<const bf8*>(
-                    &As[(wr * 64 + i * 16 + (lane & 15)) * kBgPitch + ks + 8 * (lane >> 4)]);
+                    &As[(wr * 64 + i * 16 + (lane & 15)) * PITCH + ks + 8 * (lane >> 4)]);
 #pragma unroll
                 for (int j = 0; j < NJ; j++) {
                     if (MODE == WGRAD) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
@@ -481,18 +488,18 @@ hipError_t launch_bwd_unpermute(int T, int H, int k, const int32_t* pair_pos, co
     return hipGetLastError();
 }
 
-template <int MODE, int BM>
+template <int MODE, int BM, int KS = 128>
 static hipError_t launch_bgemm_t(const BgemmArgs& a, dim3 grid, int NB, hipStream_t s)
 {
-    constexpr int LDS = BgTile<BM>::LDS;
+    constexpr int LDS = BgTile<BM, KS>::LDS;
     static bool lds_ok = false;
     if (!lds_ok) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_bgemm<MODE, BM>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_bgemm<MODE, BM, KS>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS) != hipSuccess)
             return hipErrorInvalidValue;
         lds_ok = true;
     }
-    hipLaunchKernelGGL((k_bgemm<MODE, BM>), grid, dim3(256), LDS, s, a, NB);
+    hipLaunchKernelGGL((k_bgemm<MODE, BM, KS>), grid, dim3(256), LDS, s, a, NB);
     return hipGetLastError();
 }
 
@@ -502,7 +509,7 @@ hipError_t launch_bgemm(int mode, int bm, const BgemmArgs& a, int n_mt_bound, in
     const int NB = a.N / 128;
     if (mode == WGRAD) {
         if (E == 0) return hipSuccess;
-        return launch_bgemm_t<WGRAD, 64>(a, dim3((unsigned)((a.M / 64) * NB), 1, (unsigned)E), NB, s);
+        return launch_bgemm_t<WGRAD, 64, 64>(a, dim3((unsigned)((a.M / 64) * NB), 1, (unsigned)E), NB, s);
     }
     const dim3 grid((unsigned)(n_mt_bound * NB));
     if (bm == 128)
