@@ -264,7 +264,10 @@ struct BgTile {
     static constexpr int QA = BM * SEGS / 256;     // A pieces per thread per stage
     static constexpr int QB = 128 * SEGS / 256;    // B pieces per thread per stage
     static constexpr int OPS_BYTES = (BM + 128) * PITCH * 2;
-    static constexpr int LDS = OPS_BYTES > BM * 132 * 4 ? OPS_BYTES : BM * 132 * 4;
+    // the fp32 tile is staged for its stores in passes of PR rows
+    static constexpr int PR = OPS_BYTES >= BM * 132 * 4 ? BM : 32;
+    static constexpr int LDS = OPS_BYTES > PR * 132 * 4 ? OPS_BYTES : PR * 132 * 4;
+    static_assert(BM % PR == 0 && PR % 16 == 0, "passes cover whole 16-row tiles");
 };
 template <int MODE, int BM, int KS>
 __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
@@ -382,54 +385,61 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
                     for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, part[i][j][q], acc[i][j][q]);
         }
     }
-    // stage the BM x 128 fp32 tile through LDS (the operand buffers reused)
-    __syncthreads();
-    float* cs = reinterpret_cast<float*>(smem_bg);            // [BM][132]
+    // stage the BM x 128 fp32 tile through LDS (the operand buffers reused),
+    // PR rows at a time, then store rows with 16-byte writes
+    constexpr int PR = TL::PR;
+    float* cs = reinterpret_cast<float*>(smem_bg);            // [PR][132]
+    for (int pass = 0; pass < BM / PR; pass++) {
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 4; i++) {
+            const int rl = wr * 64 + i * 16;
+            if (rl / PR != pass) continue;
 #pragma unroll
-        for (int j = 0; j < NJ; j++)
+            for (int j = 0; j < NJ; j++)
 #pragma unroll
-            for (int q = 0; q < 4; q++)
-                cs[(wr * 64 + i * 16 + 4 * (lane >> 4) + q) * 132 + wc * NJ * 16 + j * 16 + (lane & 15)] = acc[i][j][q];
-    __syncthreads();
-    for (int idx = tid; idx < BM * 32; idx += 256) {
-        const int r = idx >> 5, c4 = (idx & 31) * 4;
-        const float4 v = *reinterpret_cast<const float4*>(&cs[r * 132 + c4]);
-        if (MODE == WGRAD) {
-            *reinterpret_cast<float4*>(a.dW + ((size_t)e * a.M + m0 + r) * a.N + n0 + c4) = v;
-        } else if (r < rows) {
-            const size_t row = (size_t)row0 + r;
-            if (MODE == DGRAD1) {
-                *reinterpret_cast<float4*>(a.dxs + row * a.H + n0 + c4) = v;
-            } else {
-                const float dh[4] = {v.x, v.y, v.z, v.w};
-                const float4 U = *reinterpret_cast<const float4*>(a.u + row * a.I + n0 + c4);
-                const float uu[4] = {U.x, U.y, U.z, U.w};
-                float dg[4], du[4];
-                if (a.act == 0) {
-                    const float4 G = *reinterpret_cast<const float4*>(a.g + row * a.I + n0 + c4);
-                    const float gg[4] = {G.x, G.y, G.z, G.w};
-#pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const float sg = 1.0f / (1.0f + expf(-gg[q]));
-                        dg[q] = dh[q] * uu[q] * sg * (1.0f + gg[q] * (1.0f - sg));
-                        du[q] = dh[q] * gg[q] * sg;
-                    }
+                for (int q = 0; q < 4; q++)
+                    cs[(rl - pass * PR + 4 * (lane >> 4) + q) * 132 + wc * NJ * 16 + j * 16 + (lane & 15)] = acc[i][j][q];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < PR * 32; idx += 256) {
+            const int r = pass * PR + (idx >> 5), c4 = (idx & 31) * 4;
+            const float4 v = *reinterpret_cast<const float4*>(&cs[(idx >> 5) * 132 + c4]);
+            if (MODE == WGRAD) {
+                *reinterpret_cast<float4*>(a.dW + ((size_t)e * a.M + m0 + r) * a.N + n0 + c4) = v;
+            } else if (r < rows) {
+                const size_t row = (size_t)row0 + r;
+                if (MODE == DGRAD1) {
+                    *reinterpret_cast<float4*>(a.dxs + row * a.H + n0 + c4) = v;
                 } else {
+                    const float dh[4] = {v.x, v.y, v.z, v.w};
+                    const float4 U = *reinterpret_cast<const float4*>(a.u + row * a.I + n0 + c4);
+                    const float uu[4] = {U.x, U.y, U.z, U.w};
+                    float dg[4], du[4];
+                    if (a.act == 0) {
+                        const float4 G = *reinterpret_cast<const float4*>(a.g + row * a.I + n0 + c4);
+                        const float gg[4] = {G.x, G.y, G.z, G.w};
 #pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        dg[q] = 0.0f;
-                        du[q] = uu[q] > 0.0f ? (a.act == 1 ? 2.0f * uu[q] * dh[q] : dh[q]) : 0.0f;
+                        for (int q = 0; q < 4; q++) {
+                            const float sg = 1.0f / (1.0f + expf(-gg[q]));
+                            dg[q] = dh[q] * uu[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+                            du[q] = dh[q] * gg[q] * sg;
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            dg[q] = 0.0f;
+                            du[q] = uu[q] > 0.0f ? (a.act == 1 ? 2.0f * uu[q] * dh[q] : dh[q]) : 0.0f;
+                        }
                     }
+                    const int ld = a.act == 0 ? 2 * a.I : a.I;
+                    uint16_t* d = a.dgu + row * ld + n0 + c4;
+                    if (a.act == 0) {
+                        *reinterpret_cast<uint2*>(d) = make_uint2(bf16x2(dg[0], dg[1]), bf16x2(dg[2], dg[3]));
+                        d += a.I;
+                    }
+                    *reinterpret_cast<uint2*>(d) = make_uint2(bf16x2(du[0], du[1]), bf16x2(du[2], du[3]));
                 }
-                const int ld = a.act == 0 ? 2 * a.I : a.I;
-                uint16_t* d = a.dgu + row * ld + n0 + c4;
-                if (a.act == 0) {
-                    *reinterpret_cast<uint2*>(d) = make_uint2(bf16x2(dg[0], dg[1]), bf16x2(dg[2], dg[3]));
-                    d += a.I;
-                }
-                *reinterpret_cast<uint2*>(d) = make_uint2(bf16x2(du[0], du[1]), bf16x2(du[2], du[3]));
             }
         }
     }
