@@ -619,8 +619,8 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
 // the weights as the A operand (FP4 codes and their E8M0 scales straight from
 // LDS, no dequantisation pass) and the tokens as the B operand, so a lane gets
 // four consecutive output columns of one token; then acc = fma(xs*blk, P, acc)
-// with one activation scale per token tile.  A row group with no valid row
-// skips its MFMAs.
+// with one activation scale per token tile.  A 16-token tile with no valid
+// row skips its MFMAs.
 // ---------------------------------------------------------------------------
 
 // Stores that another XCD may read within the same launch: agent-scope
@@ -762,6 +762,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     const int row0 = uniform(a.mt_row0[mt]);
     const int rows = uniform(min(M, a.offsets[e + 1] - row0));
     const bool active = rows > rg * RG;                      // this row group has a valid row
+    const int nti = uniform(min(MTW, (rows - rg * RG + 15) / 16));  // token tiles with a valid row
     const int K = PHASE == 1 ? a.H : a.I;
     const int N = PHASE == 1 ? a.I : a.H;
     const int C = K / 128;
@@ -858,61 +859,75 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
     for (int u = 0; u < NS - 1; u++)
         if (u < C) issue(u, u);
 
-    for (int c = 0; c < C; c++) {
-        wait_stages<TL::OPS>(min(NS - 2, C - 1 - c));
-        __syncthreads();
-        if (c + NS - 1 < C) issue(c + NS - 1, (c + NS - 1) % NS);
-        if (!active) continue;
+    // The chunk loop is instantiated per count of token tiles holding a valid
+    // row, chosen once per wave (only the last m-tile of an expert has fewer
+    // than MTW).  Every instance runs the same sequence of barriers, one per
+    // chunk, so waves of different row groups may run different instances.
+    auto chunk_loop = [&](auto count) {
+        constexpr int NTI = decltype(count)::value;
+        for (int c = 0; c < C; c++) {
+            wait_stages<TL::OPS>(min(NS - 2, C - 1 - c));
+            __syncthreads();
+            if (c + NS - 1 < C) issue(c + NS - 1, (c + NS - 1) % NS);
+            if (!active) continue;
 
-        const uint8_t* st = smem + (c % NS) * TL::STAGE;
-        uint4 bq[8];
+            const uint8_t* st = smem + (c % NS) * TL::STAGE;
+            uint4 bq[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            bq[j] = *reinterpret_cast<const uint4*>(st + TL::B_OFF + (cg * 8 + j) * 1024 + lane * 16);
-        const int sc[2] = {*reinterpret_cast<const int*>(st + TL::S_OFF + (cg * 2) * 256 + lane * 4),
-                           *reinterpret_cast<const int*>(st + TL::S_OFF + (cg * 2 + 1) * 256 + lane * 4)};
-        const float sb0 = blk0[c];
-        const float sb1 = blk1[c];
-        // this lane's token in each token tile: one activation scale per tile
-        float xsv[MTW];
-        {
-            const float* xr = reinterpret_cast<const float*>(st + TL::X_OFF + rg * 256) + (lane & 15) * MTW;
-            if (MTW == 4) {
-                const float4 v = *reinterpret_cast<const float4*>(xr);
-                xsv[0] = v.x; xsv[1] = v.y; xsv[2 % MTW] = v.z; xsv[3 % MTW] = v.w;
-            } else if (MTW == 2) {
-                const float2 v = *reinterpret_cast<const float2*>(xr);
-                xsv[0] = v.x; xsv[1 % MTW] = v.y;
-            } else {
+            for (int j = 0; j < 8; j++)
+                bq[j] = *reinterpret_cast<const uint4*>(st + TL::B_OFF + (cg * 8 + j) * 1024 + lane * 16);
+            const int sc[2] = {*reinterpret_cast<const int*>(st + TL::S_OFF + (cg * 2) * 256 + lane * 4),
+                               *reinterpret_cast<const int*>(st + TL::S_OFF + (cg * 2 + 1) * 256 + lane * 4)};
+            const float sb0 = blk0[c];
+            const float sb1 = blk1[c];
+            // this lane's token in each token tile: one activation scale per tile
+            float xsv[MTW];
+            {
+                const float* xr = reinterpret_cast<const float*>(st + TL::X_OFF + rg * 256) + (lane & 15) * MTW;
+                if (MTW == 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(xr);
+                    xsv[0] = v.x; xsv[1] = v.y; xsv[2 % MTW] = v.z; xsv[3 % MTW] = v.w;
+                } else if (MTW == 2) {
+                    const float2 v = *reinterpret_cast<const float2*>(xr);
+                    xsv[0] = v.x; xsv[1 % MTW] = v.y;
+                } else {
 #pragma unroll
-                for (int i = 0; i < MTW; i++) xsv[i] = xr[i];
+                    for (int i = 0; i < MTW; i++) xsv[i] = xr[i];
+                }
+            }
+            // Every token tile with a valid row is computed (rows past the end
+            // hold finite filler and are never stored; tiles wholly past the end
+            // keep zero accumulators), in straight-line code: the eight
+            // independent MFMAs of a token tile are all in flight before their
+            // results are promoted.
+#pragma unroll
+            for (int i = 0; i < NTI; i++) {
+                const int r = rg * RG + i * 16 + (lane & 15);
+                const int sw = (r >> 1) & 7;
+                const int g = lane >> 4;
+                const uint8_t* arow = st + TL::A_OFF + r * 128;
+                const uint4 a0 = *reinterpret_cast<const uint4*>(arow + ((g ^ sw) * 16));
+                const uint4 a1 = *reinterpret_cast<const uint4*>(arow + (((g + 4) ^ sw) * 16));
+                const v8i xf = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                v4f P[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) P[j] = mfma_e2m1_e4m3_sel(j & 3, bq[j], sc[j >> 2], xf);
+                const float s0 = xsv[i] * sb0;
+                const float s1 = xsv[i] * sb1;
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const float s = (PHASE == 1 && G && j >= 4) ? s1 : s0;
+#pragma unroll
+                    for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, P[j][q], acc[i][j][q]);
+                }
             }
         }
-        // Every token tile of the row group is computed (rows past the end hold
-        // finite filler and are never stored), so the eight independent MFMAs
-        // of a token tile are all in flight before their results are promoted.
-#pragma unroll
-        for (int i = 0; i < MTW; i++) {
-            const int r = rg * RG + i * 16 + (lane & 15);
-            const int sw = (r >> 1) & 7;
-            const int g = lane >> 4;
-            const uint8_t* arow = st + TL::A_OFF + r * 128;
-            const uint4 a0 = *reinterpret_cast<const uint4*>(arow + ((g ^ sw) * 16));
-            const uint4 a1 = *reinterpret_cast<const uint4*>(arow + (((g + 4) ^ sw) * 16));
-            const v8i xf = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            v4f P[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) P[j] = mfma_e2m1_e4m3_sel(j & 3, bq[j], sc[j >> 2], xf);
-            const float s0 = xsv[i] * sb0;
-            const float s1 = xsv[i] * sb1;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float s = (PHASE == 1 && G && j >= 4) ? s1 : s0;
-#pragma unroll
-                for (int q = 0; q < 4; q++) acc[i][j][q] = __builtin_fmaf(s, P[j][q], acc[i][j][q]);
-            }
-        }
-    }
+    };
+    if (nti >= MTW) chunk_loop(std::integral_constant<int, MTW>{});
+    else if (MTW >= 4 && nti == 3) chunk_loop(std::integral_constant<int, (MTW >= 4 ? 3 : 1)>{});
+    else if (MTW >= 2 && nti == 2) chunk_loop(std::integral_constant<int, (MTW >= 2 ? 2 : 1)>{});
+    else chunk_loop(std::integral_constant<int, 1>{});
     __syncthreads();   // every wave is done with the ring: its first stages become staging space
 
     if (PHASE == 1 && !G) {
