@@ -179,6 +179,23 @@ def test_shapes_full_parity(T, H, I, E, k, mode, bias):
     full_check(custom(T, H, I, E, k, mode=mode, bias=bias), f"T{T}H{H}I{I}E{E}k{k}")
 
 
+
+# Every token to every expert (k = E): each expert holds exactly T rows, so T
+# fixes how many rows the last m-tile of every expert has, and with it how many
+# 16-row token tiles of each row group hold a valid row (the tile computes
+# only those).  128-row tiles (two launches, two row groups of 64 rows):
+# 97 -> 64 + 33 rows, 129 -> 1 row, 144 -> 16, 145 -> 17, 176 -> 48, 192 -> 64
+# (second row group empty), 193 -> 65, 224 -> 96, 241 -> 113, 256 -> full.
+# 64-row tiles (persistent): 41, 64, 81; 32-row tiles: 17, 33.
+@pytest.mark.parametrize("T", [17, 33, 41, 64, 81, 97, 129, 144, 145, 176, 192, 193, 224, 241, 256])
+def test_last_m_tile_token_tiles(T):
+    full_check(custom(T, 512, 256, 4, 4, seed=5), f"T{T}H512I256E4k4")
+
+
+@pytest.mark.parametrize("T", [145, 241])
+def test_last_m_tile_token_tiles_gateless(T):
+    full_check(custom(T, 512, 512, 4, 4, seed=6, act=inputs.ACT_RELU2), f"T{T}H512I512E4k4relu2")
+
 RELU2, RELU = inputs.ACT_RELU2, inputs.ACT_RELU
 
 
