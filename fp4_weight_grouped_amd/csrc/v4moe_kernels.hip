@@ -450,8 +450,16 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __
     const bool active = part < P;
     const int b0 = active ? (int)((long long)part * nblk / P) : 0;
     const int b1 = active ? (int)((long long)(part + 1) * nblk / P) : 0;
+    // 16 loads in flight per batch (integer sums: any order gives the same total)
+    constexpr int U = 16;
     int s = 0;
-    for (int b = b0; b < b1; b++) s += hist[(size_t)b * E + e];
+    for (int b = b0; b < b1; b += U) {
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) v[u] = b + u < b1 ? hist[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < U; u++) s += v[u];
+    }
     part_sum[tid] = active ? s : 0;
     __syncthreads();
     int tot = 0;
@@ -468,10 +476,16 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __
         int run = 0;
         for (int p = 0; p < part; p++) run += part_sum[p * E + e];
         run += offsets[e];
-        for (int b = b0; b < b1; b++) {
-            const int c = hist[(size_t)b * E + e];
-            hist[(size_t)b * E + e] = run;
-            run += c;
+        for (int b = b0; b < b1; b += U) {
+            int v[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) v[u] = b + u < b1 ? hist[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (b + u < b1) {
+                    hist[(size_t)(b + u) * E + e] = run;
+                    run += v[u];
+                }
         }
     }
 }
@@ -1121,16 +1135,30 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const uint
     const size_t t = idx / (H / 8);
     const size_t c = idx % (H / 8);
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < k; j++) {
-        const float wj = w[t * k + j];
-        const uint4 v = *reinterpret_cast<const uint4*>(y + (t * k + j) * H + c * 8);
+    auto add = [&](float wj, uint4 v) {
         const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             acc[2 * u] = __builtin_fmaf(wj, bf16_to_f32(q[u] & 0xFFFFu), acc[2 * u]);
             acc[2 * u + 1] = __builtin_fmaf(wj, bf16_to_f32(q[u] >> 16), acc[2 * u + 1]);
         }
-    }
+    };
+    // the rows of the first eight slots are all loaded before any is added,
+    // then added in slot order (further slots follow in order)
+    constexpr int KU = 8;
+    uint4 v[KU];
+    float wv[KU];
+#pragma unroll
+    for (int j = 0; j < KU; j++)
+        if (j < k) {
+            wv[j] = w[t * k + j];
+            v[j] = *reinterpret_cast<const uint4*>(y + (t * k + j) * H + c * 8);
+        }
+#pragma unroll
+    for (int j = 0; j < KU; j++)
+        if (j < k) add(wv[j], v[j]);
+    for (int j = KU; j < k; j++)
+        add(w[t * k + j], *reinterpret_cast<const uint4*>(y + (t * k + j) * H + c * 8));
     const uint4 o = make_uint4(bf16x2(acc[0], acc[1]), bf16x2(acc[2], acc[3]), bf16x2(acc[4], acc[5]),
                                bf16x2(acc[6], acc[7]));
     *reinterpret_cast<uint4*>(out + t * H + c * 8) = o;
