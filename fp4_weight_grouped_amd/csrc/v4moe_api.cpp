@@ -189,8 +189,15 @@ BwdLayout bwd_layout(const v4moe_dims* d)
 
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
+// Outputs of the permutation when it runs fused with the tile list (small
+// batches: one block for both, in place of moe_permute's launches).
+struct FusedPerm {
+    const int32_t* ids;
+    int32_t *offsets, *sorted_pair, *pair_pos;
+};
+
 int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws, bool persistent,
-            DeviceInfo* di, hipStream_t s)
+            DeviceInfo* di, hipStream_t s, const FusedPerm* ff = nullptr)
 {
     const int NB1 = nb1(d, L.CW), NB2 = d->H / (128 * L.CW);
     hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
@@ -203,11 +210,15 @@ int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws,
     const double mt_per_expert = (double)d->T * d->topk / d->E / (16.0 * L.MT) + 0.5;
     const double items_per_wave = kWaveExperts * (mt_per_expert < 1.0 ? 1.0 : mt_per_expert) * NB1;
     const int lag = 1 + (int)(1.5 * grid / items_per_wave);
-    if (launch_build_tiles(d->E, L.MT, NB1, NB2, persistent ? 1 : 0, lag, a,
-                           reinterpret_cast<int32_t*>(ws + L.mt_expert),
-                           reinterpret_cast<int32_t*>(ws + L.mt_row0),
-                           reinterpret_cast<uint32_t*>(ws + L.queue), s) != hipSuccess)
-        return V4MOE_ELAUNCH;
+    int32_t* mt_expert = reinterpret_cast<int32_t*>(ws + L.mt_expert);
+    int32_t* mt_row0 = reinterpret_cast<int32_t*>(ws + L.mt_row0);
+    uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
+    const hipError_t e = ff ? launch_perm_tiles(d->T, d->topk, d->E, ff->ids, ff->offsets, ff->sorted_pair,
+                                                ff->pair_pos, L.MT, NB1, NB2, persistent ? 1 : 0, lag, a, mt_expert,
+                                                mt_row0, queue, s)
+                            : launch_build_tiles(d->E, L.MT, NB1, NB2, persistent ? 1 : 0, lag, a, mt_expert,
+                                                 mt_row0, queue, s);
+    if (e != hipSuccess) return V4MOE_ELAUNCH;
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return V4MOE_ELAUNCH;
     if (persistent) {
         const int max_items = L.n_mt_bound * (NB1 + NB2);
@@ -370,19 +381,23 @@ __attribute__((visibility("default"))) int moe_layer_forward(
     int32_t* sp = reinterpret_cast<int32_t*>(ws + L.sorted_pair);
     int32_t* pp = reinterpret_cast<int32_t*>(ws + L.pair_pos);
     uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+    // Small batches: the permutation and the tile list run as one block (same
+    // device code, same results).
+    const bool fuse = perm_tiles_one_block(d->T, d->topk, d->E);
     if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w,
                      reinterpret_cast<float*>(ws + L.z), s) != hipSuccess)
         return V4MOE_ELAUNCH;
     if (launch_quant_x(d->T, d->H, x, xq, xs, s) != hipSuccess) return V4MOE_ELAUNCH;
-    if (launch_permute(d->T, d->topk, d->E, topk_ids, expert_offsets, sp, pp,
-                       reinterpret_cast<int32_t*>(ws + L.hist), s) != hipSuccess)
+    if (!fuse && launch_permute(d->T, d->topk, d->E, topk_ids, expert_offsets, sp, pp,
+                                reinterpret_cast<int32_t*>(ws + L.hist), s) != hipSuccess)
         return V4MOE_ELAUNCH;
     const FfnArgs a = ffn_args(d, L, ws, xq, xs, expert_offsets, sp, w, y);
+    const FusedPerm ff{topk_ids, expert_offsets, sp, pp};
     // The wave-scheduled persistent kernel for weight-streaming batches (m-tiles
     // of at most 64 rows); with 128-row m-tiles it measured 5-10% slower than
     // the two launches on one GPU, where there is no transfer to hide.  Both
     // run the same tiles: the results are identical.
-    int rc = run_ffn(d, L, a, ws, L.MT < 8, di, s);
+    int rc = run_ffn(d, L, a, ws, L.MT < 8, di, s, fuse ? &ff : nullptr);
     if (rc) return rc;
     if (launch_combine(d->T, d->H, d->topk, y, topk_w, out, s) != hipSuccess) return V4MOE_ELAUNCH;
     return V4MOE_OK;

@@ -51,6 +51,12 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offs
 hipError_t launch_build_tiles(int E, int MT, int NB1, int NB2, int build_queue, int lag,
                               const FfnArgs& a, int32_t* mt_expert, int32_t* mt_row0,
                               uint32_t* queue, hipStream_t s);
+// Small batches (perm_tiles_one_block): the permutation and launch_build_tiles'
+// work in one block, in place of launch_permute + launch_build_tiles.
+bool perm_tiles_one_block(int T, int k, int E);
+hipError_t launch_perm_tiles(int T, int k, int E, const int32_t* ids, int32_t* offsets, int32_t* sorted_pair,
+                             int32_t* pair_pos, int MT, int NB1, int NB2, int build_queue, int lag, const FfnArgs& a,
+                             int32_t* mt_expert, int32_t* mt_row0, uint32_t* queue, hipStream_t s);
 // CW = wave columns per tile (2 or 4, from choose_cw); MT = 8 tiles also have
 // two wave rows.
 hipError_t launch_ffn(int phase, int MT, int CW, const FfnArgs& a, hipStream_t s);

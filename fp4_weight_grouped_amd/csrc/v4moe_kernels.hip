@@ -239,12 +239,9 @@ __global__ __launch_bounds__(256) void k_route_logits_any(int T, int H, int E, c
 // Top-k per token (one wave per token): the k largest logits, the lower expert
 // id winning ties, slot j = j-th pick; then lanes 0..k-1 compute the affinity
 // sqrt(softplus(z)) and the weights normalised over the k picks.
-__global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, const float* __restrict__ zg,
-                                                      int32_t* __restrict__ ids, float* __restrict__ wts)
+__device__ __forceinline__ void select_token(int t, int lane, int E, int k, const float* __restrict__ zg,
+                                             int32_t* __restrict__ ids, float* __restrict__ wts)
 {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
     const float* z = zg + (size_t)t * E;
     float zv[16];
 #pragma unroll
@@ -279,6 +276,13 @@ __global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, const
         ids[(size_t)t * k + lane] = my_e;
         wts[(size_t)t * k + lane] = sum > 0.0f ? a / sum : 1.0f / (float)k;
     }
+}
+__global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, const float* __restrict__ zg,
+                                                      int32_t* __restrict__ ids, float* __restrict__ wts)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    select_token(t, threadIdx.x & 63, E, k, zg, ids, wts);
 }
 
 // Hash routing: expert_j = splitmix64(id*k + j) mod E, +1 mod E past repeats.
@@ -494,12 +498,10 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __
 // chunks (wave w handles chunk w): histograms, offsets and per-chunk bases,
 // positions.  Same results as the three kernels above.  LDS: hist[nblk][E]
 // then cnt[nblk][E].
-__global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t* __restrict__ ids,
-                                                     int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ sorted_pair,
-                                                     int32_t* __restrict__ pair_pos)
+__device__ __forceinline__ void perm_small_block(int P, int E, const int32_t* __restrict__ ids,
+                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+                                                 int32_t* __restrict__ pair_pos, int32_t* sh)
 {
-    extern __shared__ int32_t sh[];
     __shared__ int total_s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nblk = (P + kPermChunk - 1) / kPermChunk;
@@ -526,6 +528,14 @@ __global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t
     __syncthreads();
     if (w < nblk) perm_chunk<false>(P, w * kPermChunk, lane, ids, cnt + w * E, hist + w * E, sorted_pair, pair_pos);
 }
+__global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t* __restrict__ ids,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_pair,
+                                                     int32_t* __restrict__ pair_pos)
+{
+    extern __shared__ int32_t sh[];
+    perm_small_block(P, E, ids, offsets, sorted_pair, pair_pos, sh);
+}
 
 // ---------------------------------------------------------------------------
 // m-tile list and persistent work queue.
@@ -537,13 +547,11 @@ __global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t
 // blocks well before its linear2 tiles are, so linear2 rarely waits.  Entry =
 // phase<<31 | mtile<<8 | n-block.  Also clears the persistent kernel's counters.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int NB2, int build_queue, int D,
-                                                      const int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ mt_expert,
-                                                      int32_t* __restrict__ mt_row0,
-                                                      int32_t* __restrict__ ctrl,
-                                                      int32_t* __restrict__ done1,
-                                                      uint32_t* __restrict__ queue)
+__device__ __forceinline__ void build_tiles_block(int E, int M, int NB1, int NB2, int build_queue, int D,
+                                                  const int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ mt_expert, int32_t* __restrict__ mt_row0,
+                                                  int32_t* __restrict__ ctrl, int32_t* __restrict__ done1,
+                                                  uint32_t* __restrict__ queue)
 {
     __shared__ int32_t base[1025];
     __shared__ int32_t qstart[257];   // start of queue segment i (queue order), then the end
@@ -602,6 +610,34 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
         const int mt = base[swv * kWaveExperts] + i / NB;
         queue[q] = ((uint32_t)sph << 31) | ((uint32_t)mt << 8) | (uint32_t)(i % NB);
     }
+}
+__global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int NB2, int build_queue, int D,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ mt_expert,
+                                                      int32_t* __restrict__ mt_row0,
+                                                      int32_t* __restrict__ ctrl,
+                                                      int32_t* __restrict__ done1,
+                                                      uint32_t* __restrict__ queue)
+{
+    build_tiles_block(E, M, NB1, NB2, build_queue, D, offsets, mt_expert, mt_row0, ctrl, done1, queue);
+}
+
+// Small batches: the permutation and the m-tile list / work queue in one
+// 1024-thread block, the same device code as k_perm_small and k_build_tiles
+// run one after the other (the tile list reads the offsets after a block
+// barrier), so the results are identical; one dependent launch fewer on the
+// latency-bound path.
+__global__ __launch_bounds__(1024) void k_perm_tiles(int P, int E, const int32_t* __restrict__ ids,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+                                                     int32_t* __restrict__ pair_pos, int M, int NB1, int NB2,
+                                                     int build_queue, int D, int32_t* __restrict__ mt_expert,
+                                                     int32_t* __restrict__ mt_row0, int32_t* __restrict__ ctrl,
+                                                     int32_t* __restrict__ done1, uint32_t* __restrict__ queue)
+{
+    extern __shared__ int32_t sh[];
+    perm_small_block(P, E, ids, offsets, sorted_pair, pair_pos, sh);
+    __syncthreads();
+    build_tiles_block(E, M, NB1, NB2, build_queue, D, offsets, mt_expert, mt_row0, ctrl, done1, queue);
 }
 
 // ---------------------------------------------------------------------------
@@ -1457,6 +1493,24 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offs
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, E, nblk, hist, offsets);
     hipLaunchKernelGGL(k_perm_pass<false>, dim3(nblk), dim3(64), (size_t)E * 4, s, P, E, ids, hist,
                        sorted_pair, pair_pos);
+    return hipGetLastError();
+}
+
+bool perm_tiles_one_block(int T, int k, int E)
+{
+    const int nblk = (T * k + kPermChunk - 1) / kPermChunk;
+    return T >= 1 && nblk <= 16 && nblk * E <= 4096;
+}
+
+hipError_t launch_perm_tiles(int T, int k, int E, const int32_t* ids, int32_t* offsets, int32_t* sorted_pair,
+                             int32_t* pair_pos, int MT, int NB1, int NB2, int build_queue, int lag, const FfnArgs& a,
+                             int32_t* mt_expert, int32_t* mt_row0, uint32_t* queue, hipStream_t s)
+{
+    const int P = T * k;
+    const int nblk = (P + kPermChunk - 1) / kPermChunk;
+    hipLaunchKernelGGL(k_perm_tiles, dim3(1), dim3(1024), (size_t)2 * nblk * E * 4, s, P, E, ids, offsets,
+                       sorted_pair, pair_pos, 16 * MT, NB1, NB2, build_queue, lag, mt_expert, mt_row0, a.ctrl,
+                       a.done1, queue);
     return hipGetLastError();
 }
 
