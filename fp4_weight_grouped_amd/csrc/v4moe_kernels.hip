@@ -679,6 +679,21 @@ __device__ __forceinline__ void store_coherent(float* p, float v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent(uint8_t* p, uint4 v);
+// h and its scales: agent-coherent stores when linear2 tiles of the same launch
+// read them (the persistent kernel), plain stores when the next launch does.
+template <bool COH>
+__device__ __forceinline__ void store_h(float* p, float v)
+{
+    if (COH) store_coherent(p, v);
+    else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void store_h(uint8_t* p, uint4 v)
+{
+    if (COH) store_coherent(p, v);
+    else *reinterpret_cast<uint4*>(p) = v;
+}
 __device__ __forceinline__ void store_coherent(uint8_t* p, uint4 v)
 {
     uint64_t* q = reinterpret_cast<uint64_t*>(p);
@@ -794,7 +809,7 @@ __device__ __forceinline__ void store_linear1(float* out, const FfnArgs& a, int 
 
 // G: the expert FFN is SwiGLU (gate and up projections); otherwise gate-less
 // (a.act selects the activation).  Phase 2 does not depend on G.
-template <int PHASE, int MT, int RW, int CW, bool G>
+template <int PHASE, int MT, int RW, int CW, bool G, bool COH = true>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8_t* smem)
 {
     using TL = TileLayout<MT, RW, CW>;
@@ -1006,7 +1021,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
             const float s = mx > 0.0f ? mx / 448.0f : 1.0f;
             const float inv = 1.0f / s;
             if (g == 0 && r < rows)
-                store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * CW + cg, s);
+                store_h<COH>(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * CW + cg, s);
 #pragma unroll
             for (int j = 0; j < 8; j++)
                 *reinterpret_cast<uint32_t*>(stage + r * SP1 + 128 * cg + 16 * j + 4 * g) =
@@ -1018,7 +1033,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         for (int s = tid; s < M * SEGS; s += NT) {
             const int r = s / SEGS, sg = s % SEGS;
             if (r < rows)
-                store_coherent(a.hq + (size_t)(row0 + r) * a.I + nb * HC1 + sg * 16,
+                store_h<COH>(a.hq + (size_t)(row0 + r) * a.I + nb * HC1 + sg * 16,
                                *reinterpret_cast<const uint4*>(stage + r * SP1 + sg * 16));
         }
         __syncthreads();
@@ -1061,7 +1076,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
             const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
             const float inv = 1.0f / s;
             if ((cg & 1) == 0 && g == 0 && r < rows)
-                store_coherent(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * (CW / 2) + (cg >> 1), s);
+                store_h<COH>(a.hs + (size_t)(row0 + r) * a.hs_stride + nb * (CW / 2) + (cg >> 1), s);
 #pragma unroll
             for (int j = 0; j < 4; j++)
                 *reinterpret_cast<uint32_t*>(stage + r * SP1 + 64 * cg + 16 * j + 4 * g) =
@@ -1072,7 +1087,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int mt, int nb, uint8
         for (int s = tid; s < M * SEGS; s += NT) {
             const int r = s / SEGS, sg = s % SEGS;
             if (r < rows)
-                store_coherent(a.hq + (size_t)(row0 + r) * a.I + nb * HC1 + sg * 16,
+                store_h<COH>(a.hq + (size_t)(row0 + r) * a.I + nb * HC1 + sg * 16,
                                *reinterpret_cast<const uint4*>(stage + r * SP1 + sg * 16));
         }
         __syncthreads();
@@ -1112,7 +1127,7 @@ __global__ __launch_bounds__(64 * RW * CW) void k_ffn(FfnArgs a, int NB)
     const int mt = blockIdx.x / NB;
     const int nb = blockIdx.x % NB;
     if (mt >= a.ctrl[0]) return;
-    ffn_tile<PHASE, MT, RW, CW, G>(a, mt, nb, smem);
+    ffn_tile<PHASE, MT, RW, CW, G, false>(a, mt, nb, smem);   // the next launch reads h
 }
 
 // Persistent, wave-scheduled: blocks take queue entries in order.  A linear2
