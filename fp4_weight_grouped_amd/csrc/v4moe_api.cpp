@@ -104,7 +104,7 @@ Layout layout(const v4moe_dims* d)
     L.hist = take((size_t)(L.nblk > 0 ? L.nblk : 1) * E * 4);
     L.mt_expert = take((size_t)L.n_mt_bound * 4);
     L.mt_row0 = take((size_t)L.n_mt_bound * 4);
-    L.ctrl = take(16 * 4);
+    L.ctrl = take(32 * 4);
     L.done1 = take((size_t)L.n_mt_bound * 4);
     L.queue = take((size_t)L.n_mt_bound * (NB1 + NB2) * 4);
     L.hq = take(P * I);
@@ -213,11 +213,17 @@ int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws,
     int32_t* mt_expert = reinterpret_cast<int32_t*>(ws + L.mt_expert);
     int32_t* mt_row0 = reinterpret_cast<int32_t*>(ws + L.mt_row0);
     uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
+    // Two launches with many experts: each expert's m-tiles (and every column
+    // block of them) run on one XCD, so its weights and activation rows are
+    // fetched into one L2 (measured 2% faster at T = 8192, E = 256).  With
+    // few experts the round-robin groups would leave XCDs idle.
+    FfnArgs b = a;
+    b.xcd_groups = !persistent && d->E >= 64 ? 1 : 0;
+    const int mode = persistent ? 1 : (b.xcd_groups ? 2 : 0);
     const hipError_t e = ff ? launch_perm_tiles(d->T, d->topk, d->E, ff->ids, ff->offsets, ff->sorted_pair,
-                                                ff->pair_pos, L.MT, NB1, NB2, persistent ? 1 : 0, lag, a, mt_expert,
-                                                mt_row0, queue, s)
-                            : launch_build_tiles(d->E, L.MT, NB1, NB2, persistent ? 1 : 0, lag, a, mt_expert,
-                                                 mt_row0, queue, s);
+                                                ff->pair_pos, L.MT, NB1, NB2, mode, lag, b, mt_expert, mt_row0,
+                                                queue, s)
+                            : launch_build_tiles(d->E, L.MT, NB1, NB2, mode, lag, b, mt_expert, mt_row0, queue, s);
     if (e != hipSuccess) return V4MOE_ELAUNCH;
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return V4MOE_ELAUNCH;
     if (persistent) {
@@ -225,8 +231,8 @@ int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws,
         if (grid > max_items) grid = max_items;
         if (launch_ffn_persistent(L.MT, L.CW, a, grid, s) != hipSuccess) return V4MOE_ELAUNCH;
     } else {
-        if (launch_ffn(1, L.MT, L.CW, a, s) != hipSuccess) return V4MOE_ELAUNCH;
-        if (launch_ffn(2, L.MT, L.CW, a, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_ffn(1, L.MT, L.CW, b, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_ffn(2, L.MT, L.CW, b, s) != hipSuccess) return V4MOE_ELAUNCH;
     }
     if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return V4MOE_ELAUNCH;
     return V4MOE_OK;

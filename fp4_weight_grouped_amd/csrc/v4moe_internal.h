@@ -37,7 +37,8 @@ struct FfnArgs {
     const int32_t* mt_row0;    // [n_mt_bound] first sorted row of each m-tile
     int32_t* ctrl;             // [0] number of m-tiles, [1] queue head, [2] queue length
     int32_t* done1;            // [n_mt_bound] finished linear1 tiles per m-tile
-    const uint32_t* queue;     // persistent schedule
+    const uint32_t* queue;     // persistent schedule, or the per-XCD m-tile lists
+    int xcd_groups;            // two-launch FFN: m-tiles grouped by XCD (k_build_tiles mode 2)
     float* g_out;              // optional [T*topk][I]: linear1 gate outputs (fp32, sorted rows), or null
     float* u_out;              // optional [T*topk][I]: linear1 up outputs, or null
 };

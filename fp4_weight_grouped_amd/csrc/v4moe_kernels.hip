@@ -575,7 +575,7 @@ __device__ __forceinline__ void build_tiles_block(int E, int M, int NB1, int NB2
     // linear1 of wave s and linear2 of wave s-D; then linear2 of waves W-D..W-1.
     // Segment index i in 0..2W-1 -> (phase, wave).
     int len = 0, ph = 0, wv = 0;
-    if (build_queue && tid < 2 * W) {
+    if (build_queue == 1 && tid < 2 * W) {
         const int i = tid;
         if (i < D) { ph = 0; wv = i; }
         else if (i < 2 * W - D) { const int s2 = i - D; ph = s2 & 1; wv = ph ? (D + s2 / 2) - D : D + s2 / 2; }
@@ -584,7 +584,7 @@ __device__ __forceinline__ void build_tiles_block(int E, int M, int NB1, int NB2
         len = a * (ph ? NB2 : NB1);
     }
     const int start = block_exclusive_scan(len, &qlen_s);
-    if (build_queue && tid < 2 * W) {
+    if (build_queue == 1 && tid < 2 * W) {
         qstart[tid] = start;
         qkey[tid] = 2 * wv + ph;
     }
@@ -592,9 +592,35 @@ __device__ __forceinline__ void build_tiles_block(int E, int M, int NB1, int NB2
         qstart[2 * W] = total * (NB1 + NB2);
         ctrl[0] = total;
         ctrl[1] = 0;
-        ctrl[2] = build_queue ? total * (NB1 + NB2) : 0;
+        ctrl[2] = build_queue == 1 ? total * (NB1 + NB2) : 0;
     }
-    if (!build_queue) return;
+    if (build_queue == 2) {
+        // Per-XCD m-tile lists for the two-launch FFN: expert e belongs to
+        // group e % 8 (the XCD that runs blocks b with b % 8 == group), its
+        // m-tiles in order; group x's list is queue[ctrl[16+x] ..], ctrl[24+x]
+        // entries long.  All m-tiles of an expert, and all column blocks of an
+        // m-tile, then share one XCD's L2.
+        __shared__ int gcount[8];
+        if (tid < 8) {
+            int c = 0;
+            for (int e2 = tid; e2 < E; e2 += 8) c += base[e2 + 1] - base[e2];
+            gcount[tid] = c;
+        }
+        __syncthreads();
+        int gstart = 0;
+        for (int x = 0; x < (tid & 7); x++) gstart += gcount[x];
+        if (tid < 8) {
+            ctrl[16 + tid] = gstart;
+            ctrl[24 + tid] = gcount[tid];
+        }
+        if (tid < E) {
+            int pos = gstart;
+            for (int e2 = tid & 7; e2 < tid; e2 += 8) pos += base[e2 + 1] - base[e2];
+            for (int m = 0; m < n; m++) queue[pos + m] = (uint32_t)(my_base + m);
+        }
+        return;
+    }
+    if (build_queue != 1) return;
     __syncthreads();
     // every entry on its own: its segment is the last one starting at or before
     // it (empty segments share their start with the next one)
@@ -1124,9 +1150,20 @@ template <int PHASE, int MT, int RW, int CW, bool G>
 __global__ __launch_bounds__(64 * RW * CW) void k_ffn(FfnArgs a, int NB)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    const int mt = blockIdx.x / NB;
-    const int nb = blockIdx.x % NB;
-    if (mt >= a.ctrl[0]) return;
+    int mt, nb;
+    if (a.xcd_groups) {
+        // block b runs on XCD b % 8 (round-robin dispatch): item b / 8 of that
+        // group's m-tile list, column block fastest
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        const int li = j / NB;
+        if (li >= a.ctrl[24 + x]) return;
+        nb = j % NB;
+        mt = (int)a.queue[a.ctrl[16 + x] + li];
+    } else {
+        mt = blockIdx.x / NB;
+        nb = blockIdx.x % NB;
+        if (mt >= a.ctrl[0]) return;
+    }
     ffn_tile<PHASE, MT, RW, CW, G, false>(a, mt, nb, smem);   // the next launch reads h
 }
 
@@ -1556,7 +1593,7 @@ static hipError_t launch_ffn_t(const FfnArgs& a, hipStream_t s)
     const int NB = PHASE == 1 ? a.I / (TL::HC * (G ? 1 : 2)) : a.H / TL::OC;
     const size_t lds = TL::BYTES;
     if (allow_lds(k_ffn<PHASE, MT, RW, CW, G>, lds, lds_ok) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_ffn<PHASE, MT, RW, CW, G>), dim3((unsigned)a.n_mt_bound * NB), dim3(TL::NT), lds, s, a,
+    hipLaunchKernelGGL((k_ffn<PHASE, MT, RW, CW, G>), dim3((unsigned)a.n_mt_bound * NB * (a.xcd_groups ? 8 : 1)), dim3(TL::NT), lds, s, a,
                        NB);
     return hipGetLastError();
 }

@@ -174,6 +174,8 @@ def test_tiny_full_parity():
     (300, 256, 128, 16, 3, 1, False),   # hash routing, odd k
     (600, 256, 256, 4, 2, 0, False),    # 128-row tiles, several per expert
     (513, 768, 128, 5, 5, 0, False),    # k = E, 128-row tiles
+    (1024, 512, 512, 64, 8, 0, False),  # 128-row tiles with m-tiles grouped per XCD (E >= 64)
+    (1300, 512, 256, 96, 8, 1, False),  # the same with hash routing and ragged groups
 ])
 def test_shapes_full_parity(T, H, I, E, k, mode, bias):
     full_check(custom(T, H, I, E, k, mode=mode, bias=bias), f"T{T}H{H}I{I}E{E}k{k}")
