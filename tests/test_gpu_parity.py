@@ -168,10 +168,11 @@ def test_tiny_full_parity():
 
 @pytest.mark.parametrize("T,H,I,E,k,mode,bias", [
     (37, 256, 128, 8, 2, 0, False),     # ragged tail, 16-row tiles
-    (16, 256, 128, 8, 8, 0, False),     # every token to every expert
-    (100, 256, 384, 12, 4, 0, True),    # I = 3 blocks, partial scheduling wave, bias
-    (200, 512, 256, 8, 2, 0, False),    # 64-row tiles
-    (300, 256, 128, 16, 3, 1, False),   # hash routing, odd k
+    (40, 512, 256, 8, 2, 0, False),     # 16-row tiles with four wave columns (the decode shape)
+    (16, 256, 128, 8, 8, 0, False),     # every token to every expert, 32-row tiles
+    (100, 256, 384, 12, 4, 0, True),    # I = 3 blocks, partial scheduling wave, bias, 64-row tiles
+    (150, 512, 256, 8, 2, 0, False),    # 64-row tiles, four wave columns
+    (300, 256, 128, 16, 3, 1, False),   # hash routing, odd k, 128-row tiles
     (600, 256, 256, 4, 2, 0, False),    # 128-row tiles, several per expert
     (513, 768, 128, 5, 5, 0, False),    # k = E, 128-row tiles
     (1024, 512, 512, 64, 8, 0, False),  # 128-row tiles with m-tiles grouped per XCD (E >= 64)
@@ -186,10 +187,11 @@ def test_shapes_full_parity(T, H, I, E, k, mode, bias):
 # fixes how many rows the last m-tile of every expert has, and with it how many
 # 16-row token tiles of each row group hold a valid row (the tile computes
 # only those).  128-row tiles (two launches, two row groups of 64 rows):
-# 97 -> 64 + 33 rows, 129 -> 1 row, 144 -> 16, 145 -> 17, 176 -> 48, 192 -> 64
-# (second row group empty), 193 -> 65, 224 -> 96, 241 -> 113, 256 -> full.
-# 64-row tiles (persistent): 41, 64, 81; 32-row tiles: 17, 33.
-@pytest.mark.parametrize("T", [17, 33, 41, 64, 81, 97, 129, 144, 145, 176, 192, 193, 224, 241, 256])
+# 64 -> 64 rows (second row group empty), 81 -> 64 + 17, 97 -> 64 + 33, 129 -> 1
+# row, 144 -> 16, 145 -> 17, 176 -> 48, 192 -> 64, 193 -> 65, 224 -> 96,
+# 241 -> 113, 256 -> full.  64-row tiles (persistent): 33, 41, 48; 32-row
+# tiles: 17, 24.
+@pytest.mark.parametrize("T", [17, 24, 33, 41, 48, 64, 81, 97, 129, 144, 145, 176, 192, 193, 224, 241, 256])
 def test_last_m_tile_token_tiles(T):
     full_check(custom(T, 512, 256, 4, 4, seed=5), f"T{T}H512I256E4k4")
 
@@ -208,10 +210,11 @@ def test_tiny_gateless_full_parity():
 @pytest.mark.parametrize("T,H,I,E,k,act", [
     (37, 256, 256, 8, 2, RELU2),        # ragged tail, 16-row tiles, two-wave-column tiles
     (40, 256, 768, 8, 2, RELU),         # I = 3 linear1 tiles of 256 columns, ReLU
-    (160, 512, 256, 8, 4, RELU2),       # 64-row tiles, persistent, CW = 2
-    (160, 512, 512, 8, 4, RELU),        # 64-row tiles, persistent, CW = 4
+    (72, 512, 256, 8, 4, RELU2),        # 64-row tiles, persistent, CW = 2
+    (72, 512, 512, 8, 4, RELU),         # 64-row tiles, persistent, CW = 4
     (600, 512, 512, 4, 2, RELU2),       # 128-row tiles (two launches), CW = 4
-    (300, 256, 256, 16, 3, RELU),       # 64-row tiles, odd k, CW = 2
+    (200, 256, 256, 16, 3, RELU),       # 64-row tiles, odd k, CW = 2
+    (160, 512, 256, 8, 4, RELU2),       # 128-row tiles (two launches), CW = 2
     (300, 256, 512, 16, 1, RELU2),      # 32-row tiles, k = 1
 ])
 def test_gateless_shapes_full_parity(T, H, I, E, k, act):
