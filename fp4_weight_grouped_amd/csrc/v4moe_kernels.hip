@@ -53,10 +53,16 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
                  :: "v"(g), "s"(lds_base) : "memory", "m0");
 }
 
-// Router logits.  Block = 4 waves, 64*TS tokens x 4*ES experts: lane l runs
-// the chains of tokens t0 + l + 64*i (i < TS) for the ES experts of its wave,
-// TS*ES independent fp32 fma chains over h in increasing order from +0; the
-// optional bias is one fp32 add afterwards.  The block's slice of W_r is
+// Router logits.  h is cut into chunks of ROUTE_CHUNK (the last one shorter
+// when it does not divide H); a logit is the fp32 sum, in increasing chunk
+// order from +0, of one fp32 fma chain per chunk (h increasing, from +0); the
+// optional bias is one fp32 add afterwards.  Block = 4 waves, 64*TS tokens x
+// 4*ES experts: lane l runs the chains of tokens t0 + l + 64*i (i < TS) for
+// the ES experts of its wave, TS*ES independent chains at a time.  With
+// gridDim.z == 1 a block folds all chunks itself and writes z (+ bias); with
+// gridDim.z == the number of chunks, block z runs chunk z only and writes its
+// chain sums, without bias, to z + blockIdx.z*T*E for the select kernel to
+// fold (more, shorter chains for batches too small to fill the chip).  The block's slice of W_r is
 // staged through LDS HC rows at a time, transposed to expert-major rows (padded
 // by 4 floats against bank conflicts), so one broadcast LDS read gives four
 // consecutive h of one expert; the next slice is loaded into registers while
@@ -64,7 +70,8 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
 // direct-to-LDS loads issued a stage ahead (rows padded by 16 bytes), for
 // batches too small to hide global-load latency behind a lane's few chains;
 // otherwise each lane reads its x rows from global memory one step ahead.
-// z is [T][E].  Needs E % (4*ES) == 0 and H % HC == 0.
+// z is [T][E].  Needs E % (4*ES) == 0, H % HC == 0 and ROUTE_CHUNK % HC == 0.
+constexpr int ROUTE_CHUNK = 512;
 template <int TS, int ES, int HC, bool XL>
 __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
                                                       const uint16_t* __restrict__ x,
@@ -85,7 +92,12 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t0 = blockIdx.x * 64 * TS;
     const int eb0 = blockIdx.y * EB;
+    static_assert(ROUTE_CHUNK % HC == 0, "a stage never straddles a chunk");
+    constexpr int SPC = ROUTE_CHUNK / HC;    // stages per chunk
     const int nst = H / HC;
+    // stages [s0, s1) of this block: all, or those of chunk blockIdx.z
+    const int s0 = gridDim.z == 1 ? 0 : blockIdx.z * SPC;
+    const int s1 = gridDim.z == 1 ? nst : min(s0 + SPC, nst);
 
     // staging: float4 f of the [HC][EB] slice = row f / (EB/4), experts 4*(f % (EB/4)) .. +3;
     // uint4 g of the x slice = token row g / (HC/8), 8 h at column g % (HC/8)
@@ -127,20 +139,20 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
             }
         }
     };
-    dma_x(0, 0);
-    load_stage(0);
-    store_stage(0);
+    dma_x(s0, s0 & 1);
+    load_stage(s0);
+    store_stage(s0 & 1);
     wait_vm<0>();
     __syncthreads();
 
     const uint4* xp[TS];
 #pragma unroll
     for (int i = 0; i < TS; i++) xp[i] = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + lane + 64 * i, T - 1) * H);
-    float acc[TS][ES];
+    float acc[TS][ES], tot[TS][ES];
 #pragma unroll
     for (int i = 0; i < TS; i++)
 #pragma unroll
-        for (int j = 0; j < ES; j++) acc[i][j] = 0.0f;
+        for (int j = 0; j < ES; j++) acc[i][j] = tot[i][j] = 0.0f;
 
     // x of 8 consecutive h of token i, for the step starting at stage-relative h
     auto xload = [&](int s, int i, int h) -> uint4 {
@@ -148,8 +160,8 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
         const int g = s * HC + h;
         return xp[i][(g < H ? g : H - 8) / 8];
     };
-    for (int s = 0; s < nst; s++) {
-        if (s + 1 < nst) {
+    for (int s = s0; s < s1; s++) {
+        if (s + 1 < s1) {
             dma_x(s + 1, (s + 1) & 1);
             load_stage(s + 1);
         }
@@ -203,10 +215,20 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
 #pragma unroll
                 for (int v = 0; v < HS / 8; v++) xc[i][v] = xn[i][v];
         }
-        if (s + 1 < nst) store_stage((s + 1) & 1);
+        if ((s + 1) % SPC == 0 || s + 1 == nst) {   // end of a chunk: fold its chain sums
+#pragma unroll
+            for (int i = 0; i < TS; i++)
+#pragma unroll
+                for (int j = 0; j < ES; j++) {
+                    tot[i][j] = tot[i][j] + acc[i][j];
+                    acc[i][j] = 0.0f;
+                }
+        }
+        if (s + 1 < s1) store_stage((s + 1) & 1);
         if (XL) wait_vm<0>();
         __syncthreads();
     }
+    float* zo = z + (size_t)blockIdx.z * T * E;
 #pragma unroll
     for (int i = 0; i < TS; i++) {
         const int t = t0 + lane + 64 * i;
@@ -214,9 +236,9 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
 #pragma unroll
             for (int j = 0; j < ES; j++) {
                 const int e = eb0 + w * ES + j;
-                float v = acc[i][j];
-                if (bias) v = v + bias[e];
-                z[(size_t)t * E + e] = v;
+                float v = tot[i][j];
+                if (bias && gridDim.z == 1) v = v + bias[e];
+                zo[(size_t)t * E + e] = v;
             }
         }
     }
@@ -230,22 +252,43 @@ __global__ __launch_bounds__(256) void k_route_logits_any(int T, int H, int E, c
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (size_t)T * E) return;
     const int t = (int)(i / E), e = (int)(i % E);
-    float acc = 0.0f;
-    for (int h = 0; h < H; h++) acc = __builtin_fmaf(bf16_to_f32(x[(size_t)t * H + h]), wr[(size_t)h * E + e], acc);
-    if (bias) acc = acc + bias[e];
-    z[i] = acc;
+    float tot = 0.0f;
+    for (int h0 = 0; h0 < H; h0 += ROUTE_CHUNK) {
+        const int h1 = min(h0 + ROUTE_CHUNK, H);
+        float acc = 0.0f;
+        for (int h = h0; h < h1; h++)
+            acc = __builtin_fmaf(bf16_to_f32(x[(size_t)t * H + h]), wr[(size_t)h * E + e], acc);
+        tot = tot + acc;
+    }
+    if (bias) tot = tot + bias[e];
+    z[i] = tot;
 }
 
 // Top-k per token (one wave per token): the k largest logits, the lower expert
 // id winning ties, slot j = j-th pick; then lanes 0..k-1 compute the affinity
-// sqrt(softplus(z)) and the weights normalised over the k picks.
-__device__ __forceinline__ void select_token(int t, int lane, int E, int k, const float* __restrict__ zg,
+// sqrt(softplus(z)) and the weights normalised over the k picks.  The logits
+// are the fp32 sum, in order from +0, of nz arrays [T][E] of chunk sums
+// (stride T*E), plus bias when it is not NULL.
+__device__ __forceinline__ void select_token(int t, int lane, int T, int E, int k, int nz,
+                                             const float* __restrict__ zg, const float* __restrict__ bias,
                                              int32_t* __restrict__ ids, float* __restrict__ wts)
 {
     const float* z = zg + (size_t)t * E;
     float zv[16];
 #pragma unroll
-    for (int q = 0; q < 16; q++) zv[q] = (q * 64 < E && lane + 64 * q < E) ? z[lane + 64 * q] : 0.0f;
+    for (int q = 0; q < 16; q++) {
+        const int e = lane + 64 * q;
+        float v = 0.0f;
+        if (q * 64 < E && e < E) {
+            if (nz == 1) {
+                v = z[e];
+            } else {
+                for (int c = 0; c < nz; c++) v = v + z[(size_t)c * T * E + e];
+            }
+            if (bias) v = v + bias[e];
+        }
+        zv[q] = v;
+    }
     uint32_t taken = 0;  // bit q: expert lane + 64q already picked
     float my_z = 0.0f;
     int my_e = 0;
@@ -277,12 +320,13 @@ __device__ __forceinline__ void select_token(int t, int lane, int E, int k, cons
         wts[(size_t)t * k + lane] = sum > 0.0f ? a / sum : 1.0f / (float)k;
     }
 }
-__global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, const float* __restrict__ zg,
+__global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, int nz, const float* __restrict__ zg,
+                                                      const float* __restrict__ bias,
                                                       int32_t* __restrict__ ids, float* __restrict__ wts)
 {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    select_token(t, threadIdx.x & 63, E, k, zg, ids, wts);
+    select_token(t, threadIdx.x & 63, T, E, k, nz, zg, bias, ids, wts);
 }
 
 // Hash routing: expert_j = splitmix64(id*k + j) mod E, +1 mod E past repeats.
@@ -1490,6 +1534,13 @@ __global__ __launch_bounds__(256) void k_dequant_export(int N, int K, int expert
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
+int route_splits(int T, int H, int E)
+{
+    if (T <= 0 || E % 4 != 0 || H % 256 != 0 || H <= ROUTE_CHUNK) return 1;
+    if (E % 8 == 0 && (size_t)((T + 63) / 64) * (E / 8) >= 512) return 1;   // enough chains already
+    return (H + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+}
+
 hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
                         const float* bias, int mode, const int64_t* token_ids,
                         int32_t* ids, float* w, float* z, hipStream_t s)
@@ -1501,8 +1552,13 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
     }
     // Large batches: two tokens x eight experts per lane (W reads shared by
     // the tokens, x conversions by the experts).  Small batches: one chain per
-    // lane, for as many waves as possible (each chain is H dependent fmas).
-    if (E % 4 != 0 || H % 256 != 0) {
+    // lane, one block per chunk of h (route_splits), so that the chains are
+    // ROUTE_CHUNK long and the grid holds chunks x as many waves.
+    const int nz = route_splits(T, H, E);
+    if (nz > 1) {
+        hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4, nz), dim3(256), 0, s, T, H,
+                           E, x, wr, bias, z);
+    } else if (E % 4 != 0 || H % 256 != 0) {
         hipLaunchKernelGGL(k_route_logits_any, dim3(blocks_for((size_t)T * E, 256)), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
     } else if (E % 32 == 0 && (size_t)((T + 127) / 128) * (E / 32) >= 512) {
@@ -1511,15 +1567,12 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
     } else if (E % 8 == 0 && (size_t)((T + 63) / 64) * (E / 8) >= 512) {
         hipLaunchKernelGGL((k_route_logits<1, 2, 256, true>), dim3((T + 63) / 64, E / 8), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
-    } else if (H % 512 == 0) {
-        // longer stages: the next slice's loads hide behind 512 dependent fmas
-        hipLaunchKernelGGL((k_route_logits<1, 1, 512, true>), dim3((T + 63) / 64, E / 4), dim3(256), 0, s, T, H, E, x,
-                           wr, bias, z);
     } else {
         hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
     }
-    hipLaunchKernelGGL(k_route_select, dim3(blocks_for(T, 4)), dim3(256), 0, s, T, E, k, z, ids, w);
+    hipLaunchKernelGGL(k_route_select, dim3(blocks_for(T, 4)), dim3(256), 0, s, T, E, k, nz, z,
+                       nz > 1 ? bias : nullptr, ids, w);
     return hipGetLastError();
 }
 

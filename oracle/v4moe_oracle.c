@@ -188,21 +188,32 @@ EXPORT void orc_dequant_matrix(int N, int K, const uint8_t* fp4, const uint8_t* 
 /* ------------------------------------------------------------------------ */
 
 /* Router logits z[t][e] = sum_h x[t][h] * W_r[h][e] (+ bias[e]).  Reading of
- * the unstated precision: one fp32 fused multiply-add per h, h ascending,
- * starting from +0; the bias is one fp32 add afterwards. */
+ * the unstated precision and order: h is cut into chunks of 512 (the last one
+ * shorter when 512 does not divide H); within a chunk one fp32 fused
+ * multiply-add per h, h ascending, starting from +0; the chunk sums are added
+ * in fp32 in increasing chunk order, starting from +0; the bias is one fp32
+ * add afterwards.  With H <= 512 this is the single chain over all h. */
+#define ORC_ROUTER_CHUNK 512
 EXPORT void orc_router_logits(int T, int H, int E, const uint16_t* x, const float* wr,
                               const float* bias, float* z)
 {
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
         float* zt = z + (size_t)t * E;
+        float* part = (float*)malloc((size_t)E * sizeof(float));
         for (int e = 0; e < E; e++) zt[e] = 0.0f;
-        /* h outer, e inner: each z[t][e] is still its own h-ascending chain */
-        for (int h = 0; h < H; h++) {
-            float xv = orc_bf16_value(x[(size_t)t * H + h]);
-            const float* w = wr + (size_t)h * E;
-            for (int e = 0; e < E; e++) zt[e] = fmaf(xv, w[e], zt[e]);
+        for (int h0 = 0; h0 < H; h0 += ORC_ROUTER_CHUNK) {
+            const int h1 = h0 + ORC_ROUTER_CHUNK < H ? h0 + ORC_ROUTER_CHUNK : H;
+            for (int e = 0; e < E; e++) part[e] = 0.0f;
+            /* h outer, e inner: each part[e] is still its own h-ascending chain */
+            for (int h = h0; h < h1; h++) {
+                float xv = orc_bf16_value(x[(size_t)t * H + h]);
+                const float* w = wr + (size_t)h * E;
+                for (int e = 0; e < E; e++) part[e] = fmaf(xv, w[e], part[e]);
+            }
+            for (int e = 0; e < E; e++) zt[e] = zt[e] + part[e];
         }
+        free(part);
         if (bias)
             for (int e = 0; e < E; e++) zt[e] = zt[e] + bias[e];
     }

@@ -389,11 +389,44 @@ def test_ragged_batch_invariance_and_determinism():
         assert np.array_equal(ids.cpu().numpy(), f["ids"][lo:hi])
 
 
+@pytest.mark.parametrize("T,H,E", [
+    (32, 4096, 256),    # one block per 512-h chunk (the decode router)
+    (128, 1280, 256),   # the same with a ragged last chunk
+    (1024, 1536, 256),  # one token per lane, chunks folded in the block
+    (8192, 1280, 256),  # two tokens x eight experts per lane
+    (50, 1280, 6),      # the generic router
+])
+def test_routing_chunk_fold_order(T, H, E):
+    """Every router variant sums the logits as the fold of 512-h chains: with
+    x = 1, expert 1 holds 2^24 at h = 0 and 1 at h = 512 and 513 (2^24 + 2 as
+    chunk sums; 2^24 as one chain, 2^24 + 1 rounding to even) and expert 0
+    holds 2^24 alone, so expert 1 ranks first only under the fold."""
+    x = inputs.to_bf16_bits(np.ones((T, H), np.float32))
+    wr = np.zeros((H, E), np.float32)
+    wr[0, 0] = wr[0, 1] = 2.0 ** 24
+    wr[512, 1] = wr[513, 1] = 1.0
+    ids_ref, w_ref = oracle.route(x, wr, 2)
+    assert np.all(ids_ref[:, 0] == 1) and np.all(ids_ref[:, 1] == 0)
+    d = v4moe.dims(T, H, 128, E, 2)
+    ids = torch.empty((T, 2), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, 2), dtype=torch.float32, device=DEV)
+    ws = torch.empty(v4moe.moe_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    v4moe.moe_route(d, torch.from_numpy(x.view(np.int16)).to(DEV), torch.from_numpy(wr).to(DEV), None, 0, None,
+                    ids, w, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=1e-6, atol=0)
+
+
 @pytest.mark.parametrize("T,H,E,k", [
     (32, 256, 8, 3),        # small-batch router
     (50, 256, 6, 2),        # E % 4 != 0: the generic router
     (4096, 512, 256, 8),    # one token per lane, two experts per lane
     (8192, 256, 256, 8),    # two tokens x eight experts per lane
+    (32, 1280, 8, 3),       # one block per 512-h chunk, ragged last chunk
+    (1024, 1536, 256, 8),   # one token per lane, chunks folded in the block
+    (8192, 1280, 256, 8),   # two tokens x eight experts per lane, ragged last chunk
+    (50, 768, 6, 2),        # the generic router over two chunks
 ])
 def test_routing_exact_ties(T, H, E, k):
     """Logits that collide exactly (x in {-1, 0, 1}, W_r columns drawn from

@@ -123,6 +123,37 @@ def test_logits_sequential_fma_order():
     assert zb[0, 0] == np.float32(0.25) and zb[0, 1] == np.float32(2.5)
 
 
+def test_logits_chunked_fold_order():
+    """Past 512 h the sum is a fold of 512-h chains: with 2^24 at h = 0 and 1 at
+    h = 512 and h = 513, one chain loses both ones (2^24 + 1 rounds to 2^24),
+    while chunk sums 2^24 and 2 add exactly to 2^24 + 2.  A ragged last chunk
+    (H = 640) is a chain of its own, and a 2^24 + 1 inside one chunk is still
+    lost.  Error bound of the fold: gamma_(512 + chunks) times the sum of
+    |products|, checked against exact sums on random data with H = 1536."""
+    for H in (1024, 640):
+        x = bf16_bits(np.ones((1, H), np.float32))
+        wr = np.zeros((H, 2), np.float32)
+        wr[0, 0], wr[512, 0], wr[513, 0] = 2.0 ** 24, 1.0, 1.0
+        wr[0, 1], wr[1, 1], wr[600, 1] = 2.0 ** 24, 1.0, -(2.0 ** 24)
+        z = oracle.router_logits(x, wr)
+        assert z[0, 0] == np.float32(2.0 ** 24 + 2)
+        assert z[0, 1] == 0.0
+    rng = np.random.default_rng(7)
+    H, E = 1536, 8
+    xf = rng.standard_normal((3, H)).astype(np.float32)
+    x = bf16_bits(xf)
+    wr = rng.standard_normal((H, E)).astype(np.float32)
+    z = oracle.router_logits(x, wr)
+    xv = bf16_vals(x).astype(np.float64)
+    u = 2.0 ** -24
+    n = 512 + 3
+    gamma = n * u / (1 - n * u)
+    for t in range(3):
+        for e in range(E):
+            prods = xv[t] * wr[:, e].astype(np.float64)
+            assert abs(float(z[t, e]) - math.fsum(prods)) <= gamma * np.abs(prods).sum()
+
+
 def test_splitmix64_published_output():
     g = json.load(open(os.path.join(GOLD, "splitmix64.json")))
     gamma = int(g["golden_gamma"], 16)
