@@ -1551,11 +1551,14 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
         return hipGetLastError();
     }
     // Large batches: two tokens x eight experts per lane (W reads shared by
-    // the tokens, x conversions by the experts).  Small batches: one chain per
-    // lane, one block per chunk of h (route_splits), so that the chains are
-    // ROUTE_CHUNK long and the grid holds chunks x as many waves.
+    // the tokens, x conversions by the experts).  Small batches: one token x
+    // four experts per lane, one block per chunk of h (route_splits), so that
+    // the chains are ROUTE_CHUNK long and the grid holds chunks x as many waves.
     const int nz = route_splits(T, H, E);
-    if (nz > 1) {
+    if (nz > 1 && E % 16 == 0) {   // four experts per wave (eight spill)
+        hipLaunchKernelGGL((k_route_logits<1, 4, 256, true>), dim3((T + 63) / 64, E / 16, nz), dim3(256), 0, s, T, H,
+                           E, x, wr, bias, z);
+    } else if (nz > 1) {
         hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4, nz), dim3(256), 0, s, T, H,
                            E, x, wr, bias, z);
     } else if (E % 4 != 0 || H % 256 != 0) {
