@@ -283,7 +283,15 @@ __device__ __forceinline__ void select_token(int t, int lane, int T, int E, int 
             if (nz == 1) {
                 v = z[e];
             } else {
-                for (int c = 0; c < nz; c++) v = v + z[(size_t)c * T * E + e];
+                // eight chunk loads in flight, then their fold in chunk order
+                for (int c0 = 0; c0 < nz; c0 += 8) {
+                    float p[8];
+#pragma unroll
+                    for (int u = 0; u < 8; u++) p[u] = c0 + u < nz ? z[(size_t)(c0 + u) * T * E + e] : 0.0f;
+#pragma unroll
+                    for (int u = 0; u < 8; u++)
+                        if (c0 + u < nz) v = v + p[u];
+                }
             }
             if (bias) v = v + bias[e];
         }
