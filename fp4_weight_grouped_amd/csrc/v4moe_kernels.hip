@@ -264,6 +264,46 @@ __global__ __launch_bounds__(256) void k_route_logits_any(int T, int H, int E, c
     z[i] = tot;
 }
 
+// Order-preserving map of fp32 bits to uint32 (finite values; -0 below +0,
+// which the logits never hold: their sums start from +0) and its inverse.
+__device__ __forceinline__ uint32_t float_order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_from_order_key(uint32_t u)
+{
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+// One DPP move of a 64-bit value (both halves with the same lane pattern).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Maximum of a 64-bit key over the whole wave (every lane active), returned to
+// every lane: within each 16-lane row by DPP (quad xor 1, quad xor 2, half-row
+// mirror, row mirror), then across the four rows by reading lanes 0/16/32/48.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
+{
+    uint64_t o;
+    o = dpp_u64<0xB1>(v);  v = o > v ? o : v;    // quad_perm [1,0,3,2]
+    o = dpp_u64<0x4E>(v);  v = o > v ? o : v;    // quad_perm [2,3,0,1]
+    o = dpp_u64<0x141>(v); v = o > v ? o : v;    // row_half_mirror
+    o = dpp_u64<0x140>(v); v = o > v ? o : v;    // row_mirror
+    uint64_t r = 0;
+#pragma unroll
+    for (int row = 0; row < 4; row++) {
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
+        const uint64_t w = ((uint64_t)hi << 32) | lo;
+        r = w > r ? w : r;
+    }
+    return r;
+}
+
 // Top-k per token (one wave per token): the k largest logits, the lower expert
 // id winning ties, slot j = j-th pick; then lanes 0..k-1 compute the affinity
 // sqrt(softplus(z)) and the weights normalised over the k picks.  The logits
@@ -301,21 +341,20 @@ __device__ __forceinline__ void select_token(int t, int lane, int T, int E, int 
     float my_z = 0.0f;
     int my_e = 0;
     for (int j = 0; j < k; j++) {
-        float bv = 0.0f;
-        int be = INT_MAX;
+        // key = order-preserving bits of z above the complemented id: the
+        // largest key is the largest z, the lower id on equal z; 0 = none
+        uint64_t key = 0;
 #pragma unroll
         for (int q = 0; q < 16; q++) {
             const int e = lane + 64 * q;
             if (q * 64 < E && e < E && !((taken >> q) & 1u)) {
-                if (be == INT_MAX || zv[q] > bv) { bv = zv[q]; be = e; }
+                const uint64_t c = ((uint64_t)float_order_key(zv[q]) << 32) | (uint32_t)~e;
+                key = c > key ? c : key;
             }
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oe = __shfl_xor(be, off);
-            const bool better = oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be));
-            if (better) { bv = ov; be = oe; }
-        }
+        key = wave_max_key(key);
+        const int be = (int)~(uint32_t)key;
+        const float bv = float_from_order_key((uint32_t)(key >> 32));
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
         if (lane == j) { my_z = bv; my_e = be; }
     }
