@@ -22,7 +22,8 @@
  *
  * Pins (tests under tests/ check each function against something other than
  * itself): formats against exhaustive enumeration and torch's casts; top-k
- * against brute force; logits against an exact-rational error bound; the
+ * against brute force; logits against an exact-rational error bound and
+ * closed forms that fix the chunked summation order; the
  * permutation against a stable library sort; the FFN against a closed form
  * and against a dense matmul formulation.  No function here is parity-unpinned.
  */
