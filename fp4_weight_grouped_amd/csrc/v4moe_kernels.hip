@@ -1602,8 +1602,8 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
     // four experts per lane, one block per chunk of h (route_splits), so that
     // the chains are ROUTE_CHUNK long and the grid holds chunks x as many waves.
     const int nz = route_splits(T, H, E);
-    if (nz > 1 && E % 16 == 0) {   // four experts per wave (eight spill)
-        hipLaunchKernelGGL((k_route_logits<1, 4, 256, true>), dim3((T + 63) / 64, E / 16, nz), dim3(256), 0, s, T, H,
+    if (nz > 1 && E % 16 == 0) {   // four experts per wave (eight spill), 128-h stages
+        hipLaunchKernelGGL((k_route_logits<1, 4, 128, true>), dim3((T + 63) / 64, E / 16, nz), dim3(256), 0, s, T, H,
                            E, x, wr, bias, z);
     } else if (nz > 1) {
         hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4, nz), dim3(256), 0, s, T, H,
