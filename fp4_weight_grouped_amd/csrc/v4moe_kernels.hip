@@ -1584,7 +1584,10 @@ static inline unsigned blocks_for(size_t n, int per) { return (unsigned)((n + pe
 int route_splits(int T, int H, int E)
 {
     if (T <= 0 || E % 4 != 0 || H % 256 != 0 || H <= ROUTE_CHUNK) return 1;
-    if (E % 8 == 0 && (size_t)((T + 63) / 64) * (E / 8) >= 512) return 1;   // enough chains already
+    // two tokens x eight experts per lane fill the chip with full-length chains
+    if (E % 32 == 0 && (size_t)((T + 127) / 128) * (E / 32) >= 512) return 1;
+    // without four experts per wave: one token x two experts per lane
+    if (E % 16 != 0 && E % 8 == 0 && (size_t)((T + 63) / 64) * (E / 8) >= 512) return 1;
     return (H + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
 }
 
