@@ -23,7 +23,7 @@
  * Pins (tests under tests/ check each function against something other than
  * itself): formats against exhaustive enumeration and torch's casts; top-k
  * against brute force; logits against an exact-rational error bound and
- * closed forms that fix the chunked summation order; the
+ * closed forms that fix the summation order (one h-ascending chain); the
  * permutation against a stable library sort; the FFN against a closed form
  * and against a dense matmul formulation.  No function here is parity-unpinned.
  */
@@ -188,33 +188,23 @@ EXPORT void orc_dequant_matrix(int N, int K, const uint8_t* fp4, const uint8_t* 
 /* Routing (P2 DeepSeekMoE notes: sqrt(softplus) affinity, hash routing)     */
 /* ------------------------------------------------------------------------ */
 
-/* Router logits z[t][e] = sum_h x[t][h] * W_r[h][e] (+ bias[e]).  Reading of
- * the unstated precision and order: h is cut into chunks of 512 (the last one
- * shorter when 512 does not divide H); within a chunk one fp32 fused
- * multiply-add per h, h ascending, starting from +0; the chunk sums are added
- * in fp32 in increasing chunk order, starting from +0; the bias is one fp32
- * add afterwards.  With H <= 512 this is the single chain over all h. */
-#define ORC_ROUTER_CHUNK 512
+/* Router logits z[t][e] = sum_h x[t][h] * W_r[h][e] (+ bias[e]) (P2,
+ * DeepSeekMoE notes: the affinity is taken of this logit).  Reading of the
+ * unstated precision and order: one fp32 fused multiply-add per h, h
+ * ascending, starting from +0; the bias is one fp32 add afterwards. */
 EXPORT void orc_router_logits(int T, int H, int E, const uint16_t* x, const float* wr,
                               const float* bias, float* z)
 {
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
         float* zt = z + (size_t)t * E;
-        float* part = (float*)malloc((size_t)E * sizeof(float));
         for (int e = 0; e < E; e++) zt[e] = 0.0f;
-        for (int h0 = 0; h0 < H; h0 += ORC_ROUTER_CHUNK) {
-            const int h1 = h0 + ORC_ROUTER_CHUNK < H ? h0 + ORC_ROUTER_CHUNK : H;
-            for (int e = 0; e < E; e++) part[e] = 0.0f;
-            /* h outer, e inner: each part[e] is still its own h-ascending chain */
-            for (int h = h0; h < h1; h++) {
-                float xv = orc_bf16_value(x[(size_t)t * H + h]);
-                const float* w = wr + (size_t)h * E;
-                for (int e = 0; e < E; e++) part[e] = fmaf(xv, w[e], part[e]);
-            }
-            for (int e = 0; e < E; e++) zt[e] = zt[e] + part[e];
+        /* h outer, e inner: each z[t][e] is still its own h-ascending chain */
+        for (int h = 0; h < H; h++) {
+            float xv = orc_bf16_value(x[(size_t)t * H + h]);
+            const float* w = wr + (size_t)h * E;
+            for (int e = 0; e < E; e++) zt[e] = fmaf(xv, w[e], zt[e]);
         }
-        free(part);
         if (bias)
             for (int e = 0; e < E; e++) zt[e] = zt[e] + bias[e];
     }
@@ -589,10 +579,24 @@ EXPORT int orc_layer_forward(int T, int H, int I, int E, int k, int act,
     uint16_t* ybuf = (uint16_t*)malloc((size_t)(P > 0 ? P : 1) * H * sizeof(uint16_t));
     double* yex = out_exact ? (double*)malloc((size_t)(P > 0 ? P : 1) * H * sizeof(double)) : NULL;
 
+    /* Experts with at least one wanted row.  Every pair's result depends only
+     * on its own token and expert, so the order in which experts and pairs
+     * are visited changes nothing: with fewer wanted pairs per expert than
+     * threads the experts are spread over the threads (one at a time per
+     * thread), otherwise the pairs of one expert are. */
+    int* todo = (int*)malloc((size_t)E * sizeof(int));
+    int ntodo = 0, npairs = 0;
     for (int e = 0; e < E; e++) {
-        int lo = offsets[e], hi = offsets[e + 1], need = 0;
-        for (int r = lo; r < hi; r++) need |= want[sorted_pair[r] / k];
-        if (!need) continue;
+        int need = 0;
+        for (int r = offsets[e]; r < offsets[e + 1]; r++) need += want[sorted_pair[r] / k];
+        if (need) todo[ntodo++] = e;
+        npairs += need;
+    }
+    const int by_expert = ntodo > 1 && npairs < ntodo * orc_num_threads();
+#pragma omp parallel for schedule(dynamic, 1) if (by_expert)
+    for (int i = 0; i < ntodo; i++) {
+        const int e = todo[i];
+        int lo = offsets[e], hi = offsets[e + 1];
         int_matrix mg = {0}, mu, md;
         size_t so = (size_t)e;
         if (act == ORC_ACT_SWIGLU)
@@ -602,7 +606,7 @@ EXPORT int orc_layer_forward(int T, int H, int I, int E, int k, int act,
                         W->blk[1] + so * (I / 128) * (H / 128));
         make_int_matrix(&md, H, I, W->fp4[2] + so * H * (I / 2), W->e8m0[2] + so * H * (I / 32),
                         W->blk[2] + so * (H / 128) * (I / 128));
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) if (!by_expert)
         for (int r = lo; r < hi; r++) {
             int p = sorted_pair[r], t = p / k;
             if (!want[t]) continue;
@@ -611,6 +615,7 @@ EXPORT int orc_layer_forward(int T, int H, int I, int E, int k, int act,
         }
         free(mg.wint); free(mu.wint); free(md.wint);
     }
+    free(todo);
 
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {

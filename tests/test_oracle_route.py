@@ -123,31 +123,34 @@ def test_logits_sequential_fma_order():
     assert zb[0, 0] == np.float32(0.25) and zb[0, 1] == np.float32(2.5)
 
 
-def test_logits_chunked_fold_order():
-    """Past 512 h the sum is a fold of 512-h chains: with 2^24 at h = 0 and 1 at
-    h = 512 and h = 513, one chain loses both ones (2^24 + 1 rounds to 2^24),
-    while chunk sums 2^24 and 2 add exactly to 2^24 + 2.  A ragged last chunk
-    (H = 640) is a chain of its own, and a 2^24 + 1 inside one chunk is still
-    lost.  Error bound of the fold: gamma_(512 + chunks) times the sum of
-    |products|, checked against exact sums on random data with H = 1536."""
-    for H in (1024, 640):
+def test_logits_single_chain_order():
+    """One h-ascending chain over all of H, however long.  With x = 1:
+    expert 0 holds 2^24 at h = 0 and 1 at h = 512 and h = 513: every partial
+    sum 2^24 + 1 rounds (to even) back to 2^24, so the chain gives 2^24, where
+    any split of h into blocks of 512 or fewer summed separately gives 2^24 + 2;
+    expert 1 holds 2^24 at h = 0, 1 at h = 1 .. H-2 and -2^24 at h = H-1: the
+    chain loses every 1 and ends at 0, while an order that adds the ones
+    first gives H - 2; expert 2 holds 1 everywhere (every partial sum exact),
+    so its logit is H.  Error bound gamma_H * sum |x_h w_h| against exact sums
+    at H = 4096 on random data."""
+    for H in (1024, 640, 4096):
         x = bf16_bits(np.ones((1, H), np.float32))
-        wr = np.zeros((H, 2), np.float32)
+        wr = np.zeros((H, 3), np.float32)
         wr[0, 0], wr[512, 0], wr[513, 0] = 2.0 ** 24, 1.0, 1.0
-        wr[0, 1], wr[1, 1], wr[600, 1] = 2.0 ** 24, 1.0, -(2.0 ** 24)
+        wr[0, 1], wr[1:H - 1, 1], wr[H - 1, 1] = 2.0 ** 24, 1.0, -(2.0 ** 24)
+        wr[:, 2] = 1.0
         z = oracle.router_logits(x, wr)
-        assert z[0, 0] == np.float32(2.0 ** 24 + 2)
+        assert z[0, 0] == np.float32(2.0 ** 24)
         assert z[0, 1] == 0.0
+        assert z[0, 2] == np.float32(H)
     rng = np.random.default_rng(7)
-    H, E = 1536, 8
-    xf = rng.standard_normal((3, H)).astype(np.float32)
-    x = bf16_bits(xf)
+    H, E = 4096, 8
+    x = bf16_bits(rng.standard_normal((3, H)).astype(np.float32))
     wr = rng.standard_normal((H, E)).astype(np.float32)
     z = oracle.router_logits(x, wr)
     xv = bf16_vals(x).astype(np.float64)
     u = 2.0 ** -24
-    n = 512 + 3
-    gamma = n * u / (1 - n * u)
+    gamma = H * u / (1 - H * u)
     for t in range(3):
         for e in range(E):
             prods = xv[t] * wr[:, e].astype(np.float64)
@@ -180,6 +183,37 @@ def test_hash_routing():
     # k = E: every expert exactly once
     ids, w = oracle.route(x[:5], wr, E, mode=1)
     assert all(sorted(r.tolist()) == list(range(E)) for r in ids)
+
+
+def _hash_ids(token_id, k, E):
+    x = bf16_bits(np.zeros((1, 128), np.float32))
+    ids, w = oracle.route(x, np.zeros((128, E), np.float32), k, mode=1,
+                          token_ids=np.array([token_id], np.int64))
+    assert np.all(w == np.float32(1.0 / k))
+    return ids[0].tolist()
+
+
+def test_hash_collision_probe_steps_up():
+    """A raw hash that repeats an earlier pick moves to the next free expert id
+    going up, wrapping from E-1 to 0 (P2's hash routing needs k distinct
+    experts; the probe direction is the stated reading).  Raw hashes
+    splitmix64(id*k + j) mod E are checked against the pinned generator, then
+    the stored ids against sequences worked out by hand from them:
+      E=16, k=4, id 17: raw 10 7 15 15 -> 15 taken, 15+1 wraps to 0;
+      E=16, k=4, id 47: raw 6 1 5 5 -> 5 taken, 6 taken, 7;
+      E=8,  k=8, id 0:  raw 7 1 6 5 2 2 0 7 -> slot 5: 2 taken, 3;
+                        slot 7: 7, 0, 1, 2, 3 taken, 4.
+    A probe stepping down (15 -> 14, 5 -> 4) or re-hashing gives other ids."""
+    cases = [
+        (17, 4, 16, [10, 7, 15, 15], [10, 7, 15, 0]),
+        (47, 4, 16, [6, 1, 5, 5], [6, 1, 5, 7]),
+        (0, 8, 8, [7, 1, 6, 5, 2, 2, 0, 7], [7, 1, 6, 5, 2, 3, 0, 4]),
+    ]
+    for tid, k, E, raw, want in cases:
+        assert [oracle.splitmix64(tid * k + j) % E for j in range(k)] == raw
+        assert _hash_ids(tid, k, E) == want, (tid, k, E)
+    # k = E: the hand-worked sequence is a permutation of all experts
+    assert sorted(cases[2][4]) == list(range(8))
 
 
 def test_permutation_matches_stable_sort():
