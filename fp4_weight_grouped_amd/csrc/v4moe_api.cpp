@@ -96,7 +96,7 @@ Layout layout(const v4moe_dims* d)
     const size_t NB1 = nb1(d, L.CW), NB2 = H / (128 * L.CW);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
-    L.z = take(T * E * 4 * (size_t)route_splits(d->T, d->H, d->E));
+    L.z = take(T * E * 4);
     L.xq = take(T * H);
     L.xs = take(T * (H / 128) * 4);
     L.sorted_pair = take(P * 4);

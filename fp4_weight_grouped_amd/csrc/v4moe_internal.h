@@ -43,9 +43,6 @@ struct FfnArgs {
     float* u_out;              // optional [T*topk][I]: linear1 up outputs, or null
 };
 
-// Number of [T][E] fp32 arrays of router chunk sums launch_route writes to z:
-// 1 (z holds the logits) or the number of h chunks (small batches).
-int route_splits(int T, int H, int E);
 hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
                         const float* bias, int mode, const int64_t* token_ids,
                         int32_t* ids, float* w, float* z, hipStream_t s);

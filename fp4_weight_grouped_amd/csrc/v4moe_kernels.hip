@@ -53,25 +53,31 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
                  :: "v"(g), "s"(lds_base) : "memory", "m0");
 }
 
-// Router logits.  h is cut into chunks of ROUTE_CHUNK (the last one shorter
-// when it does not divide H); a logit is the fp32 sum, in increasing chunk
-// order from +0, of one fp32 fma chain per chunk (h increasing, from +0); the
-// optional bias is one fp32 add afterwards.  Block = 4 waves, 64*TS tokens x
-// 4*ES experts: lane l runs the chains of tokens t0 + l + 64*i (i < TS) for
-// the ES experts of its wave, TS*ES independent chains at a time.  With
-// gridDim.z == 1 a block folds all chunks itself and writes z (+ bias); with
-// gridDim.z == the number of chunks, block z runs chunk z only and writes its
-// chain sums, without bias, to z + blockIdx.z*T*E for the select kernel to
-// fold (more, shorter chains for batches too small to fill the chip).  The block's slice of W_r is
-// staged through LDS HC rows at a time, transposed to expert-major rows (padded
-// by 4 floats against bank conflicts), so one broadcast LDS read gives four
-// consecutive h of one expert; the next slice is loaded into registers while
-// the current one is used.  With XL the tokens' x rows are staged too, by
-// direct-to-LDS loads issued a stage ahead (rows padded by 16 bytes), for
-// batches too small to hide global-load latency behind a lane's few chains;
-// otherwise each lane reads its x rows from global memory one step ahead.
-// z is [T][E].  Needs E % (4*ES) == 0, H % HC == 0 and ROUTE_CHUNK % HC == 0.
-constexpr int ROUTE_CHUNK = 512;
+// A value known to be equal in every lane, moved to scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uniform(T* p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+// Router logits, every variant: z[t][e] is one fp32 fma chain over h
+// ascending from +0 (x exact as float), plus the optional bias as one fp32 add
+// afterwards.  The variants differ only in which chains a lane runs and how the
+// operands reach it.
+//
+// k_route_logits: lane = TS tokens x ES experts of independent chains (tokens
+// t0 + l + 64*i, i < TS; the ES experts of its wave).  Block = 4 waves, 64*TS
+// tokens x 4*ES experts.  The block's slice of W_r is staged through LDS HC
+// rows at a time, transposed to expert-major rows (padded by 4 floats against
+// bank conflicts), so one broadcast LDS read gives four consecutive h of one
+// expert; the next slice is loaded into registers while the current one is
+// used.  With XL the tokens' x rows are staged too, by direct-to-LDS loads
+// issued a stage ahead (rows padded by 16 bytes); otherwise each lane reads its
+// x rows from global memory one step ahead.  z is [T][E].  Needs E % (4*ES) ==
+// 0 and H % HC == 0.
 template <int TS, int ES, int HC, bool XL>
 __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
                                                       const uint16_t* __restrict__ x,
@@ -92,12 +98,7 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t0 = blockIdx.x * 64 * TS;
     const int eb0 = blockIdx.y * EB;
-    static_assert(ROUTE_CHUNK % HC == 0, "a stage never straddles a chunk");
-    constexpr int SPC = ROUTE_CHUNK / HC;    // stages per chunk
     const int nst = H / HC;
-    // stages [s0, s1) of this block: all, or those of chunk blockIdx.z
-    const int s0 = gridDim.z == 1 ? 0 : blockIdx.z * SPC;
-    const int s1 = gridDim.z == 1 ? nst : min(s0 + SPC, nst);
 
     // staging: float4 f of the [HC][EB] slice = row f / (EB/4), experts 4*(f % (EB/4)) .. +3;
     // uint4 g of the x slice = token row g / (HC/8), 8 h at column g % (HC/8)
@@ -139,20 +140,20 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
             }
         }
     };
-    dma_x(s0, s0 & 1);
-    load_stage(s0);
-    store_stage(s0 & 1);
+    dma_x(0, 0);
+    load_stage(0);
+    store_stage(0);
     wait_vm<0>();
     __syncthreads();
 
     const uint4* xp[TS];
 #pragma unroll
     for (int i = 0; i < TS; i++) xp[i] = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + lane + 64 * i, T - 1) * H);
-    float acc[TS][ES], tot[TS][ES];
+    float acc[TS][ES];
 #pragma unroll
     for (int i = 0; i < TS; i++)
 #pragma unroll
-        for (int j = 0; j < ES; j++) acc[i][j] = tot[i][j] = 0.0f;
+        for (int j = 0; j < ES; j++) acc[i][j] = 0.0f;
 
     // x of 8 consecutive h of token i, for the step starting at stage-relative h
     auto xload = [&](int s, int i, int h) -> uint4 {
@@ -160,8 +161,8 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
         const int g = s * HC + h;
         return xp[i][(g < H ? g : H - 8) / 8];
     };
-    for (int s = s0; s < s1; s++) {
-        if (s + 1 < s1) {
+    for (int s = 0; s < nst; s++) {
+        if (s + 1 < nst) {
             dma_x(s + 1, (s + 1) & 1);
             load_stage(s + 1);
         }
@@ -215,20 +216,10 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
 #pragma unroll
                 for (int v = 0; v < HS / 8; v++) xc[i][v] = xn[i][v];
         }
-        if ((s + 1) % SPC == 0 || s + 1 == nst) {   // end of a chunk: fold its chain sums
-#pragma unroll
-            for (int i = 0; i < TS; i++)
-#pragma unroll
-                for (int j = 0; j < ES; j++) {
-                    tot[i][j] = tot[i][j] + acc[i][j];
-                    acc[i][j] = 0.0f;
-                }
-        }
-        if (s + 1 < s1) store_stage((s + 1) & 1);
+        if (s + 1 < nst) store_stage((s + 1) & 1);
         if (XL) wait_vm<0>();
         __syncthreads();
     }
-    float* zo = z + (size_t)blockIdx.z * T * E;
 #pragma unroll
     for (int i = 0; i < TS; i++) {
         const int t = t0 + lane + 64 * i;
@@ -236,12 +227,134 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
 #pragma unroll
             for (int j = 0; j < ES; j++) {
                 const int e = eb0 + w * ES + j;
-                float v = tot[i][j];
-                if (bias && gridDim.z == 1) v = v + bias[e];
-                zo[(size_t)t * E + e] = v;
+                float v = acc[i][j];
+                if (bias) v = v + bias[e];
+                z[(size_t)t * E + e] = v;
             }
         }
     }
+}
+
+// k_route_lane: for batches too small to fill the chip with several chains
+// per lane, where a 4096-long chain is latency-bound (a dependent fp32 fma
+// takes about 1.5 issue slots) and the time goes to getting operands to it.
+// Lane = one chain: wave = EL experts x 64/EL tokens; block = NTW such waves
+// plus one producer wave.  The producer issues every global load of the block
+// as a direct-to-LDS load NS-1 stages of RH rows ahead (the W_r slice, rows
+// of EL experts, natural [h][e] layout; the block's x rows as bf16), waits for
+// a stage's loads, converts its x to fp32 in LDS and releases the stage with
+// one barrier.  The consumer waves do nothing but the chain: per step of 16 h
+// they read 16 W values (lanes of one expert share each read) and four fp32
+// x values per token (lanes of one token share those), the reads of the next
+// step issued before the fmas of the current one.  Small EL keeps the W slice
+// a block streams through its CU small.  Needs E % 4 == 0 and H % RH == 0;
+// lanes past E read clamped columns and store nothing.
+template <int EL, int NTW, int RH, int NS>
+__global__ __launch_bounds__(64 * (NTW + 1)) void k_route_lane(int T, int H, int E, const uint16_t* __restrict__ x,
+                                                             const float* __restrict__ wr,
+                                                             const float* __restrict__ bias, float* __restrict__ z)
+{
+    constexpr int TPW = 64 / EL;                 // tokens per consumer wave
+    constexpr int NTOK = NTW * TPW;              // tokens per block
+    constexpr int SPR = EL / 4;                  // 16-byte segments per W row
+    constexpr int RPD = 64 / SPR;                // W rows per 1 KiB load
+    constexpr int WD = RH / RPD;                 // W loads per stage
+    constexpr int XSEG = RH / 8;                 // 16-byte x segments per token row per stage
+    constexpr int XD = (NTOK * XSEG + 63) / 64;  // x loads per stage
+    constexpr int OPS = WD + XD;                 // producer loads per stage
+    constexpr int HS = 16;                       // h per consumer step
+    static_assert(EL % 4 == 0 && 64 % EL == 0 && RH % RPD == 0 && RH % (2 * HS) == 0, "stage shape");
+    static_assert(NS >= 2 && NS <= 4 && OPS * (NS - 2) < 64, "loads in flight fit the counter");
+    __shared__ __align__(16) float wl[NS][RH * EL];
+    __shared__ __align__(16) uint4 xst[NS][XD * 64];
+    __shared__ __align__(16) float xf[NS][NTOK][RH];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = uniform(tid >> 6);
+    const int neg = (E + EL - 1) / EL;
+    const int eg = blockIdx.x % neg, tg = blockIdx.x / neg;
+    const int e0 = eg * EL, t0 = tg * NTOK;
+    const int nst = H / RH;
+
+    if (w == NTW) {
+        // ---- producer ----
+        const int ccol = min(e0 + 4 * (lane % SPR), E - 4);
+        auto issue = [&](int st) {
+            const int slot = st % NS;
+            const uint32_t wbase = (uint32_t)(uintptr_t)&wl[slot][0];
+#pragma unroll
+            for (int k = 0; k < WD; k++)   // rows k*RPD + lane/SPR
+                dma16(wr + (size_t)(st * RH + k * RPD + lane / SPR) * E + ccol, uniform((int)(wbase + k * 1024)));
+            const uint32_t xbase = (uint32_t)(uintptr_t)&xst[slot][0];
+#pragma unroll
+            for (int k = 0; k < XD; k++) { // segment g: token g / XSEG (the last one repeated past the end)
+                const int g = min(64 * k + lane, NTOK * XSEG - 1);
+                const int t = min(t0 + g / XSEG, T - 1);
+                dma16(x + (size_t)t * H + st * RH + (g % XSEG) * 8, uniform((int)(xbase + k * 1024)));
+            }
+        };
+        for (int u = 0; u < NS - 1; u++)
+            if (u < nst) issue(u);
+        for (int s = 0; s < nst; s++) {
+            // stage s has landed; later stages may still be in flight
+            constexpr int A2 = NS - 2 >= 2 ? 2 * OPS : 0;
+            const int ahead = min(NS - 2, nst - 1 - s);
+            if (ahead >= 2) wait_vm<A2>(); else if (ahead == 1) wait_vm<OPS>(); else wait_vm<0>();
+            const int slot = s % NS;
+            for (int g = lane; g < NTOK * XSEG; g += 64) {
+                const uint4 q = xst[slot][g];
+                float* d = &xf[slot][g / XSEG][(g % XSEG) * 8];
+                *reinterpret_cast<float4*>(d) = make_float4(bf16_to_f32(q.x & 0xFFFFu), bf16_to_f32(q.x >> 16),
+                                                            bf16_to_f32(q.y & 0xFFFFu), bf16_to_f32(q.y >> 16));
+                *reinterpret_cast<float4*>(d + 4) = make_float4(bf16_to_f32(q.z & 0xFFFFu), bf16_to_f32(q.z >> 16),
+                                                                bf16_to_f32(q.w & 0xFFFFu), bf16_to_f32(q.w >> 16));
+            }
+            __syncthreads();
+            // slot (s-1) % NS is free: every consumer finished stage s-1 before this barrier
+            if (s + NS - 1 < nst) issue(s + NS - 1);
+        }
+        return;
+    }
+    // ---- consumers: one barrier per stage, the producer's matching one ----
+    const int el = lane % EL, tl = lane / EL;
+    float acc = 0.0f;
+    for (int s = 0; s < nst; s++) {
+        __syncthreads();
+        const int slot = s % NS;
+        const float* wb = &wl[slot][el];
+        const float* xb = &xf[slot][w * TPW + tl][0];
+        // two register sets in turn: the reads of the next step are issued
+        // before the fmas of the current one, with no register copies
+        float wA[HS], wB[HS];
+        float4 xA[HS / 4], xB[HS / 4];
+        auto ld = [&](float (&wv)[HS], float4 (&xv)[HS / 4], int h) {
+#pragma unroll
+            for (int u = 0; u < HS; u++) wv[u] = wb[(h + u) * EL];
+#pragma unroll
+            for (int v = 0; v < HS / 4; v++) xv[v] = *reinterpret_cast<const float4*>(xb + h + 4 * v);
+        };
+        auto mac = [&](const float (&wv)[HS], const float4 (&xv)[HS / 4]) {
+#pragma unroll
+            for (int v = 0; v < HS / 4; v++) {
+                acc = __builtin_fmaf(xv[v].x, wv[4 * v + 0], acc);
+                acc = __builtin_fmaf(xv[v].y, wv[4 * v + 1], acc);
+                acc = __builtin_fmaf(xv[v].z, wv[4 * v + 2], acc);
+                acc = __builtin_fmaf(xv[v].w, wv[4 * v + 3], acc);
+            }
+            // the step's chain is complete here: later reads are not hoisted
+            // above it, nor its fmas sunk below them
+            asm volatile("" : "+v"(acc)::"memory");
+        };
+        ld(wA, xA, 0);
+#pragma unroll
+        for (int h = 0; h < RH; h += 2 * HS) {
+            ld(wB, xB, h + HS);
+            mac(wA, xA);
+            if (h + 2 * HS < RH) ld(wA, xA, h + 2 * HS);
+            mac(wB, xB);
+        }
+    }
+    const int e = e0 + el, t = t0 + w * TPW + tl;
+    if (e < E && t < T) z[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
 }
 
 // The same logits for any E: one thread per (token, expert).
@@ -252,16 +365,10 @@ __global__ __launch_bounds__(256) void k_route_logits_any(int T, int H, int E, c
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (size_t)T * E) return;
     const int t = (int)(i / E), e = (int)(i % E);
-    float tot = 0.0f;
-    for (int h0 = 0; h0 < H; h0 += ROUTE_CHUNK) {
-        const int h1 = min(h0 + ROUTE_CHUNK, H);
-        float acc = 0.0f;
-        for (int h = h0; h < h1; h++)
-            acc = __builtin_fmaf(bf16_to_f32(x[(size_t)t * H + h]), wr[(size_t)h * E + e], acc);
-        tot = tot + acc;
-    }
-    if (bias) tot = tot + bias[e];
-    z[i] = tot;
+    float acc = 0.0f;
+    for (int h = 0; h < H; h++) acc = __builtin_fmaf(bf16_to_f32(x[(size_t)t * H + h]), wr[(size_t)h * E + e], acc);
+    if (bias) acc = acc + bias[e];
+    z[i] = acc;
 }
 
 // Order-preserving map of fp32 bits to uint32 (finite values; -0 below +0,
@@ -306,11 +413,8 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
 
 // Top-k per token (one wave per token): the k largest logits, the lower expert
 // id winning ties, slot j = j-th pick; then lanes 0..k-1 compute the affinity
-// sqrt(softplus(z)) and the weights normalised over the k picks.  The logits
-// are the fp32 sum, in order from +0, of nz arrays [T][E] of chunk sums
-// (stride T*E), plus bias when it is not NULL.
-__device__ __forceinline__ void select_token(int t, int lane, int T, int E, int k, int nz,
-                                             const float* __restrict__ zg, const float* __restrict__ bias,
+// sqrt(softplus(z)) and the weights normalised over the k picks.  z is [T][E].
+__device__ __forceinline__ void select_token(int t, int lane, int E, int k, const float* __restrict__ zg,
                                              int32_t* __restrict__ ids, float* __restrict__ wts)
 {
     const float* z = zg + (size_t)t * E;
@@ -318,24 +422,7 @@ __device__ __forceinline__ void select_token(int t, int lane, int T, int E, int 
 #pragma unroll
     for (int q = 0; q < 16; q++) {
         const int e = lane + 64 * q;
-        float v = 0.0f;
-        if (q * 64 < E && e < E) {
-            if (nz == 1) {
-                v = z[e];
-            } else {
-                // eight chunk loads in flight, then their fold in chunk order
-                for (int c0 = 0; c0 < nz; c0 += 8) {
-                    float p[8];
-#pragma unroll
-                    for (int u = 0; u < 8; u++) p[u] = c0 + u < nz ? z[(size_t)(c0 + u) * T * E + e] : 0.0f;
-#pragma unroll
-                    for (int u = 0; u < 8; u++)
-                        if (c0 + u < nz) v = v + p[u];
-                }
-            }
-            if (bias) v = v + bias[e];
-        }
-        zv[q] = v;
+        zv[q] = (q * 64 < E && e < E) ? z[e] : 0.0f;
     }
     uint32_t taken = 0;  // bit q: expert lane + 64q already picked
     float my_z = 0.0f;
@@ -367,13 +454,12 @@ __device__ __forceinline__ void select_token(int t, int lane, int T, int E, int 
         wts[(size_t)t * k + lane] = sum > 0.0f ? a / sum : 1.0f / (float)k;
     }
 }
-__global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, int nz, const float* __restrict__ zg,
-                                                      const float* __restrict__ bias,
+__global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, const float* __restrict__ zg,
                                                       int32_t* __restrict__ ids, float* __restrict__ wts)
 {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    select_token(t, threadIdx.x & 63, T, E, k, nz, zg, bias, ids, wts);
+    select_token(t, threadIdx.x & 63, E, k, zg, ids, wts);
 }
 
 // Hash routing: expert_j = splitmix64(id*k + j) mod E, +1 mod E past repeats.
@@ -834,16 +920,6 @@ __device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t l
 {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
-}
-// A value known to be equal in every lane, moved to scalar registers.
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-template <typename T>
-__device__ __forceinline__ T* uniform(T* p)
-{
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
 // wait until at most OPS*k operations are outstanding, k = 0..2 at run time
 template <int OPS>
@@ -1581,16 +1657,6 @@ __global__ __launch_bounds__(256) void k_dequant_export(int N, int K, int expert
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
-int route_splits(int T, int H, int E)
-{
-    if (T <= 0 || E % 4 != 0 || H % 256 != 0 || H <= ROUTE_CHUNK) return 1;
-    // two tokens x eight experts per lane fill the chip with full-length chains
-    if (E % 32 == 0 && (size_t)((T + 127) / 128) * (E / 32) >= 512) return 1;
-    // without four experts per wave: one token x two experts per lane
-    if (E % 16 != 0 && E % 8 == 0 && (size_t)((T + 63) / 64) * (E / 8) >= 512) return 1;
-    return (H + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
-}
-
 hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
                         const float* bias, int mode, const int64_t* token_ids,
                         int32_t* ids, float* w, float* z, hipStream_t s)
@@ -1600,32 +1666,36 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
                            token_ids, ids, w);
         return hipGetLastError();
     }
-    // Large batches: two tokens x eight experts per lane (W reads shared by
-    // the tokens, x conversions by the experts).  Small batches: one token x
-    // four experts per lane, one block per chunk of h (route_splits), so that
-    // the chains are ROUTE_CHUNK long and the grid holds chunks x as many waves.
-    const int nz = route_splits(T, H, E);
-    if (nz > 1 && E % 16 == 0) {   // four experts per wave (eight spill), 128-h stages
-        hipLaunchKernelGGL((k_route_logits<1, 4, 128, true>), dim3((T + 63) / 64, E / 16, nz), dim3(256), 0, s, T, H,
-                           E, x, wr, bias, z);
-    } else if (nz > 1) {
-        hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4, nz), dim3(256), 0, s, T, H,
-                           E, x, wr, bias, z);
-    } else if (E % 4 != 0 || H % 256 != 0) {
+    // Variants by the number of chains T*E (measured at H = 4096, E = 256):
+    // up to 32768 (T = 128), one chain per lane (k_route_lane, 27 us; the
+    // others 46 us and more); up to 131072 (T = 512), one token x one expert
+    // per lane (51 us); large batches ((T/128)*(E/32) >= 512), two tokens x
+    // eight experts per lane (W reads shared by the tokens, x conversions by
+    // the experts); in between, one token x four experts per lane (T = 1024 /
+    // 2048 / 4096: 85 / 108 / 205 us, against 97 / 181 / 352 with one expert).
+    const long long chains = (long long)T * E;
+    if (E % 4 != 0 || H % 256 != 0) {
         hipLaunchKernelGGL(k_route_logits_any, dim3(blocks_for((size_t)T * E, 256)), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
+    } else if (E >= 32 && chains <= 32768) {
+        constexpr int EL = 32, NTW = 2;
+        const unsigned grid = (unsigned)(((T + NTW * 2 - 1) / (NTW * 2)) * ((E + EL - 1) / EL));
+        hipLaunchKernelGGL((k_route_lane<EL, NTW, 256, 3>), dim3(grid), dim3(64 * (NTW + 1)), 0, s, T, H, E, x, wr,
+                           bias, z);
     } else if (E % 32 == 0 && (size_t)((T + 127) / 128) * (E / 32) >= 512) {
         hipLaunchKernelGGL((k_route_logits<2, 8, 256, false>), dim3((T + 127) / 128, E / 32), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
-    } else if (E % 8 == 0 && (size_t)((T + 63) / 64) * (E / 8) >= 512) {
+    } else if (E % 16 == 0 && chains > 131072) {
+        hipLaunchKernelGGL((k_route_logits<1, 4, 128, true>), dim3((T + 63) / 64, E / 16), dim3(256), 0, s, T, H, E, x,
+                           wr, bias, z);
+    } else if (E % 8 == 0 && chains > 131072) {
         hipLaunchKernelGGL((k_route_logits<1, 2, 256, true>), dim3((T + 63) / 64, E / 8), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
     } else {
         hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
     }
-    hipLaunchKernelGGL(k_route_select, dim3(blocks_for(T, 4)), dim3(256), 0, s, T, E, k, nz, z,
-                       nz > 1 ? bias : nullptr, ids, w);
+    hipLaunchKernelGGL(k_route_select, dim3(blocks_for(T, 4)), dim3(256), 0, s, T, E, k, z, ids, w);
     return hipGetLastError();
 }
 

@@ -31,9 +31,8 @@ def test_workspace_bytes():
     P = 128 * 8
     # at least the hq, y and xq buffers
     assert n >= P * 2048 + P * 4096 * 2 + 128 * 4096
-    # a batch this small runs the router one block per 512-h chunk: eight fp32
-    # [T][E] arrays of chunk sums besides those buffers
-    assert n >= 8 * 128 * 256 * 4 + P * 2048 + P * 4096 * 2 + 128 * 4096
+    # and the router logits, fp32 [T][E]
+    assert n >= 128 * 256 * 4 + P * 2048 + P * 4096 * 2 + 128 * 4096
     assert n % 256 == 0
     assert v4moe.moe_workspace_bytes(v4moe.dims(0, 4096, 2048, 256, 8)) > 0
     for bad in [v4moe.dims(1, 100, 2048, 256, 8), v4moe.dims(1, 4096, 100, 256, 8),

@@ -26,13 +26,20 @@ def bf16_f64(bits):
     return a.view(np.float32).astype(np.float64)
 
 
-def check_out(got_bits, ref_bits, what=""):
+def check_out(got_bits, ref_bits, what="", max_bar=True):
+    """The layer output (bf16) against the oracle at both bars.  With
+    max_bar=False (the per-expert rows y, an intermediate) only the relative-L2
+    bar applies: one E4M3 step of a single h element, which the matrix
+    instructions' inexact chunk sums can flip near a rounding boundary, moves
+    a y element directly, while the output averages k such rows with weights
+    below one.  The maximum is printed either way."""
     g, r = bf16_f64(got_bits), bf16_f64(ref_bits)
     rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
     mx = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
     print(f"  {what} rel_l2={rel:.3e} max_rel={mx:.3e} exact={np.mean(g == r):.4f}", flush=True)
     assert rel <= REL_L2, (what, rel)
-    assert mx <= MAX_REL, (what, mx)
+    if max_bar:
+        assert mx <= MAX_REL, (what, mx)
 
 
 _layers = {}
@@ -97,7 +104,7 @@ def full_check(inp, label):
     assert np.array_equal(g["pair_pos"], ref["pair_pos"])
     assert np.array_equal(g["xq"], ref["xq"])
     assert np.array_equal(g["xs"], ref["xs"])
-    check_out(g["y"], ref["y"], f"{label} y")
+    check_out(g["y"], ref["y"], f"{label} y", max_bar=False)
     check_out(g["out"], ref["out"], f"{label} out")
     f = run_fused(inp)
     assert np.array_equal(f["ids"], g["ids"]) and np.array_equal(f["offsets"], g["offsets"])
@@ -301,15 +308,45 @@ def test_skewed_experts_some_empty():
 
 
 # ---- full-size workloads (H=4096, I=2048, E=256, k=8) ----------------------------------------
-def sampled_check(inp, label, n_sample=12, seed=0):
+def mtile_rows(d):
+    """Rows per m-tile for these dimensions (16 .. 128, about 4/3 of the mean
+    rows per expert); only used to pick which sorted rows to sample."""
+    avg = d.T * d.topk / d.E
+    return 16 if avg <= 12 else 32 if avg <= 24 else 64 if avg <= 48 else 128
+
+
+def sample_tokens(g, d, n_random, seed=0):
+    """Tokens whose outputs are compared with the oracle: n_random seeded
+    random ones; for every active expert, the token of its last sorted row
+    (so every expert's last m-tile meets the oracle); for the three hottest
+    experts, the tokens of the first 16, a spread of middle and the last 16
+    rows of their last m-tile; and the first and last token of the batch."""
+    T, k = d.T, d.topk
+    off, sp = g["offsets"], g["sorted_pair"]
+    cnt = np.diff(off)
+    active = np.nonzero(cnt)[0]
+    parts = [np.random.default_rng(seed).choice(T, size=min(n_random, T), replace=False),
+             sp[off[active + 1] - 1] // k, [0, T - 1]]
+    M = mtile_rows(d)
+    for e in np.argsort(-cnt, kind="stable")[:3]:
+        lo, hi = int(off[e]), int(off[e + 1])
+        first = lo + (hi - lo - 1) // M * M                 # first row of the expert's last m-tile
+        rows = np.arange(first, hi)
+        if len(rows) > 48:
+            rows = np.concatenate([rows[:16], rows[16:-16][::max(1, (len(rows) - 32) // 16)], rows[-16:]])
+        parts.append(sp[rows] // k)
+    return np.unique(np.concatenate([np.asarray(p, np.int64) for p in parts]))
+
+
+def sampled_check(inp, label, n_random=128, repeats=10):
+    """Full-size workload: ids, weights, offsets, permutation and the FP8
+    payload against the oracle in full; y and out element by element on the
+    sampled tokens; the fused path bit-identical to the unfused one and to
+    itself over `repeats` runs."""
     d = inp.dims
     print(f"[{label}] T={d.T}", flush=True)
     g = run_unfused(inp)
-    sample = np.random.default_rng(seed).choice(d.T, size=min(n_sample, d.T), replace=False)
-    cnt = np.bincount(g["ids"].ravel(), minlength=d.E)
-    hot = int(np.argmax(cnt))
-    hot_tok = np.nonzero((g["ids"] == hot).any(1))[0][:2]
-    sample = np.unique(np.concatenate([sample, hot_tok, [0, d.T - 1]]))
+    sample = sample_tokens(g, d, n_random)
     ref = oracle.layer_forward(inp, subset=sample, want_y=True)
     assert np.array_equal(g["ids"], ref["ids"])
     np.testing.assert_allclose(g["w"], ref["w"], rtol=1e-6, atol=0)
@@ -318,54 +355,58 @@ def sampled_check(inp, label, n_sample=12, seed=0):
     assert np.array_equal(g["pair_pos"], ref["pair_pos"])
     assert np.array_equal(g["xq"], ref["xq"])
     assert np.array_equal(g["xs"], ref["xs"])
+    cnt = np.diff(g["offsets"])
+    experts = np.unique(g["ids"][sample])
+    print(f"  sampled {len(sample)} tokens covering {len(experts)} of {(cnt > 0).sum()} active experts; "
+          f"load max/mean={cnt.max() / cnt.mean():.2f} idle={(cnt == 0).sum()}", flush=True)
+    assert len(experts) == (cnt > 0).sum()
     rows = (sample[:, None] * d.topk + np.arange(d.topk)[None, :]).ravel()
-    check_out(g["y"][rows], ref["y"][rows], f"{label} y[sample]")
+    check_out(g["y"][rows], ref["y"][rows], f"{label} y[sample]", max_bar=False)
     check_out(g["out"][sample], ref["out"][sample], f"{label} out[sample]")
-    print(f"  load max/mean={cnt.max() / cnt.mean():.2f} idle={(cnt == 0).sum()}", flush=True)
     f = run_fused(inp)
     assert np.array_equal(f["out"], g["out"]), "wave-scheduled path differs from the unfused path"
+    layer = layer_for(inp)
+    x, bias, tid = dev_inputs(inp)
+    for _ in range(repeats - 1):
+        out, ids, *_ = layer.forward(x, bias, inp.mode, tid)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), f["out"]), "repeated run differs"
+        assert np.array_equal(ids.cpu().numpy(), f["ids"])
+    print(f"  {repeats} fused runs bit-identical", flush=True)
     return g, f
 
 
 @pytest.mark.slow
 def test_decode_full_size():
-    inp = inputs.make("decode")
-    g, f = sampled_check(inp, "decode", n_sample=24)
-    for _ in range(3):
-        assert np.array_equal(run_fused(inp)["out"], f["out"])
+    sampled_check(inputs.make("decode"), "decode", n_random=64)
 
 
 @pytest.mark.slow
 def test_prefill_full_size():
-    inp = inputs.make("prefill")
-    g, f = sampled_check(inp, "prefill", n_sample=10)
-    assert np.array_equal(run_fused(inp)["out"], f["out"])
+    sampled_check(inputs.make("prefill"), "prefill")
 
 
 @pytest.mark.slow
 def test_decode_gateless_full_size():
     """Gate-less squared-ReLU experts at I = 3072 (the SwiGLU experts' parameter count)."""
-    inp = inputs.make("decode_relu2")
-    g, f = sampled_check(inp, "decode_relu2", n_sample=16)
-    assert np.array_equal(run_fused(inp)["out"], f["out"])
+    sampled_check(inputs.make("decode_relu2"), "decode_relu2", n_random=64)
 
 
 @pytest.mark.slow
 def test_prefill_gateless_full_size():
-    inp = inputs.make("prefill_relu2")
-    sampled_check(inp, "prefill_relu2", n_sample=8)
+    sampled_check(inputs.make("prefill_relu2"), "prefill_relu2")
 
 
 @pytest.mark.slow
 def test_zipf_full_size():
-    g, _ = sampled_check(inputs.make("zipf"), "zipf", n_sample=8)
+    g, _ = sampled_check(inputs.make("zipf"), "zipf")
     cnt = np.diff(g["offsets"])
     assert cnt.max() > 10 * cnt.mean() and (cnt == 0).sum() > 0
 
 
 @pytest.mark.slow
 def test_hash_full_size():
-    g, _ = sampled_check(inputs.make("hash"), "hash", n_sample=8)
+    g, _ = sampled_check(inputs.make("hash"), "hash")
     assert np.all(g["w"] == np.float32(1 / 8))
 
 
@@ -375,12 +416,9 @@ def test_ragged_batch_invariance_and_determinism():
     L = inp.lengths
     starts = np.concatenate([[0], np.cumsum(L)])
     print(f"[ragged] T={inp.dims.T} requests={len(L)}", flush=True)
-    g, f = sampled_check(inp, "ragged", n_sample=8)
+    g, f = sampled_check(inp, "ragged")
     layer = layer_for(inp)
     x, _, _ = dev_inputs(inp)
-    for _ in range(10):
-        out, *_ = layer.forward(x)
-        assert np.array_equal(out.cpu().numpy(), f["out"])
     for r in range(len(L)):
         lo, hi = int(starts[r]), int(starts[r + 1])
         out, ids, *_ = layer.forward(x[lo:hi].contiguous())
@@ -389,27 +427,48 @@ def test_ragged_batch_invariance_and_determinism():
         assert np.array_equal(ids.cpu().numpy(), f["ids"][lo:hi])
 
 
-@pytest.mark.parametrize("T,H,E", [
-    (32, 4096, 256),    # one block per 512-h chunk (the decode router)
-    (128, 1280, 256),   # the same with a ragged last chunk
-    (1024, 1536, 256),  # one token per lane, chunks folded in the block
+# Router variants (launch_route), by the number of chains T*E: E % 4 != 0 ->
+# one thread per logit; E >= 32 and T*E <= 32768 -> one chain per lane over
+# 32 experts x 2 tokens per wave with a producer wave; T*E <= 131072 -> one
+# token x one expert per lane; large batches (E % 32 == 0, (T/128)*(E/32) >=
+# 512) -> two tokens x eight experts per lane; otherwise one token x four
+# (E % 16 == 0) or two (E % 8 == 0) experts per lane.
+ROUTER_VARIANTS = [
+    (32, 4096, 256),    # one chain per lane (the decode router)
+    (128, 1280, 256),   # the same at its largest batch, H not a multiple of 512
+    (200, 1280, 100),   # the same with the last group of 32 experts holding 4
+    (512, 1536, 256),   # one token x one expert per lane
+    (2000, 1024, 256),  # one token x four experts per lane, ragged last token block
+    (4000, 1280, 40),   # one token x two experts per lane
     (8192, 1280, 256),  # two tokens x eight experts per lane
-    (50, 1280, 6),      # the generic router
-])
-def test_routing_chunk_fold_order(T, H, E):
-    """Every router variant sums the logits as the fold of 512-h chains: with
-    x = 1, expert 1 holds 2^24 at h = 0 and 1 at h = 512 and 513 (2^24 + 2 as
-    chunk sums; 2^24 as one chain, 2^24 + 1 rounding to even) and expert 0
-    holds 2^24 alone, so expert 1 ranks first only under the fold."""
+    (64, 1024, 8),      # few experts: one token x one expert per lane
+    (50, 1280, 6),      # E % 4 != 0: one thread per logit
+]
+
+
+@pytest.mark.parametrize("T,H,E", ROUTER_VARIANTS)
+def test_routing_single_chain_order(T, H, E):
+    """Every router variant sums a logit as one fp32 fma chain over h
+    ascending.  With x = 1: expert 0 holds 2^24 at h = 0; expert 1 the same
+    plus 1 at h = 512 and 513 (each 2^24 + 1 rounds back to 2^24, so it ties
+    with expert 0 and ranks second; blocks of 512 summed apart would give
+    2^24 + 2 and rank it first); expert 2 holds 2^24 at h = 0, 1 at h = 1 ..
+    H-2 and -2^24 at h = H-1 (the chain ends at 0, an order adding the ones
+    first at H - 2); expert 3 holds 1 at h = 0.  The chain ranks 0, 1, 3, 2."""
     x = inputs.to_bf16_bits(np.ones((T, H), np.float32))
     wr = np.zeros((H, E), np.float32)
-    wr[0, 0] = wr[0, 1] = 2.0 ** 24
+    wr[0, 0] = wr[0, 1] = wr[0, 2] = 2.0 ** 24
     wr[512, 1] = wr[513, 1] = 1.0
-    ids_ref, w_ref = oracle.route(x, wr, 2)
-    assert np.all(ids_ref[:, 0] == 1) and np.all(ids_ref[:, 1] == 0)
-    d = v4moe.dims(T, H, 128, E, 2)
-    ids = torch.empty((T, 2), dtype=torch.int32, device=DEV)
-    w = torch.empty((T, 2), dtype=torch.float32, device=DEV)
+    wr[1:H - 1, 2] = 1.0
+    wr[H - 1, 2] = -(2.0 ** 24)
+    wr[0, 3] = 1.0
+    k = 4
+    ids_ref, w_ref = oracle.route(x, wr, k)
+    assert np.all(ids_ref == np.array([0, 1, 3, 2]))
+    print(f"[chain order] T={T} H={H} E={E}", flush=True)
+    d = v4moe.dims(T, H, 128, E, k)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
     ws = torch.empty(v4moe.moe_workspace_bytes(d), dtype=torch.uint8, device=DEV)
     v4moe.moe_route(d, torch.from_numpy(x.view(np.int16)).to(DEV), torch.from_numpy(wr).to(DEV), None, 0, None,
                     ids, w, ws)
@@ -419,14 +478,17 @@ def test_routing_chunk_fold_order(T, H, E):
 
 
 @pytest.mark.parametrize("T,H,E,k", [
-    (32, 256, 8, 3),        # small-batch router
-    (50, 256, 6, 2),        # E % 4 != 0: the generic router
-    (4096, 512, 256, 8),    # one token per lane, two experts per lane
+    (32, 4096, 256, 8),     # one chain per lane
+    (32, 256, 1024, 16),    # the same over 1024 experts, top-16
+    (200, 768, 100, 4),     # the same with a partial last group of experts
+    (512, 512, 256, 8),     # one token x one expert per lane
+    (64, 256, 1024, 16),    # the same over 1024 experts
+    (2000, 256, 256, 8),    # one token x four experts per lane
+    (4000, 256, 40, 4),     # one token x two experts per lane
     (8192, 256, 256, 8),    # two tokens x eight experts per lane
-    (32, 1280, 8, 3),       # one block per 512-h chunk, ragged last chunk
-    (1024, 1536, 256, 8),   # one token per lane, chunks folded in the block
-    (8192, 1280, 256, 8),   # two tokens x eight experts per lane, ragged last chunk
-    (50, 768, 6, 2),        # the generic router over two chunks
+    (32, 256, 8, 3),        # few experts
+    (50, 256, 6, 2),        # E % 4 != 0: one thread per logit
+    (50, 768, 6, 2),
 ])
 def test_routing_exact_ties(T, H, E, k):
     """Logits that collide exactly (x in {-1, 0, 1}, W_r columns drawn from
