@@ -7,7 +7,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SO = os.path.join(HERE, "libv4moe.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("v4moe_kernels.hip", "v4moe_bwd.hip", "v4moe_api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("v4moe_kernels.hip", "v4moe_bwd.hip", "v4moe_api.cpp",
+                                                               "v4moe_noalloc.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in ("v4moe_device.h", "v4moe_internal.h")] + \
     [os.path.join(ROOT, "include", "v4moe.h")]
 

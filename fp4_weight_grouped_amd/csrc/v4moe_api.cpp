@@ -20,13 +20,12 @@ using namespace v4moe;
 
 namespace {
 
-constexpr int kMaxDevices = 64;
-
 struct DeviceInfo {
     std::once_flag once;
     int ok = 0;          // 1: gfx950
     int cus = 0;
     int persist_per_cu[2][2][9] = {};   // [gated][CW == 4][MT]
+    int scratch_ok = 0;  // 1: the static scratch array's address was found
 };
 DeviceInfo g_dev[kMaxDevices];
 
@@ -44,6 +43,7 @@ DeviceInfo* device_info()
         for (int g = 0; g < 2; g++)
             for (int mt : {1, 2, 4})
                 for (int cw : {2, 4}) di->persist_per_cu[g][cw == 4][mt] = persistent_blocks_per_cu(mt, cw, g == 1);
+        di->scratch_ok = noalloc_setup_device(dev) == hipSuccess;
     });
     return di->ok ? di : nullptr;
 }
@@ -242,6 +242,66 @@ int run_ffn(const v4moe_dims* d, const Layout& L, const FfnArgs& a, uint8_t* ws,
 
 }  // namespace
 
+namespace v4moe {
+
+bool device_ready() { return device_info() != nullptr; }
+
+// The layer forward on a given workspace (moe_layer_forward and
+// moe_layer_forward_noalloc).
+int layer_forward_ws(
+    const v4moe_dims* d, const uint16_t* x, const float* w_router, const float* bias, int32_t mode,
+    const int64_t* token_ids, const v4moe_experts* w, int32_t* topk_ids, float* topk_w,
+    int32_t* expert_offsets, uint16_t* out, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!dims_ok(d)) return V4MOE_EDIMS;
+    if (mode != V4MOE_ROUTE_LEARNED && mode != V4MOE_ROUTE_HASH) return V4MOE_EDIMS;
+    if (!expert_offsets) return V4MOE_ENULL;
+    if (d->T == 0) {
+        // an empty batch: only the offsets (E+1 zeros) are written
+        if (!device_info()) return V4MOE_EDEVICE;
+        return launch_fill_i32(expert_offsets, 0, d->E + 1, as_stream(stream)) == hipSuccess ? V4MOE_OK
+                                                                                           : V4MOE_ELAUNCH;
+    }
+    if (!x || !w || !topk_ids || !topk_w || !out || !workspace) return V4MOE_ENULL;
+    if (mode == V4MOE_ROUTE_LEARNED && !w_router) return V4MOE_ENULL;
+    if ((gated(d) && !mat_ok(w->gate)) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return V4MOE_EALIGN;
+    if (mode == V4MOE_ROUTE_LEARNED && !aligned16(w_router)) return V4MOE_EALIGN;
+    const Layout L = layout(d);
+    if (ws_bytes < L.total) return V4MOE_EWORKSPACE;
+    DeviceInfo* di = device_info();
+    if (!di) return V4MOE_EDEVICE;
+    hipStream_t s = as_stream(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* xq = ws + L.xq;
+    float* xs = reinterpret_cast<float*>(ws + L.xs);
+    int32_t* sp = reinterpret_cast<int32_t*>(ws + L.sorted_pair);
+    int32_t* pp = reinterpret_cast<int32_t*>(ws + L.pair_pos);
+    uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+    // Small batches: the permutation and the tile list run as one block (same
+    // device code, same results).
+    const bool fuse = perm_tiles_one_block(d->T, d->topk, d->E);
+    if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w,
+                     reinterpret_cast<float*>(ws + L.z), s) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    if (launch_quant_x(d->T, d->H, x, xq, xs, s) != hipSuccess) return V4MOE_ELAUNCH;
+    if (!fuse && launch_permute(d->T, d->topk, d->E, topk_ids, expert_offsets, sp, pp,
+                                reinterpret_cast<int32_t*>(ws + L.hist), s) != hipSuccess)
+        return V4MOE_ELAUNCH;
+    const FfnArgs a = ffn_args(d, L, ws, xq, xs, expert_offsets, sp, w, y);
+    const FusedPerm ff{topk_ids, expert_offsets, sp, pp};
+    // The wave-scheduled persistent kernel for weight-streaming batches (m-tiles
+    // of at most 64 rows); with 128-row m-tiles it measured 5-10% slower than
+    // the two launches on one GPU, where there is no transfer to hide.  Both
+    // run the same tiles: the results are identical.
+    int rc = run_ffn(d, L, a, ws, L.MT < 8, di, s, fuse ? &ff : nullptr);
+    if (rc) return rc;
+    if (launch_combine(d->T, d->H, d->topk, y, topk_w, out, s) != hipSuccess) return V4MOE_ELAUNCH;
+    return V4MOE_OK;
+}
+
+}  // namespace v4moe
+
 extern "C" {
 
 __attribute__((visibility("default"))) size_t moe_workspace_bytes(const v4moe_dims* d)
@@ -364,51 +424,8 @@ __attribute__((visibility("default"))) int moe_layer_forward(
     const int64_t* token_ids, const v4moe_experts* w, int32_t* topk_ids, float* topk_w,
     int32_t* expert_offsets, uint16_t* out, void* workspace, size_t ws_bytes, void* stream)
 {
-    if (!dims_ok(d)) return V4MOE_EDIMS;
-    if (mode != V4MOE_ROUTE_LEARNED && mode != V4MOE_ROUTE_HASH) return V4MOE_EDIMS;
-    if (!expert_offsets) return V4MOE_ENULL;
-    if (d->T == 0) {
-        // an empty batch: only the offsets (E+1 zeros) are written
-        if (!device_info()) return V4MOE_EDEVICE;
-        return launch_fill_i32(expert_offsets, 0, d->E + 1, as_stream(stream)) == hipSuccess ? V4MOE_OK
-                                                                                           : V4MOE_ELAUNCH;
-    }
-    if (!x || !w || !topk_ids || !topk_w || !out || !workspace) return V4MOE_ENULL;
-    if (mode == V4MOE_ROUTE_LEARNED && !w_router) return V4MOE_ENULL;
-    if ((gated(d) && !mat_ok(w->gate)) || !mat_ok(w->up) || !mat_ok(w->down)) return V4MOE_ENULL;
-    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return V4MOE_EALIGN;
-    if (mode == V4MOE_ROUTE_LEARNED && !aligned16(w_router)) return V4MOE_EALIGN;
-    const Layout L = layout(d);
-    if (ws_bytes < L.total) return V4MOE_EWORKSPACE;
-    DeviceInfo* di = device_info();
-    if (!di) return V4MOE_EDEVICE;
-    hipStream_t s = as_stream(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    uint8_t* xq = ws + L.xq;
-    float* xs = reinterpret_cast<float*>(ws + L.xs);
-    int32_t* sp = reinterpret_cast<int32_t*>(ws + L.sorted_pair);
-    int32_t* pp = reinterpret_cast<int32_t*>(ws + L.pair_pos);
-    uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
-    // Small batches: the permutation and the tile list run as one block (same
-    // device code, same results).
-    const bool fuse = perm_tiles_one_block(d->T, d->topk, d->E);
-    if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w,
-                     reinterpret_cast<float*>(ws + L.z), s) != hipSuccess)
-        return V4MOE_ELAUNCH;
-    if (launch_quant_x(d->T, d->H, x, xq, xs, s) != hipSuccess) return V4MOE_ELAUNCH;
-    if (!fuse && launch_permute(d->T, d->topk, d->E, topk_ids, expert_offsets, sp, pp,
-                                reinterpret_cast<int32_t*>(ws + L.hist), s) != hipSuccess)
-        return V4MOE_ELAUNCH;
-    const FfnArgs a = ffn_args(d, L, ws, xq, xs, expert_offsets, sp, w, y);
-    const FusedPerm ff{topk_ids, expert_offsets, sp, pp};
-    // The wave-scheduled persistent kernel for weight-streaming batches (m-tiles
-    // of at most 64 rows); with 128-row m-tiles it measured 5-10% slower than
-    // the two launches on one GPU, where there is no transfer to hide.  Both
-    // run the same tiles: the results are identical.
-    int rc = run_ffn(d, L, a, ws, L.MT < 8, di, s, fuse ? &ff : nullptr);
-    if (rc) return rc;
-    if (launch_combine(d->T, d->H, d->topk, y, topk_w, out, s) != hipSuccess) return V4MOE_ELAUNCH;
-    return V4MOE_OK;
+    return v4moe::layer_forward_ws(d, x, w_router, bias, mode, token_ids, w, topk_ids, topk_w, expert_offsets, out,
+                                   workspace, ws_bytes, stream);
 }
 
 __attribute__((visibility("default"))) int moe_prepack_weights(const v4moe_dims* d,

@@ -5,10 +5,17 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "v4moe.h"
+
 namespace v4moe {
 
 // Pairs handled by one block of the permutation passes.
 constexpr int kPermChunk = 256;
+// Devices the library keeps per-device state for (indexed by HIP device id).
+constexpr int kMaxDevices = 64;
+// Bytes of the library's static per-device scratch array, the workspace of
+// moe_layer_forward_noalloc (v4moe_noalloc.hip).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
 // Experts per scheduling wave of the persistent kernel (P1 §1.2: experts are
 // split into waves of a few experts each).
 constexpr int kWaveExperts = 8;
@@ -111,5 +118,20 @@ inline int bwd_tile_rows(int T, int k, int E) { return (long long)T * k >= 64LL 
 // Wave columns per tile: a tile covers 64*CW columns of h in linear1 (128*CW
 // gate-less) and 128*CW output columns in linear2.
 int choose_cw(int MT, int H, int I, bool gated);
+
+// ---- allocation-free layer forward (v4moe_noalloc.hip) ----
+// Looks up, with device `dev` current, the address of the static scratch
+// array on that device and keeps it; called once per device at set-up.
+hipError_t noalloc_setup_device(int dev);
+// The scratch array's device address on `dev`, or nullptr if set-up failed.
+void* noalloc_scratch(int dev);
+// Device set-up of the library (gfx950 check, occupancy, scratch address) for
+// the current device; false if the device is unusable.
+bool device_ready();
+// moe_layer_forward on the given workspace (both layer-forward entry points).
+int layer_forward_ws(const v4moe_dims* d, const uint16_t* x, const float* w_router, const float* bias,
+                     int32_t mode, const int64_t* token_ids, const v4moe_experts* w, int32_t* topk_ids,
+                     float* topk_w, int32_t* expert_offsets, uint16_t* out, void* workspace, size_t ws_bytes,
+                     void* stream);
 
 }  // namespace v4moe

@@ -81,9 +81,14 @@ def lib():
         L.moe_transpose_weights.argtypes = [_DP, ctypes.POINTER(ExpertsC), _vp, _vp, _vp]
         L.moe_layer_backward.argtypes = [_DP, _vp, _vp, _vp, _i32, _vp, ctypes.POINTER(ExpertsC), _vp, _vp,
                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_layer_forward_noalloc.argtypes = [_DP, _vp, _vp, _vp, _i32, _vp, ctypes.POINTER(ExpertsC),
+                                                _vp, _vp, _vp, _vp, _vp]
+        L.moe_noalloc_max_workspace_bytes.argtypes = []
+        L.moe_noalloc_max_workspace_bytes.restype = _sz
         L.moe_time_next_ffn.argtypes = [_vp, _vp]
         L.moe_time_next_ffn.restype = None
         for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+                  "moe_layer_forward_noalloc",
                   "moe_prepack_weights", "moe_dequant_fp8", "moe_quantize_weights", "moe_transpose_weights",
                   "moe_layer_backward"):
             getattr(L, f).restype = ctypes.c_int
@@ -171,6 +176,18 @@ def moe_layer_forward(d: Dims, x, w_router, bias, mode, token_ids, experts: Devi
     _check(lib().moe_layer_forward(ctypes.byref(d), _p(x), _p(w_router), _p(bias), mode, _p(token_ids),
                                    ctypes.byref(ex), _p(topk_ids), _p(topk_w), _p(expert_offsets),
                                    _p(out), _p(workspace), workspace.numel(), _stream()))
+
+
+def moe_layer_forward_noalloc(d: Dims, x, w_router, bias, mode, token_ids, experts: DeviceExperts,
+                              topk_ids, topk_w, expert_offsets, out):
+    ex = experts.c()
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(d), _p(x), _p(w_router), _p(bias), mode, _p(token_ids),
+                                           ctypes.byref(ex), _p(topk_ids), _p(topk_w), _p(expert_offsets),
+                                           _p(out), _stream()))
+
+
+def moe_noalloc_max_workspace_bytes() -> int:
+    return lib().moe_noalloc_max_workspace_bytes()
 
 
 def moe_prepack_weights(d: Dims, canonical: DeviceExperts, packed: DeviceExperts, workspace):

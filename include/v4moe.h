@@ -194,6 +194,25 @@ int moe_layer_forward(const v4moe_dims* d, const uint16_t* x, const float* w_rou
                       int32_t* expert_offsets, uint16_t* out,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/* moe_layer_forward without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * moe_layer_forward (bit-identical outputs); the workspace is instead a
+ * static device array of the library, one per GPU, of
+ * moe_noalloc_max_workspace_bytes() bytes (16 MiB: the full decode layer, H =
+ * 4096, I = 2048, E = 256, top-8, fits up to T = 189), held by each GPU the
+ * library runs on until the process ends.  Nothing is allocated or freed.
+ * Errors: V4MOE_EDIMS for unsupported dimensions; V4MOE_EWORKSPACE when
+ * moe_workspace_bytes(d) exceeds the array (nothing is enqueued); otherwise
+ * as moe_layer_forward.  Every call on one GPU shares the array: calls that
+ * overlap on a GPU (other streams, other host threads) race, calls on one
+ * stream are ordered.  No contents need to survive between calls. */
+size_t moe_noalloc_max_workspace_bytes(void);
+int moe_layer_forward_noalloc(const v4moe_dims* d, const uint16_t* x, const float* w_router,
+                              const float* bias, int32_t mode, const int64_t* token_ids,
+                              const v4moe_experts* w, int32_t* topk_ids, float* topk_w,
+                              int32_t* expert_offsets, uint16_t* out, void* stream);
+
 /* FP32 master weights -> FP4 weights (P1 §4 and P4 §4: FP4 quantisation-aware
  * training quantises the FP32 master weights to FP4 in the forward pass;
  * element format and shared-exponent rule per the OCP MX specification the

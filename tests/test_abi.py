@@ -13,7 +13,8 @@ def test_exports_every_declared_function():
     assert set(names) >= {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
                           "moe_layer_forward", "moe_workspace_bytes", "moe_prepack_weights",
                           "moe_dequant_fp8", "moe_quantize_weights", "moe_strerror", "moe_transpose_weights",
-                          "moe_layer_backward", "moe_backward_workspace_bytes"}
+                          "moe_layer_backward", "moe_backward_workspace_bytes", "moe_layer_forward_noalloc",
+                          "moe_noalloc_max_workspace_bytes"}
     L = v4moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -95,3 +96,22 @@ def test_error_paths_without_device():
     assert L.moe_quantize_weights(1, 128, 128, None, 0, ctypes.byref(m), None, None) == -1
     assert L.moe_quantize_weights(1, 128, 128, mis, 0, ctypes.byref(m), None, None) == -3
     assert L.moe_quantize_weights(1, 128, 128, p, 0, ctypes.byref(v4moe.Mat(4096, 0, 4096)), None, None) == -1
+
+
+def test_noalloc_limits_without_device():
+    """The allocation-free layer forward checks dimensions and its static
+    scratch size before touching a device."""
+    L = v4moe.lib()
+    cap = L.moe_noalloc_max_workspace_bytes()
+    assert cap == 16 << 20
+    p = ctypes.c_void_p(4096)
+    ex = v4moe.ExpertsC(v4moe.Mat(4096, 4096, 4096), v4moe.Mat(4096, 4096, 4096), v4moe.Mat(4096, 4096, 4096))
+    bad = v4moe.dims(4, 255, 128, 8, 2)
+    assert L.moe_layer_forward_noalloc(ctypes.byref(bad), p, p, None, 0, None, ctypes.byref(ex), p, p, p, p,
+                                       None) == -2
+    # the decode layer fits up to T = 189; T = 190 does not
+    fits = v4moe.dims(189, 4096, 2048, 256, 8)
+    over = v4moe.dims(190, 4096, 2048, 256, 8)
+    assert L.moe_workspace_bytes(ctypes.byref(fits)) <= cap < L.moe_workspace_bytes(ctypes.byref(over))
+    assert L.moe_layer_forward_noalloc(ctypes.byref(over), p, p, None, 0, None, ctypes.byref(ex), p, p, p, p,
+                                       None) == -4
