@@ -17,7 +17,19 @@ HBM traffic of the FFN (roofline.traffic) comes from the committed rocprofv3
 TCC counter summary (FETCH_SIZE + WRITE_SIZE per FFN, scaled by
 the same counters' reading for a plain copy kernel of known size); it is
 reported only while the kernel sources hash to the value recorded with it.
-The CPU baseline is the C oracle (test infrastructure) timed on the host cores.
+Every workload record carries both roofline fractions of its FFN (HBM GB/s
+on the weight bytes, FP8 TFLOP/s on the algorithmic FLOP), a cold-cache
+protocol run (512 MiB of scratch written between steps, outside the per-step
+HIP events, so nothing is left in the 256 MB last-level cache) and a
+determinism flag (the first and the last timed step's outputs bit-identical).
+Records: the headline decode batch, prefill (T=8192), the skewed batch with a
+Zipf router bias (T=4096), hash routing (T=4096), the ragged batch of 64
+requests and the tiny layer (T=64, H=256, I=128, E=8, k=2).
+The CPU baseline is the C oracle (test infrastructure) timed on the host
+cores: the whole decode batch for the headline, and a bounded sample of 16
+tokens (all tokens routed) for each side record.  Its outputs are also
+compared with the GPU's on the same inputs; the result is the record's
+`parity` (ids and offsets bit-exact, weights, output rel-L2 and max|d|).
 The weight quantiser (FP32 master -> MXFP4, one layer's experts), the layer
 backward (decode and prefill) and the gate-less squared-ReLU layer at the same
 parameter count (I=3072) are reported as side records.  Each workload record also carries the
@@ -199,7 +211,17 @@ def sustained_power_clock(fn, seconds=1.0):
                 source="amdgpu sysfs (hwmon power1_average, pp_dpm_sclk), sampled every 20 ms")
 
 
-def run_gpu(name, steps, warmup, layer_cache, extras=True):
+SCRATCH_BYTES = 512 << 20      # written between protocol steps: 2x the 256 MB last-level cache
+
+
+def run_gpu(name, steps, warmup, layer_cache, extras=True, scratch=None):
+    """Time one workload.  The contract loop: `steps` back-to-back layer
+    forwards, bracketed by synchronisations (ms_per_step, tokens/s).  The
+    cold-cache protocol loop: the same number of steps, each preceded by a
+    write of SCRATCH_BYTES (outside its HIP events), so weights and
+    activations come from HBM; per-step device times from those events.
+    Determinism: the output of the first and the last timed step of both
+    loops must be bit-identical."""
     import torch
     from fp4_weight_grouped_amd import inputs, v4moe
 
@@ -222,27 +244,54 @@ def run_gpu(name, steps, warmup, layer_cache, extras=True):
     tid = None if inp.token_ids is None else torch.from_numpy(inp.token_ids).to(dev)
     out = torch.empty((d.T, d.H), dtype=torch.int16, device=dev)
 
+    def new_events(n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:    # torch creates the HIP event on first record
+            a.record()
+            b.record()
+        return evs
+
     for _ in range(warmup):
         layer.forward(x, bias, inp.mode, tid, out=out)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev + sev:    # torch creates the HIP event on first record
-        a.record()
-        b.record()
+    first = None
+    ev, sev = new_events(steps), new_events(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         sev[i][0].record()
         v4moe.moe_time_next_ffn(*ev[i])
-        _, ids, _, off = layer.forward(x, bias, inp.mode, tid, out=out)
+        _, ids, w, off = layer.forward(x, bias, inp.mode, tid, out=out)
         sev[i][1].record()
+        if i == 0:
+            first = out.clone()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    deterministic = bool(torch.equal(first, out))
     ms_step = (t1 - t0) * 1e3 / steps
     ffn_all = [a.elapsed_time(b) for a, b in ev]
     step_all = [a.elapsed_time(b) for a, b in sev]
     ffn_ms = float(np.mean(ffn_all))
+
+    # cold-cache protocol: SCRATCH_BYTES written between steps, outside the events
+    cold = None
+    if scratch is not None:
+        cev, csev = new_events(steps), new_events(steps)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            scratch.fill_(i & 0xFF)
+            csev[i][0].record()
+            v4moe.moe_time_next_ffn(*cev[i])
+            layer.forward(x, bias, inp.mode, tid, out=out)
+            csev[i][1].record()
+        torch.cuda.synchronize()
+        deterministic = deterministic and bool(torch.equal(first, out))
+        cs = [a.elapsed_time(b) for a, b in csev]
+        cf = [a.elapsed_time(b) for a, b in cev]
+        cold = dict(scratch_bytes=scratch.numel(), step_device_ms=dict(median=float(np.median(cs)), p10=pct(cs, 10),
+                                                                       p90=pct(cs, 90)),
+                    ffn_device_ms=dict(median=float(np.median(cf)), p10=pct(cf, 10), p90=pct(cf, 90)),
+                    tokens_per_s=d.T / (float(np.median(cs)) / 1e3))
     attr = attribution(layer, x, bias, inp.mode, tid) if extras else None
     pc = sustained_power_clock(lambda: layer.forward(x, bias, inp.mode, tid, out=out)) if extras else None
     counts = np.diff(off.cpu().numpy())
@@ -251,18 +300,28 @@ def run_gpu(name, steps, warmup, layer_cache, extras=True):
     wbytes = n_active * weight_bytes_per_expert(d.H, d.I, mats)
     flops = ffn_flops(d.T, d.topk, d.H, d.I, mats)
     act = {inputs.ACT_SWIGLU: "swiglu", inputs.ACT_RELU2: "relu2 (gate-less)", inputs.ACT_RELU: "relu (gate-less)"}
-    r = dict(workload=name, T=d.T, H=d.H, I=d.I, E=d.E, topk=d.topk, activation=act[d.act], ms_per_step=ms_step,
-             tokens_per_s=d.T / (ms_step / 1e3), ffn_ms=ffn_ms, active_experts=n_active,
+    hbm = wbytes / (ffn_ms / 1e3) / 1e9
+    tfl = flops / (ffn_ms / 1e3) / 1e12
+    r = dict(workload=name, T=d.T, H=d.H, I=d.I, E=d.E, topk=d.topk, activation=act[d.act],
+             routing="hash" if inp.mode == inputs.ROUTE_HASH else ("learned + zipf bias" if inp.bias is not None
+                                                                    else "learned"),
+             ms_per_step=ms_step, tokens_per_s=d.T / (ms_step / 1e3), ffn_ms=ffn_ms, active_experts=n_active,
              load_max_over_mean=float(counts.max() / counts.mean()), idle_experts=int((counts == 0).sum()),
-             weight_bytes=wbytes, ffn_hbm_gbs=wbytes / (ffn_ms / 1e3) / 1e9,
-             ffn_tflops=flops / (ffn_ms / 1e3) / 1e12,
+             weight_bytes=wbytes, ffn_flop=flops, ffn_hbm_gbs=hbm, ffn_tflops=tfl,
+             roofline_hbm=dict(achieved=hbm, peak=HBM_PEAK_GBS, unit="GB/s", frac=hbm / HBM_PEAK_GBS,
+                               work="FP4 codes + E8M0 + fp32 block scales of the active experts"),
+             roofline_mfma=dict(achieved=tfl, peak=FP8_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
+                                frac=tfl / FP8_DENSE_PEAK_TFLOPS, work=f"2*T*k*{mats}*H*I FLOP"),
+             deterministic=deterministic,
              step_device_ms=dict(median=float(np.median(step_all)), p10=pct(step_all, 10), p90=pct(step_all, 90)),
              ffn_device_ms=dict(median=float(np.median(ffn_all)), p10=pct(ffn_all, 10), p90=pct(ffn_all, 90)),
-             attribution_ms=attr, power_clock=pc)
+             cold_cache=cold, attribution_ms=attr, power_clock=pc)
+    r["_gpu"] = dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), offsets=off.cpu().numpy(), out=out.cpu().numpy())
     log(f"[bench] {name}: {ms_step:.3f} ms/step, ffn {ffn_ms:.3f} ms, "
-        f"{r['ffn_hbm_gbs']:.0f} GB/s, {r['ffn_tflops']:.0f} TFLOP/s, active {n_active}")
+        f"{hbm:.0f} GB/s, {tfl:.0f} TFLOP/s, active {n_active}, deterministic {deterministic}")
     log(f"[bench] {name}: step device ms median {r['step_device_ms']['median']:.3f} "
-        f"(p10 {r['step_device_ms']['p10']:.3f}, p90 {r['step_device_ms']['p90']:.3f})")
+        f"(p10 {r['step_device_ms']['p10']:.3f}, p90 {r['step_device_ms']['p90']:.3f})"
+        + (f"; cold-cache median {cold['step_device_ms']['median']:.3f}" if cold else ""))
     if extras:
         log(f"[bench] {name}: attribution {', '.join(f'{k} {v:.3f}' for k, v in attr.items())}; power/clock {pc}")
     return r, inp
@@ -364,17 +423,25 @@ def run_backward(name, steps, warmup, layer_cache):
     return rec
 
 
-def cpu_baseline(inp, max_tokens=128, min_seconds=10.0, max_reps=8):
-    """The oracle's layer forward on the same inputs, repeated until about
-    min_seconds of CPU work have been timed."""
+def cpu_baseline(inp, gpu=None, max_tokens=128, min_seconds=10.0, max_reps=8):
+    """The oracle's layer forward on the same inputs (test infrastructure: it
+    shares no code with the library), repeated until about min_seconds of CPU
+    work have been timed: routing, quantisation and permutation of all T
+    tokens, the expert FFN and combine of a bounded sample of tokens.  With
+    `gpu` (the GPU record's outputs of the same inputs) the oracle's results
+    are also compared with them: ids and offsets bit for bit, the output of the
+    sampled tokens at the stated bars."""
     import oracle
     T = inp.dims.T
-    sub = None if T <= max_tokens else np.arange(max_tokens, dtype=np.int32)
+    if T <= max_tokens:
+        sub = None
+    else:   # evenly spread tokens, always the first and the last
+        sub = np.unique(np.linspace(0, T - 1, max_tokens).round().astype(np.int32))
     n = T if sub is None else len(sub)
-    reps, dt = 0, 0.0
+    reps, dt, ref = 0, 0.0, None
     while reps < max_reps and (reps == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        oracle.layer_forward(inp, subset=sub)
+        ref = oracle.layer_forward(inp, subset=sub)
         dt += time.perf_counter() - t0
         reps += 1
     cpu_model = None
@@ -385,11 +452,27 @@ def cpu_baseline(inp, max_tokens=128, min_seconds=10.0, max_reps=8):
                 break
     except OSError:
         pass
-    return dict(value=reps * n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                seconds=dt, repetitions=reps, cpu_model=cpu_model,
-                sample=(f"whole layer forward of all {T} tokens of the workload, {reps} times" if sub is None else
-                        f"routing/quantisation/permutation of all {T} tokens, expert FFN + combine "
-                        f"of the first {n} tokens, {reps} times; rate = those tokens / wall time"))
+    rec = dict(value=reps * n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+               seconds=dt, repetitions=reps, cpu_model=cpu_model,
+               sample=(f"whole layer forward of all {T} tokens of the workload, {reps} times" if sub is None else
+                       f"routing/quantisation/permutation of all {T} tokens, expert FFN + combine "
+                       f"of {n} evenly spaced tokens, {reps} times; rate = those tokens / wall time"))
+    if gpu is not None:
+        toks = np.arange(T) if sub is None else sub
+
+        def f64(bits):
+            return (np.asarray(bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        g, r = f64(gpu["out"][toks]), f64(ref["out"][toks])
+        rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+        mx = float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-30))
+        wrel = float(np.max(np.abs(gpu["w"].astype(np.float64) - ref["w"]) / np.abs(ref["w"])))
+        rec["parity"] = dict(ids_bit_exact=bool(np.array_equal(gpu["ids"], ref["ids"])),
+                             offsets_bit_exact=bool(np.array_equal(gpu["offsets"], ref["offsets"])),
+                             weights_max_rel=wrel, out_rel_l2=rel, out_max_rel=mx, tokens_compared=int(len(toks)),
+                             within_bar=bool(rel <= 2e-3 and mx <= 1e-2 and wrel <= 1e-6),
+                             bar="ids/offsets bit-exact; weights 1e-6 relative; out rel-L2 <= 2e-3, "
+                                 "max|d| <= 1e-2 max|ref|")
+    return rec
 
 
 def main():
@@ -408,6 +491,10 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0, help="only run the counter-calibration copy")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-entry-point attribution and the power/clock sampling")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the tiny, zipf, hash and ragged side records")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache protocol loop (scratch writes between steps)")
     ap.add_argument("--only-quantizer", action="store_true",
                     help="only time the weight quantiser on the workload's layer shape and print its record")
     args = ap.parse_args()
@@ -431,10 +518,21 @@ def main():
         print(json.dumps({"weight_quantizer": run_quantizer(d.E, d.H, d.I, args.steps)}), flush=True)
         return
     cache = {}
-    head, inp = run_gpu(args.workload, args.steps, args.warmup, cache, not args.no_extras)
-    side = None
+    scratch = None if args.no_cold else torch.empty(SCRATCH_BYTES, dtype=torch.uint8, device="cuda:0")
+    head, inp = run_gpu(args.workload, args.steps, args.warmup, cache, not args.no_extras, scratch)
+    side = side_inp = None
+    side_steps, side_warm = max(5, min(20, args.steps)), max(2, args.warmup // 2)
     if not args.no_prefill and args.workload != "prefill":
-        side, _ = run_gpu("prefill", max(5, min(20, args.steps)), max(2, args.warmup // 2), cache, not args.no_extras)
+        side, side_inp = run_gpu("prefill", side_steps, side_warm, cache, not args.no_extras, scratch)
+
+    # the other configurations of the method: skewed (Zipf bias), hash routing,
+    # the ragged batch of 64 requests (same layer as decode/prefill), and the
+    # tiny layer (run last: it replaces the cached layer)
+    others = []
+    if not args.no_workloads:
+        for w in ("zipf", "hash", "ragged"):
+            if w != args.workload:
+                others.append(run_gpu(w, side_steps, side_warm, cache, False, scratch))
 
     bwd = None
     if not args.no_backward:
@@ -466,13 +564,22 @@ def main():
     if not args.no_gateless and args.workload in ("decode", "prefill"):
         gateless = []
         for w in ("decode_relu2", "prefill_relu2"):
-            r, _ = run_gpu(w, max(5, min(20, args.steps)), max(2, args.warmup // 2), cache, False)
+            r, _ = run_gpu(w, side_steps, side_warm, cache, False, scratch)
+            r.pop("_gpu")
             gateless.append(dict(r, roofline=roofline(r)))
+    if not args.no_workloads and args.workload != "tiny":
+        others.append(run_gpu("tiny", side_steps, side_warm, cache, False, scratch))
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(inp)
+        cpu = cpu_baseline(inp, head["_gpu"])
+        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads; parity {cpu['parity']}")
+        # a bounded oracle leg per side record: its time, and the parity of that record
+        for r, winp in ([(side, side_inp)] if side is not None else []) + others:
+            r["cpu_baseline"] = cpu_baseline(winp, r["_gpu"], max_tokens=16, min_seconds=0.0, max_reps=1)
+            log(f"[bench] {r['workload']}: oracle parity {r['cpu_baseline']['parity']}")
+    head.pop("_gpu")
 
     rec = {
         "metric": METRIC,
@@ -493,10 +600,16 @@ def main():
                    "parallelism": "none (one GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parity": cpu["parity"] if cpu else None,
+        "deterministic": head["deterministic"],
         "detail": head,
     }
     if side is not None:
+        side.pop("_gpu")
         rec["prefill"] = dict(side, roofline=roofline(side))
+    for r, _ in others:
+        r.pop("_gpu")
+        rec[r["workload"]] = dict(r, roofline=roofline(r))
     if quant is not None:
         rec["weight_quantizer"] = quant
     if bwd is not None:
