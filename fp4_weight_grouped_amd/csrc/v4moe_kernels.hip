@@ -772,29 +772,18 @@ __device__ __forceinline__ void build_tiles_block(int E, int M, int NB1, int NB2
         ctrl[2] = build_queue == 1 ? total * (NB1 + NB2) : 0;
     }
     if (build_queue == 2) {
-        // Per-XCD m-tile lists for the two-launch FFN: expert e belongs to
-        // group e % 8 (the XCD that runs blocks b with b % 8 == group), its
-        // m-tiles in order; group x's list is queue[ctrl[16+x] ..], ctrl[24+x]
-        // entries long.  All m-tiles of an expert, and all column blocks of an
-        // m-tile, then share one XCD's L2.
-        __shared__ int gcount[8];
+        // Per-XCD m-tile lists for the two-launch FFN: the m-tiles, in expert
+        // order, cut into eight contiguous ranges of equal length (+-1); range
+        // x runs on XCD x (the blocks b with b % 8 == x) and is queue[ctrl[16+x]
+        // ..], ctrl[24+x] entries long.  Consecutive m-tiles of an expert, and
+        // all column blocks of an m-tile, then share one XCD's L2, and a hot
+        // expert's m-tiles spread over as many XCDs as their count needs.
         if (tid < 8) {
-            int c = 0;
-            for (int e2 = tid; e2 < E; e2 += 8) c += base[e2 + 1] - base[e2];
-            gcount[tid] = c;
+            const int s0 = (int)((long long)tid * total / 8), s1 = (int)((long long)(tid + 1) * total / 8);
+            ctrl[16 + tid] = s0;
+            ctrl[24 + tid] = s1 - s0;
         }
-        __syncthreads();
-        int gstart = 0;
-        for (int x = 0; x < (tid & 7); x++) gstart += gcount[x];
-        if (tid < 8) {
-            ctrl[16 + tid] = gstart;
-            ctrl[24 + tid] = gcount[tid];
-        }
-        if (tid < E) {
-            int pos = gstart;
-            for (int e2 = tid & 7; e2 < tid; e2 += 8) pos += base[e2 + 1] - base[e2];
-            for (int m = 0; m < n; m++) queue[pos + m] = (uint32_t)(my_base + m);
-        }
+        for (int i = tid; i < total; i += 1024) queue[i] = (uint32_t)i;
         return;
     }
     if (build_queue != 1) return;
