@@ -9,7 +9,10 @@ reported alongside.  Weights are random FP4 E2M1 with power-of-two sub-block
 scales and fp32 128x128 block scales (seed 0).
 
 Roofline of the dominant kernel (the expert-FFN kernel), timed with HIP events
-that the library records around it on its own stream in every timed step:
+that the library records around it on its own stream, in an instrumented pass
+of the same number of steps right after the contract loop (recording events
+between kernels adds a few microseconds per step, so the contract loop runs
+bare steps):
   decode:  algorithmic bytes = active experts x (FP4 codes + E8M0 sub-block
            scales + fp32 block scales) = 13,375,488 B each, against 8 TB/s;
   prefill: algorithmic FLOP = 2*T*k*3*H*I against the dense FP8 peak 5.0 PFLOP/s.
@@ -217,11 +220,13 @@ SCRATCH_BYTES = 512 << 20      # written between protocol steps: 2x the 256 MB l
 def run_gpu(name, steps, warmup, layer_cache, extras=True, scratch=None):
     """Time one workload.  The contract loop: `steps` back-to-back layer
     forwards, bracketed by synchronisations (ms_per_step, tokens/s).  The
-    cold-cache protocol loop: the same number of steps, each preceded by a
-    write of SCRATCH_BYTES (outside its HIP events), so weights and
-    activations come from HBM; per-step device times from those events.
-    Determinism: the output of the first and the last timed step of both
-    loops must be bit-identical."""
+    instrumented pass: the same steps with HIP events around each step and
+    around each FFN launch (the roofline's kernel time).  The cold-cache
+    protocol loop: the same number of steps, each preceded by a write of
+    SCRATCH_BYTES (outside its HIP events), so weights and activations come
+    from HBM; per-step device times from those events.  Determinism: the
+    output of every pass must equal that of a step run before them, bit for
+    bit."""
     import torch
     from fp4_weight_grouped_amd import inputs, v4moe
 
@@ -254,21 +259,29 @@ def run_gpu(name, steps, warmup, layer_cache, extras=True, scratch=None):
     for _ in range(warmup):
         layer.forward(x, bias, inp.mode, tid, out=out)
     torch.cuda.synchronize()
-    first = None
-    ev, sev = new_events(steps), new_events(steps)
+    first = layer.forward(x, bias, inp.mode, tid)[0]
+    # the contract loop: `steps` bare layer forwards back to back
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        sev[i][0].record()
-        v4moe.moe_time_next_ffn(*ev[i])
         _, ids, w, off = layer.forward(x, bias, inp.mode, tid, out=out)
-        sev[i][1].record()
-        if i == 0:
-            first = out.clone()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     deterministic = bool(torch.equal(first, out))
     ms_step = (t1 - t0) * 1e3 / steps
+    # the instrumented pass right after it: HIP events around each step and,
+    # recorded by the library on its launch stream, around each FFN launch
+    # (recording them adds a few microseconds between kernels, so they are
+    # kept out of the contract loop)
+    ev, sev = new_events(steps), new_events(steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        sev[i][0].record()
+        v4moe.moe_time_next_ffn(*ev[i])
+        layer.forward(x, bias, inp.mode, tid, out=out)
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    deterministic = deterministic and bool(torch.equal(first, out))
     ffn_all = [a.elapsed_time(b) for a, b in ev]
     step_all = [a.elapsed_time(b) for a, b in sev]
     ffn_ms = float(np.mean(ffn_all))

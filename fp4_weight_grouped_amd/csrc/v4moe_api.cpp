@@ -279,12 +279,14 @@ int layer_forward_ws(
     int32_t* pp = reinterpret_cast<int32_t*>(ws + L.pair_pos);
     uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
     // Small batches: the permutation and the tile list run as one block (same
-    // device code, same results).
+    // device code, same results).  Decode-sized batches: the router also
+    // writes the FP8 dispatch payload.
     const bool fuse = perm_tiles_one_block(d->T, d->topk, d->E);
     if (launch_route(d->T, d->H, d->E, d->topk, x, w_router, bias, mode, token_ids, topk_ids, topk_w,
-                     reinterpret_cast<float*>(ws + L.z), s) != hipSuccess)
+                     reinterpret_cast<float*>(ws + L.z), s, xq, xs) != hipSuccess)
         return V4MOE_ELAUNCH;
-    if (launch_quant_x(d->T, d->H, x, xq, xs, s) != hipSuccess) return V4MOE_ELAUNCH;
+    if (!route_writes_payload(d->T, d->H, d->E, mode) && launch_quant_x(d->T, d->H, x, xq, xs, s) != hipSuccess)
+        return V4MOE_ELAUNCH;
     if (!fuse && launch_permute(d->T, d->topk, d->E, topk_ids, expert_offsets, sp, pp,
                                 reinterpret_cast<int32_t*>(ws + L.hist), s) != hipSuccess)
         return V4MOE_ELAUNCH;

@@ -50,9 +50,14 @@ struct FfnArgs {
     float* u_out;              // optional [T*topk][I]: linear1 up outputs, or null
 };
 
+// Routing.  With xq/xs given, the decode-sized router (route_writes_payload)
+// also writes the FP8 dispatch payload of x (what launch_quant_x writes);
+// otherwise they are ignored and the caller launches launch_quant_x.
+bool route_writes_payload(int T, int H, int E, int mode);
 hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
                         const float* bias, int mode, const int64_t* token_ids,
-                        int32_t* ids, float* w, float* z, hipStream_t s);
+                        int32_t* ids, float* w, float* z, hipStream_t s,
+                        uint8_t* xq = nullptr, float* xs = nullptr);
 hipError_t launch_quant_x(int T, int H, const uint16_t* x, uint8_t* xq, float* xs, hipStream_t s);
 hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos, int32_t* hist, hipStream_t s);

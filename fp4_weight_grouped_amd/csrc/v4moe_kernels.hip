@@ -63,6 +63,26 @@ __device__ __forceinline__ T* uniform(T* p)
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
+// One 128-channel group of the FP8 dispatch payload held by 16 consecutive
+// lanes, 8 channels each (f): amax over the group, s = amax / 448 (1 for an
+// all-zero group), codes = E4M3(f / s).  Every lane of the 16 must call it;
+// lanes with store = false only take part in the reduction.  The scale goes
+// to *scale when that pointer is not null.
+__device__ __forceinline__ void x_quant_group(const float (&f)[8], bool store, uint8_t* q8, float* scale)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; u++) amax = fmaxf(amax, fabsf(f[u]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (!store) return;
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const uint32_t lo = e4m3x2(f[0] / s, f[1] / s) | (e4m3x2(f[2] / s, f[3] / s) << 16);
+    const uint32_t hi = e4m3x2(f[4] / s, f[5] / s) | (e4m3x2(f[6] / s, f[7] / s) << 16);
+    *reinterpret_cast<uint2*>(q8) = make_uint2(lo, hi);
+    if (scale) *scale = s;
+}
+
 // Router logits, every variant: z[t][e] is one fp32 fma chain over h
 // ascending from +0 (x exact as float), plus the optional bias as one fp32 add
 // afterwards.  The variants differ only in which chains a lane runs and how the
@@ -252,7 +272,8 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
 template <int EL, int NTW, int RH, int NS>
 __global__ __launch_bounds__(64 * (NTW + 1)) void k_route_lane(int T, int H, int E, const uint16_t* __restrict__ x,
                                                              const float* __restrict__ wr,
-                                                             const float* __restrict__ bias, float* __restrict__ z)
+                                                             const float* __restrict__ bias, float* __restrict__ z,
+                                                             uint8_t* __restrict__ xq, float* __restrict__ xs)
 {
     constexpr int TPW = 64 / EL;                 // tokens per consumer wave
     constexpr int NTOK = NTW * TPW;              // tokens per block
@@ -300,13 +321,23 @@ __global__ __launch_bounds__(64 * (NTW + 1)) void k_route_lane(int T, int H, int
             const int ahead = min(NS - 2, nst - 1 - s);
             if (ahead >= 2) wait_vm<A2>(); else if (ahead == 1) wait_vm<OPS>(); else wait_vm<0>();
             const int slot = s % NS;
+            // with xq: the stages s = eg (mod groups of experts) of the block's
+            // tokens also get their FP8 dispatch payload here (x_quant_group:
+            // 16 lanes per 128-channel group), so each is written exactly once
+            const bool quant = xq != nullptr && s % neg == eg;
             for (int g = lane; g < NTOK * XSEG; g += 64) {
                 const uint4 q = xst[slot][g];
+                float f[8] = {bf16_to_f32(q.x & 0xFFFFu), bf16_to_f32(q.x >> 16), bf16_to_f32(q.y & 0xFFFFu),
+                              bf16_to_f32(q.y >> 16), bf16_to_f32(q.z & 0xFFFFu), bf16_to_f32(q.z >> 16),
+                              bf16_to_f32(q.w & 0xFFFFu), bf16_to_f32(q.w >> 16)};
                 float* d = &xf[slot][g / XSEG][(g % XSEG) * 8];
-                *reinterpret_cast<float4*>(d) = make_float4(bf16_to_f32(q.x & 0xFFFFu), bf16_to_f32(q.x >> 16),
-                                                            bf16_to_f32(q.y & 0xFFFFu), bf16_to_f32(q.y >> 16));
-                *reinterpret_cast<float4*>(d + 4) = make_float4(bf16_to_f32(q.z & 0xFFFFu), bf16_to_f32(q.z >> 16),
-                                                                bf16_to_f32(q.w & 0xFFFFu), bf16_to_f32(q.w >> 16));
+                *reinterpret_cast<float4*>(d) = make_float4(f[0], f[1], f[2], f[3]);
+                *reinterpret_cast<float4*>(d + 4) = make_float4(f[4], f[5], f[6], f[7]);
+                if (quant) {
+                    const int t = t0 + g / XSEG;
+                    const size_t off = (size_t)min(t, T - 1) * H + (size_t)s * RH + (g % XSEG) * 8;
+                    x_quant_group(f, t < T, xq + off, t < T && (g & 15) == 0 ? xs + off / 128 : nullptr);
+                }
             }
             __syncthreads();
             // slot (s-1) % NS is free: every consumer finished stage s-1 before this barrier
@@ -495,8 +526,7 @@ __global__ __launch_bounds__(256) void k_quant_x(int T, int H, const uint16_t* _
     const size_t total = (size_t)T * H / 8;
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     const bool ok = idx < total;
-    float f[8];
-    float amax = 0.0f;
+    float f[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     if (ok) {
         uint4 v = *reinterpret_cast<const uint4*>(x + idx * 8);
         uint32_t q[4] = {v.x, v.y, v.z, v.w};
@@ -505,17 +535,8 @@ __global__ __launch_bounds__(256) void k_quant_x(int T, int H, const uint16_t* _
             f[2 * u] = bf16_to_f32(q[u] & 0xFFFFu);
             f[2 * u + 1] = bf16_to_f32(q[u] >> 16);
         }
-#pragma unroll
-        for (int u = 0; u < 8; u++) amax = fmaxf(amax, fabsf(f[u]));
     }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if (!ok) return;
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-    const uint32_t lo = e4m3x2(f[0] / s, f[1] / s) | (e4m3x2(f[2] / s, f[3] / s) << 16);
-    const uint32_t hi = e4m3x2(f[4] / s, f[5] / s) | (e4m3x2(f[6] / s, f[7] / s) << 16);
-    *reinterpret_cast<uint2*>(xq + idx * 8) = make_uint2(lo, hi);
-    if ((idx & 15) == 0) xs[idx / 16] = s;
+    x_quant_group(f, ok, xq + (ok ? idx * 8 : 0), ok && (idx & 15) == 0 ? xs + idx / 16 : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -526,26 +547,43 @@ __global__ __launch_bounds__(256) void k_quant_x(int T, int H, const uint16_t* _
 // follow pair order exactly.  Pass <true> writes per-block counts; the scan
 // turns them into per-block bases; pass <false> writes the positions.
 // ---------------------------------------------------------------------------
+// The expert ids of one chunk of kPermChunk pairs starting at p0, for one wave:
+// ev[i] = id of pair p0 + 64i + lane, or -1 past the end.  Loaded once, all
+// in flight together, and used by both passes.
+__device__ __forceinline__ void load_chunk_ids(int P, int p0, int lane, const int32_t* __restrict__ ids,
+                                               int (&ev)[kPermChunk / 64])
+{
+#pragma unroll
+    for (int i = 0; i < kPermChunk / 64; i++) {
+        const int p = p0 + 64 * i + lane;
+        ev[i] = p < P ? ids[p] : -1;
+    }
+}
+
+// Bits of an expert-id key: ids are < E and E itself marks an invalid pair.
+__device__ __forceinline__ int id_key_bits(int E) { return 32 - __clz(E); }
+
 // One wave over one chunk of kPermChunk pairs starting at p0, in pair order.
 // cnt[E] (LDS) holds the chunk's running per-expert counts (zero on entry).
 // A pair's rank among the equal-expert pairs of its 64 is found by ballots
-// over the 11 bits of the expert id.  Count pass: cnt ends as the chunk's
+// over the bits of the expert id.  Count pass: cnt ends as the chunk's
 // histogram.  Position pass: pair p goes to row[e] + (earlier pairs of e in
 // the chunk), row[e] being the chunk's base for expert e.
 template <bool kCount>
-__device__ __forceinline__ void perm_chunk(int P, int p0, int lane, const int32_t* __restrict__ ids,
+__device__ __forceinline__ void perm_chunk(int p0, int lane, int E, const int (&ev)[kPermChunk / 64],
                                            int32_t* cnt, const int32_t* row,
                                            int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos)
 {
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int it = 0; it < kPermChunk; it += 64) {
-        const int p = p0 + it + lane;
-        const bool valid = p < P;
-        const int e = valid ? ids[p] : 0;
-        const uint32_t key = valid ? (uint32_t)e : 0x7FFu;
-        uint64_t peers = ~0ull;
+    const int nbits = id_key_bits(E);
 #pragma unroll
-        for (int bit = 0; bit < 11; bit++) {
+    for (int i = 0; i < kPermChunk / 64; i++) {
+        const int p = p0 + 64 * i + lane;
+        const bool valid = ev[i] >= 0;
+        const int e = valid ? ev[i] : 0;
+        const uint32_t key = valid ? (uint32_t)e : (uint32_t)E;
+        uint64_t peers = ~0ull;
+        for (int bit = 0; bit < nbits; bit++) {
             const bool bb = (key >> bit) & 1u;
             const uint64_t m = __ballot(bb);
             peers &= bb ? m : ~m;
@@ -578,7 +616,9 @@ __global__ __launch_bounds__(64) void k_perm_pass(int P, int E, const int32_t* _
     int32_t* row = hist + (size_t)b * E;
     for (int e = lane; e < E; e += 64) cnt[e] = 0;
     __syncthreads();
-    perm_chunk<kCount>(P, b * kPermChunk, lane, ids, cnt, row, sorted_pair, pair_pos);
+    int ev[kPermChunk / 64];
+    load_chunk_ids(P, b * kPermChunk, lane, ids, ev);
+    perm_chunk<kCount>(b * kPermChunk, lane, E, ev, cnt, row, sorted_pair, pair_pos);
     if (kCount) {
         __syncthreads();
         for (int e = lane; e < E; e += 64) row[e] = cnt[e];
@@ -674,19 +714,21 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __
 // The whole permutation in one 1024-thread block when there are at most 16
 // chunks (wave w handles chunk w): histograms, offsets and per-chunk bases,
 // positions.  Same results as the three kernels above.  LDS: hist[nblk][E]
-// then cnt[nblk][E].
+// then cnt[nblk][E]; off_lds (E+1 ints, optional) receives the offsets too.
 __device__ __forceinline__ void perm_small_block(int P, int E, const int32_t* __restrict__ ids,
                                                  int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
-                                                 int32_t* __restrict__ pair_pos, int32_t* sh)
+                                                 int32_t* __restrict__ pair_pos, int32_t* sh, int32_t* off_lds)
 {
     __shared__ int total_s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nblk = (P + kPermChunk - 1) / kPermChunk;
     int32_t* hist = sh;
     int32_t* cnt = sh + nblk * E;
+    int ev[kPermChunk / 64];
+    if (w < nblk) load_chunk_ids(P, w * kPermChunk, lane, ids, ev);
     for (int i = tid; i < 2 * nblk * E; i += 1024) sh[i] = 0;
     __syncthreads();
-    if (w < nblk) perm_chunk<true>(P, w * kPermChunk, lane, ids, hist + w * E, nullptr, sorted_pair, pair_pos);
+    if (w < nblk) perm_chunk<true>(w * kPermChunk, lane, E, ev, hist + w * E, nullptr, sorted_pair, pair_pos);
     __syncthreads();
     int tot = 0;
     if (tid < E)
@@ -694,6 +736,7 @@ __device__ __forceinline__ void perm_small_block(int P, int E, const int32_t* __
     const int off = block_exclusive_scan(tid < E ? tot : 0, &total_s);
     if (tid < E) {
         offsets[tid] = off;
+        if (off_lds) off_lds[tid] = off;
         int run = off;
         for (int b = 0; b < nblk; b++) {
             const int c = hist[b * E + tid];
@@ -701,9 +744,12 @@ __device__ __forceinline__ void perm_small_block(int P, int E, const int32_t* __
             run += c;
         }
     }
-    if (tid == 0) offsets[E] = total_s;
+    if (tid == 0) {
+        offsets[E] = total_s;
+        if (off_lds) off_lds[E] = total_s;
+    }
     __syncthreads();
-    if (w < nblk) perm_chunk<false>(P, w * kPermChunk, lane, ids, cnt + w * E, hist + w * E, sorted_pair, pair_pos);
+    if (w < nblk) perm_chunk<false>(w * kPermChunk, lane, E, ev, cnt + w * E, hist + w * E, sorted_pair, pair_pos);
 }
 __global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t* __restrict__ ids,
                                                      int32_t* __restrict__ offsets,
@@ -711,7 +757,7 @@ __global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t
                                                      int32_t* __restrict__ pair_pos)
 {
     extern __shared__ int32_t sh[];
-    perm_small_block(P, E, ids, offsets, sorted_pair, pair_pos, sh);
+    perm_small_block(P, E, ids, offsets, sorted_pair, pair_pos, sh, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -725,7 +771,7 @@ __global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t
 // phase<<31 | mtile<<8 | n-block.  Also clears the persistent kernel's counters.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void build_tiles_block(int E, int M, int NB1, int NB2, int build_queue, int D,
-                                                  const int32_t* __restrict__ offsets,
+                                                  const int32_t* offsets,
                                                   int32_t* __restrict__ mt_expert, int32_t* __restrict__ mt_row0,
                                                   int32_t* __restrict__ ctrl, int32_t* __restrict__ done1,
                                                   uint32_t* __restrict__ queue)
@@ -827,9 +873,11 @@ __global__ __launch_bounds__(1024) void k_perm_tiles(int P, int E, const int32_t
                                                      int32_t* __restrict__ done1, uint32_t* __restrict__ queue)
 {
     extern __shared__ int32_t sh[];
-    perm_small_block(P, E, ids, offsets, sorted_pair, pair_pos, sh);
+    __shared__ int32_t off_lds[1025];
+    perm_small_block(P, E, ids, offsets, sorted_pair, pair_pos, sh, off_lds);
     __syncthreads();
-    build_tiles_block(E, M, NB1, NB2, build_queue, D, offsets, mt_expert, mt_row0, ctrl, done1, queue);
+    // the tile list reads the offsets from LDS, not back from global memory
+    build_tiles_block(E, M, NB1, NB2, build_queue, D, off_lds, mt_expert, mt_row0, ctrl, done1, queue);
 }
 
 // ---------------------------------------------------------------------------
@@ -1646,10 +1694,16 @@ __global__ __launch_bounds__(256) void k_dequant_export(int N, int K, int expert
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
+bool route_writes_payload(int T, int H, int E, int mode)
+{
+    return mode == 0 && E % 4 == 0 && H % 256 == 0 && E >= 32 && (long long)T * E <= 32768;
+}
+
 hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const float* wr,
                         const float* bias, int mode, const int64_t* token_ids,
-                        int32_t* ids, float* w, float* z, hipStream_t s)
+                        int32_t* ids, float* w, float* z, hipStream_t s, uint8_t* xq, float* xs)
 {
+    if (!route_writes_payload(T, H, E, mode)) xq = nullptr, xs = nullptr;
     if (mode == 1) {
         hipLaunchKernelGGL(k_route_hash, dim3(blocks_for(T, 256)), dim3(256), 0, s, T, E, k,
                            token_ids, ids, w);
@@ -1666,11 +1720,11 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
     if (E % 4 != 0 || H % 256 != 0) {
         hipLaunchKernelGGL(k_route_logits_any, dim3(blocks_for((size_t)T * E, 256)), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
-    } else if (E >= 32 && chains <= 32768) {
+    } else if (route_writes_payload(T, H, E, 0)) {
         constexpr int EL = 32, NTW = 2;
         const unsigned grid = (unsigned)(((T + NTW * 2 - 1) / (NTW * 2)) * ((E + EL - 1) / EL));
         hipLaunchKernelGGL((k_route_lane<EL, NTW, 256, 3>), dim3(grid), dim3(64 * (NTW + 1)), 0, s, T, H, E, x, wr,
-                           bias, z);
+                           bias, z, xq, xs);
     } else if (E % 32 == 0 && (size_t)((T + 127) / 128) * (E / 32) >= 512) {
         hipLaunchKernelGGL((k_route_logits<2, 8, 256, false>), dim3((T + 127) / 128, E / 32), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
