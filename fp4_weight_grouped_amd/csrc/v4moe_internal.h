@@ -42,7 +42,8 @@ struct FfnArgs {
     uint16_t* y;               // [T*topk][H] bf16, row = pair id
     const int32_t* mt_expert;  // [n_mt_bound] expert of each m-tile
     const int32_t* mt_row0;    // [n_mt_bound] first sorted row of each m-tile
-    int32_t* ctrl;             // [0] number of m-tiles, [1] queue head, [2] queue length
+    int32_t* ctrl;             // [0] number of m-tiles, [1] queue head, [2] queue length, [4] start of the
+                               // linear2 tile list (two launches), [16+x], [24+x] XCD x's m-tile range
     int32_t* done1;            // [n_mt_bound] finished linear1 tiles per m-tile
     const uint32_t* queue;     // persistent schedule, or the per-XCD m-tile lists
     int xcd_groups;            // two-launch FFN: m-tiles grouped by XCD (k_build_tiles mode 2)

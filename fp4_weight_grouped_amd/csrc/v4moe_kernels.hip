@@ -818,18 +818,36 @@ __device__ __forceinline__ void build_tiles_block(int E, int M, int NB1, int NB2
         ctrl[2] = build_queue == 1 ? total * (NB1 + NB2) : 0;
     }
     if (build_queue == 2) {
-        // Per-XCD m-tile lists for the two-launch FFN: the m-tiles, in expert
+        // Per-XCD tile lists for the two-launch FFN: the m-tiles, in expert
         // order, cut into eight contiguous ranges of equal length (+-1); range
-        // x runs on XCD x (the blocks b with b % 8 == x) and is queue[ctrl[16+x]
-        // ..], ctrl[24+x] entries long.  Consecutive m-tiles of an expert, and
-        // all column blocks of an m-tile, then share one XCD's L2, and a hot
-        // expert's m-tiles spread over as many XCDs as their count needs.
+        // x = m-tiles ctrl[16+x] .. + ctrl[24+x] runs on XCD x (the blocks b
+        // with b % 8 == x).  Its tiles are listed with each expert's column
+        // blocks outer and that expert's m-tiles (within the range) inner, so
+        // the tiles that read the same weights are dispatched next to each
+        // other on one XCD and share its L2, and the column blocks of an
+        // m-tile (the same activation rows) follow closely; a hot expert's
+        // m-tiles spread over as many XCDs as their count needs.  Linear1
+        // list: queue[s0*NB1 ..]; linear2 list: queue[ctrl[4] + s0*NB2 ..];
+        // entry = m-tile<<8 | column block.
         if (tid < 8) {
             const int s0 = (int)((long long)tid * total / 8), s1 = (int)((long long)(tid + 1) * total / 8);
             ctrl[16 + tid] = s0;
             ctrl[24 + tid] = s1 - s0;
         }
-        for (int i = tid; i < total; i += 1024) queue[i] = (uint32_t)i;
+        if (tid == 0) ctrl[4] = total * NB1;
+        if (n > 0) {
+            for (int x = 0; x < 8; x++) {
+                const int s0 = (int)((long long)x * total / 8), s1 = (int)((long long)(x + 1) * total / 8);
+                const int g0 = max(my_base, s0), g1 = min(my_base + n, s1), gl = g1 - g0;
+                for (int i = g0; i < g1; i++) {
+                    for (int nb = 0; nb < NB1; nb++)
+                        queue[(size_t)g0 * NB1 + nb * gl + (i - g0)] = ((uint32_t)i << 8) | (uint32_t)nb;
+                    for (int nb = 0; nb < NB2; nb++)
+                        queue[(size_t)total * NB1 + (size_t)g0 * NB2 + nb * gl + (i - g0)] =
+                            ((uint32_t)i << 8) | (uint32_t)nb;
+                }
+            }
+        }
         return;
     }
     if (build_queue != 1) return;
@@ -967,7 +985,10 @@ __device__ __forceinline__ void wait_stages(int k)
     else wait_vm<0>();
 }
 
-__host__ __device__ constexpr int ring_stages(int MT) { return MT == 1 ? 4 : 3; }
+// Ring depth: 128-row m-tiles with two wave columns keep two stages, so that
+// two blocks share a CU (each block's per-chunk barrier and operand reads
+// then overlap the other's MFMAs).
+__host__ __device__ constexpr int ring_stages(int MT, int CW) { return MT == 1 ? 4 : (MT == 8 && CW == 2 ? 2 : 3); }
 
 template <int MT, int RW, int CW>
 struct TileLayout {
@@ -978,7 +999,7 @@ struct TileLayout {
     static constexpr int RG = M / RW;                        // rows per row group
     static constexpr int HC = 64 * CW;                       // phase-1 columns of h
     static constexpr int OC = 128 * CW;                      // phase-2 output columns
-    static constexpr int NS = ring_stages(MT);
+    static constexpr int NS = ring_stages(MT, CW);
     static constexpr int NBR = 8 / RW;                       // B records per wave per stage
     static constexpr int NSR = 2 / RW;                       // scale records per wave per stage
     static constexpr int AB = M / 8;                         // 1 KiB A blocks per stage
@@ -1356,13 +1377,13 @@ __global__ __launch_bounds__(64 * RW * CW) void k_ffn(FfnArgs a, int NB)
     extern __shared__ __align__(16) uint8_t smem[];
     int mt, nb;
     if (a.xcd_groups) {
-        // block b runs on XCD b % 8 (round-robin dispatch): item b / 8 of that
-        // group's m-tile list, column block fastest
+        // block b runs on XCD b % 8 (round-robin dispatch): entry b / 8 of
+        // that XCD's tile list
         const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-        const int li = j / NB;
-        if (li >= a.ctrl[24 + x]) return;
-        nb = j % NB;
-        mt = (int)a.queue[a.ctrl[16 + x] + li];
+        if (j >= a.ctrl[24 + x] * NB) return;
+        const uint32_t it = a.queue[(PHASE == 1 ? 0 : a.ctrl[4]) + a.ctrl[16 + x] * NB + j];
+        mt = (int)(it >> 8);
+        nb = (int)(it & 0xFFu);
     } else {
         mt = blockIdx.x / NB;
         nb = blockIdx.x % NB;
@@ -1812,8 +1833,10 @@ static hipError_t launch_ffn_t(const FfnArgs& a, hipStream_t s)
     const int NB = PHASE == 1 ? a.I / (TL::HC * (G ? 1 : 2)) : a.H / TL::OC;
     const size_t lds = TL::BYTES;
     if (allow_lds(k_ffn<PHASE, MT, RW, CW, G>, lds, lds_ok) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_ffn<PHASE, MT, RW, CW, G>), dim3((unsigned)a.n_mt_bound * NB * (a.xcd_groups ? 8 : 1)), dim3(TL::NT), lds, s, a,
-                       NB);
+    // per-XCD lists: each holds at most ceil(n_mt_bound / 8) m-tiles
+    const unsigned grid = a.xcd_groups ? 8u * (unsigned)NB * (unsigned)((a.n_mt_bound + 7) / 8)
+                                       : (unsigned)a.n_mt_bound * NB;
+    hipLaunchKernelGGL((k_ffn<PHASE, MT, RW, CW, G>), dim3(grid), dim3(TL::NT), lds, s, a, NB);
     return hipGetLastError();
 }
 
@@ -1968,13 +1991,15 @@ int choose_mt(int T, int k, int E)
 
 int choose_cw(int MT, int H, int I, bool gated)
 {
-    // Four wave columns whenever the shape divides: for large m-tiles (MFMA-
-    // bound) they halve the operand traffic per MFMA; for the weight-streaming
-    // small m-tiles one four-wave block per CU with twice the bytes per ring
-    // stage measured faster than two two-wave blocks (T = 128: 0.558 -> 0.541
-    // ms; T = 512 and 1024: 5% faster).  A linear1 tile spans 64*CW columns of
-    // h gated, 128*CW gate-less.
-    (void)MT;
+    // Weight-streaming small m-tiles: four wave columns whenever the shape
+    // divides; one four-wave block per CU with twice the bytes per ring stage
+    // measured faster than two two-wave blocks (T = 128: 0.558 -> 0.541 ms;
+    // T = 512 and 1024: 5% faster).  128-row m-tiles (MFMA-bound): two wave
+    // columns and a two-stage ring, two blocks per CU, measured 6% faster at
+    // T = 8192 than one eight-wave block with four columns and three stages,
+    // though each block reads its activation rows for half the columns.  A
+    // linear1 tile spans 64*CW columns of h gated, 128*CW gate-less.
+    if (MT == 8) return 2;
     return (I % (gated ? 256 : 512) == 0 && H % 512 == 0) ? 4 : 2;
 }
 
