@@ -1994,12 +1994,14 @@ int choose_cw(int MT, int H, int I, bool gated)
     // Weight-streaming small m-tiles: four wave columns whenever the shape
     // divides; one four-wave block per CU with twice the bytes per ring stage
     // measured faster than two two-wave blocks (T = 128: 0.558 -> 0.541 ms;
-    // T = 512 and 1024: 5% faster).  128-row m-tiles (MFMA-bound): two wave
-    // columns and a two-stage ring, two blocks per CU, measured 6% faster at
+    // T = 512 and 1024: 5% faster).  128-row m-tiles (MFMA-bound), gated: two
+    // wave columns and a two-stage ring, two blocks per CU, measured 6% faster at
     // T = 8192 than one eight-wave block with four columns and three stages,
     // though each block reads its activation rows for half the columns.  A
-    // linear1 tile spans 64*CW columns of h gated, 128*CW gate-less.
-    if (MT == 8) return 2;
+    // linear1 tile spans 64*CW columns of h gated, 128*CW gate-less.  (The
+    // gate-less two-column linear1 tile needs more than 256 registers, so it
+    // keeps the four-column layout.)
+    if (MT == 8 && gated) return 2;
     return (I % (gated ? 256 : 512) == 0 && H % 512 == 0) ? 4 : 2;
 }
 
