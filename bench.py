@@ -77,9 +77,13 @@ def ffn_flops(T: int, k: int, H: int, I: int, mats: int = 3) -> int:
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the HIP/C++ sources of the library, in file-name order."""
+    """sha256 over the sources the layer forward is built from (every file of
+    the library's csrc/ except the backward kernels, v4moe_bwd.hip), in
+    file-name order."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "fp4_weight_grouped_amd", "csrc", "*"))):
+        if os.path.basename(f) == "v4moe_bwd.hip":
+            continue
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
