@@ -444,37 +444,43 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
 
 // Top-k per token (one wave per token): the k largest logits, the lower expert
 // id winning ties, slot j = j-th pick; then lanes 0..k-1 compute the affinity
-// sqrt(softplus(z)) and the weights normalised over the k picks.  z is [T][E].
+// sqrt(softplus(z)) and the weights normalised over the k picks.  z is [T][E];
+// lane l holds experts l + 64q, q < NQ (NQ*64 >= E).  Each lane keeps the
+// largest key of its experts not yet picked; a round takes the wave maximum
+// of those, and only the lane that held the pick finds its next best.
+template <int NQ>
 __device__ __forceinline__ void select_token(int t, int lane, int E, int k, const float* __restrict__ zg,
                                              int32_t* __restrict__ ids, float* __restrict__ wts)
 {
     const float* z = zg + (size_t)t * E;
-    float zv[16];
+    // key = order-preserving bits of z above the complemented id: the largest
+    // key is the largest z, the lower id on equal z; 0 = none (a real key has
+    // ~id != 0 in its low half)
+    uint64_t cand[NQ];
 #pragma unroll
-    for (int q = 0; q < 16; q++) {
+    for (int q = 0; q < NQ; q++) {
         const int e = lane + 64 * q;
-        zv[q] = (q * 64 < E && e < E) ? z[e] : 0.0f;
+        cand[q] = e < E ? ((uint64_t)float_order_key(z[e]) << 32) | (uint32_t)~e : 0;
     }
-    uint32_t taken = 0;  // bit q: expert lane + 64q already picked
+    auto best_of = [&]() {
+        uint64_t b = 0;
+#pragma unroll
+        for (int q = 0; q < NQ; q++) b = cand[q] > b ? cand[q] : b;
+        return b;
+    };
+    uint64_t best = best_of();
     float my_z = 0.0f;
     int my_e = 0;
     for (int j = 0; j < k; j++) {
-        // key = order-preserving bits of z above the complemented id: the
-        // largest key is the largest z, the lower id on equal z; 0 = none
-        uint64_t key = 0;
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-            const int e = lane + 64 * q;
-            if (q * 64 < E && e < E && !((taken >> q) & 1u)) {
-                const uint64_t c = ((uint64_t)float_order_key(zv[q]) << 32) | (uint32_t)~e;
-                key = c > key ? c : key;
-            }
-        }
-        key = wave_max_key(key);
+        const uint64_t key = wave_max_key(best);
         const int be = (int)~(uint32_t)key;
-        const float bv = float_from_order_key((uint32_t)(key >> 32));
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) { my_z = bv; my_e = be; }
+        if ((be & 63) == lane) {
+#pragma unroll
+            for (int q = 0; q < NQ; q++)
+                if (q == (be >> 6)) cand[q] = 0;
+            best = best_of();
+        }
+        if (lane == j) { my_z = float_from_order_key((uint32_t)(key >> 32)); my_e = be; }
     }
     // affinity sqrt(softplus(z)), softplus(z) = max(z,0) + log1p(exp(-|z|))
     const float a = sqrtf(fmaxf(my_z, 0.0f) + log1pf(expf(-fabsf(my_z))));
@@ -485,12 +491,13 @@ __device__ __forceinline__ void select_token(int t, int lane, int E, int k, cons
         wts[(size_t)t * k + lane] = sum > 0.0f ? a / sum : 1.0f / (float)k;
     }
 }
+template <int NQ>
 __global__ __launch_bounds__(256) void k_route_select(int T, int E, int k, const float* __restrict__ zg,
                                                       int32_t* __restrict__ ids, float* __restrict__ wts)
 {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    select_token(t, threadIdx.x & 63, E, k, zg, ids, wts);
+    select_token<NQ>(t, threadIdx.x & 63, E, k, zg, ids, wts);
 }
 
 // Hash routing: expert_j = splitmix64(id*k + j) mod E, +1 mod E past repeats.
@@ -1759,7 +1766,12 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
         hipLaunchKernelGGL((k_route_logits<1, 1, 256, true>), dim3((T + 63) / 64, E / 4), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
     }
-    hipLaunchKernelGGL(k_route_select, dim3(blocks_for(T, 4)), dim3(256), 0, s, T, E, k, z, ids, w);
+    const dim3 sg(blocks_for(T, 4));
+    if (E <= 64) hipLaunchKernelGGL(k_route_select<1>, sg, dim3(256), 0, s, T, E, k, z, ids, w);
+    else if (E <= 128) hipLaunchKernelGGL(k_route_select<2>, sg, dim3(256), 0, s, T, E, k, z, ids, w);
+    else if (E <= 256) hipLaunchKernelGGL(k_route_select<4>, sg, dim3(256), 0, s, T, E, k, z, ids, w);
+    else if (E <= 512) hipLaunchKernelGGL(k_route_select<8>, sg, dim3(256), 0, s, T, E, k, z, ids, w);
+    else hipLaunchKernelGGL(k_route_select<16>, sg, dim3(256), 0, s, T, E, k, z, ids, w);
     return hipGetLastError();
 }
 
