@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256) void k_route_logits(int T, int H, int E,
     constexpr int LD = (NV + 255) / 256;     // float4 loads per thread per stage
     constexpr int XP = HC / 8 + 1;           // uint4 per staged x row
     constexpr int NSLOT = XL ? 64 * TS * XP : 0;      // uint4 slots of staged x per stage
-    constexpr int HS = XL && ES < 8 ? 64 : 8;  // h per inner step (one LDS wait per step; eight experts' W
-                                               // reads of 64 h would not fit the registers)
+    constexpr int HS = XL && TS * ES < 8 ? 64 : 8;  // h per inner step (one LDS wait per step; eight chains'
+                                                    // W and x reads of 64 h would not fit the registers)
     __shared__ __align__(16) float wt[2][EB * PITCH];
     __shared__ __align__(16) uint4 xt[XL ? 2 : 1][XL ? 64 * TS * XP : 1];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1741,14 +1741,16 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
     // Variants by the number of chains T*E (measured at H = 4096, E = 256):
     // up to 32768 (T = 128), one chain per lane (k_route_lane, 27 us; the
     // others 46 us and more); up to 131072 (T = 512), one token x one expert
-    // per lane (51 us); large batches ((T/128)*(E/32) >= 384), two tokens x
-    // eight experts per lane (W reads shared by the tokens, x conversions by
-    // the experts), the block's x rows staged 64 h at a time by direct-to-LDS
-    // loads (T = 6144 / 8192: 305 / 330 us, against 357 us with one token x four
-    // experts and 350 us with each lane reading its own x rows at 8192; slower
-    // below T = 6144: 264 vs 242 us at 4096); in between, one token x four
-    // experts per lane (T = 1024 / 2048 / 4096: 85 / 108 / 205 us, against 97 /
-    // 181 / 352 with one expert).
+    // per lane (51 us); from two blocks per CU of 128 tokens x 32 experts
+    // ((T/128)*(E/32) >= 512), two tokens x eight experts per lane (W reads
+    // shared by the tokens, x conversions by the experts), the block's x rows
+    // staged 64 h at a time by direct-to-LDS loads (T = 8192: 324 us, against
+    // 350 us with each lane reading its own x rows); from two blocks per CU of
+    // 128 tokens x 16 experts, the same with four experts per lane (T = 4096 /
+    // 6144: 209 / 269 us, against 239 / 357 us with one token x four experts
+    // and 307 us with eight experts at 6144, which leaves CUs a block short);
+    // below, one token x four experts per lane (T = 1024 / 2048: 99 / 128 us;
+    // two tokens: 174 / 181 us).
     const long long chains = (long long)T * E;
     if (E % 4 != 0 || H % 256 != 0) {
         hipLaunchKernelGGL(k_route_logits_any, dim3(blocks_for((size_t)T * E, 256)), dim3(256), 0, s, T, H, E, x,
@@ -1758,8 +1760,11 @@ hipError_t launch_route(int T, int H, int E, int k, const uint16_t* x, const flo
         const unsigned grid = (unsigned)(((T + NTW * 2 - 1) / (NTW * 2)) * ((E + EL - 1) / EL));
         hipLaunchKernelGGL((k_route_lane<EL, NTW, 256, 3>), dim3(grid), dim3(64 * (NTW + 1)), 0, s, T, H, E, x, wr,
                            bias, z, xq, xs);
-    } else if (E % 32 == 0 && (size_t)((T + 127) / 128) * (E / 32) >= 384) {
+    } else if (E % 32 == 0 && (size_t)((T + 127) / 128) * (E / 32) >= 512) {
         hipLaunchKernelGGL((k_route_logits<2, 8, 64, true>), dim3((T + 127) / 128, E / 32), dim3(256), 0, s, T, H, E, x,
+                           wr, bias, z);
+    } else if (E % 16 == 0 && (size_t)((T + 127) / 128) * (E / 16) >= 512) {
+        hipLaunchKernelGGL((k_route_logits<2, 4, 64, true>), dim3((T + 127) / 128, E / 16), dim3(256), 0, s, T, H, E, x,
                            wr, bias, z);
     } else if (E % 16 == 0 && chains > 131072) {
         hipLaunchKernelGGL((k_route_logits<1, 4, 128, true>), dim3((T + 63) / 64, E / 16), dim3(256), 0, s, T, H, E, x,

@@ -431,7 +431,8 @@ def test_ragged_batch_invariance_and_determinism():
 # one thread per logit; E >= 32 and T*E <= 32768 -> one chain per lane over
 # 32 experts x 2 tokens per wave with a producer wave; T*E <= 131072 -> one
 # token x one expert per lane; large batches (E % 32 == 0, (T/128)*(E/32) >=
-# 384) -> two tokens x eight experts per lane; otherwise one token x four
+# 512) -> two tokens x eight experts per lane, (E % 16 == 0, (T/128)*(E/16) >=
+# 512) -> two tokens x four experts per lane; otherwise one token x four
 # (E % 16 == 0) or two (E % 8 == 0) experts per lane.
 ROUTER_VARIANTS = [
     (32, 4096, 256),    # one chain per lane (the decode router)
@@ -441,7 +442,8 @@ ROUTER_VARIANTS = [
     (2000, 1024, 256),  # one token x four experts per lane, ragged last token block
     (4000, 1280, 40),   # one token x two experts per lane
     (8192, 1280, 256),  # two tokens x eight experts per lane
-    (6100, 1280, 256),  # the same at its smallest batch, ragged last token block
+    (6100, 1280, 256),  # two tokens x four experts per lane, ragged last token block
+    (4096, 1280, 256),  # the same at its smallest batch
     (64, 1024, 8),      # few experts: one token x one expert per lane
     (50, 1280, 6),      # E % 4 != 0: one thread per logit
 ]
@@ -487,7 +489,7 @@ def test_routing_single_chain_order(T, H, E):
     (2000, 256, 256, 8),    # one token x four experts per lane
     (4000, 256, 40, 4),     # one token x two experts per lane
     (8192, 256, 256, 8),    # two tokens x eight experts per lane
-    (6100, 512, 256, 8),    # the same, ragged last token block
+    (6100, 512, 256, 8),    # two tokens x four experts per lane, ragged last token block
     (32, 256, 8, 3),        # few experts
     (50, 256, 6, 2),        # E % 4 != 0: one thread per logit
     (50, 768, 6, 2),
