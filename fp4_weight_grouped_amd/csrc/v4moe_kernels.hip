@@ -555,14 +555,15 @@ __global__ __launch_bounds__(256) void k_quant_x(int T, int H, const uint16_t* _
 // follow pair order exactly.  Pass <true> writes per-block counts; the scan
 // turns them into per-block bases; pass <false> writes the positions.
 // ---------------------------------------------------------------------------
-// The expert ids of one chunk of kPermChunk pairs starting at p0, for one wave:
+// The expert ids of one chunk of CH pairs starting at p0, for one wave:
 // ev[i] = id of pair p0 + 64i + lane, or -1 past the end.  Loaded once, all
 // in flight together, and used by both passes.
+template <int CH = kPermChunk>
 __device__ __forceinline__ void load_chunk_ids(int P, int p0, int lane, const int32_t* __restrict__ ids,
-                                               int (&ev)[kPermChunk / 64])
+                                               int (&ev)[CH / 64])
 {
 #pragma unroll
-    for (int i = 0; i < kPermChunk / 64; i++) {
+    for (int i = 0; i < CH / 64; i++) {
         const int p = p0 + 64 * i + lane;
         ev[i] = p < P ? ids[p] : -1;
     }
@@ -571,21 +572,21 @@ __device__ __forceinline__ void load_chunk_ids(int P, int p0, int lane, const in
 // Bits of an expert-id key: ids are < E and E itself marks an invalid pair.
 __device__ __forceinline__ int id_key_bits(int E) { return 32 - __clz(E); }
 
-// One wave over one chunk of kPermChunk pairs starting at p0, in pair order.
+// One wave over one chunk of CH pairs starting at p0, in pair order.
 // cnt[E] (LDS) holds the chunk's running per-expert counts (zero on entry).
 // A pair's rank among the equal-expert pairs of its 64 is found by ballots
 // over the bits of the expert id.  Count pass: cnt ends as the chunk's
 // histogram.  Position pass: pair p goes to row[e] + (earlier pairs of e in
 // the chunk), row[e] being the chunk's base for expert e.
-template <bool kCount>
-__device__ __forceinline__ void perm_chunk(int p0, int lane, int E, const int (&ev)[kPermChunk / 64],
+template <bool kCount, int CH = kPermChunk>
+__device__ __forceinline__ void perm_chunk(int p0, int lane, int E, const int (&ev)[CH / 64],
                                            int32_t* cnt, const int32_t* row,
                                            int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos)
 {
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int nbits = id_key_bits(E);
 #pragma unroll
-    for (int i = 0; i < kPermChunk / 64; i++) {
+    for (int i = 0; i < CH / 64; i++) {
         const int p = p0 + 64 * i + lane;
         const bool valid = ev[i] >= 0;
         const int e = valid ? ev[i] : 0;
@@ -720,23 +721,27 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nblk, int32_t* __
 }
 
 // The whole permutation in one 1024-thread block when there are at most 16
-// chunks (wave w handles chunk w): histograms, offsets and per-chunk bases,
-// positions.  Same results as the three kernels above.  LDS: hist[nblk][E]
-// then cnt[nblk][E]; off_lds (E+1 ints, optional) receives the offsets too.
+// chunks of CH pairs (wave w handles chunk w): histograms, offsets and
+// per-chunk bases, positions.  Same results as the three kernels above (the
+// positions are the stable order whatever the chunking).  Small batches use
+// 64-pair chunks, so all 16 waves share the ballot passes.  LDS:
+// hist[nblk][E] then cnt[nblk][E]; off_lds (E+1 ints, optional) receives the
+// offsets too.
+template <int CH>
 __device__ __forceinline__ void perm_small_block(int P, int E, const int32_t* __restrict__ ids,
                                                  int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
                                                  int32_t* __restrict__ pair_pos, int32_t* sh, int32_t* off_lds)
 {
     __shared__ int total_s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int nblk = (P + kPermChunk - 1) / kPermChunk;
+    const int nblk = (P + CH - 1) / CH;
     int32_t* hist = sh;
     int32_t* cnt = sh + nblk * E;
-    int ev[kPermChunk / 64];
-    if (w < nblk) load_chunk_ids(P, w * kPermChunk, lane, ids, ev);
+    int ev[CH / 64];
+    if (w < nblk) load_chunk_ids<CH>(P, w * CH, lane, ids, ev);
     for (int i = tid; i < 2 * nblk * E; i += 1024) sh[i] = 0;
     __syncthreads();
-    if (w < nblk) perm_chunk<true>(w * kPermChunk, lane, E, ev, hist + w * E, nullptr, sorted_pair, pair_pos);
+    if (w < nblk) perm_chunk<true, CH>(w * CH, lane, E, ev, hist + w * E, nullptr, sorted_pair, pair_pos);
     __syncthreads();
     int tot = 0;
     if (tid < E)
@@ -757,15 +762,16 @@ __device__ __forceinline__ void perm_small_block(int P, int E, const int32_t* __
         if (off_lds) off_lds[E] = total_s;
     }
     __syncthreads();
-    if (w < nblk) perm_chunk<false>(w * kPermChunk, lane, E, ev, cnt + w * E, hist + w * E, sorted_pair, pair_pos);
+    if (w < nblk) perm_chunk<false, CH>(w * CH, lane, E, ev, cnt + w * E, hist + w * E, sorted_pair, pair_pos);
 }
+template <int CH>
 __global__ __launch_bounds__(1024) void k_perm_small(int P, int E, const int32_t* __restrict__ ids,
                                                      int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ sorted_pair,
                                                      int32_t* __restrict__ pair_pos)
 {
     extern __shared__ int32_t sh[];
-    perm_small_block(P, E, ids, offsets, sorted_pair, pair_pos, sh, nullptr);
+    perm_small_block<CH>(P, E, ids, offsets, sorted_pair, pair_pos, sh, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -860,19 +866,15 @@ __device__ __forceinline__ void build_tiles_block(int E, int M, int NB1, int NB2
     }
     if (build_queue != 1) return;
     __syncthreads();
-    // every entry on its own: its segment is the last one starting at or before
-    // it (empty segments share their start with the next one)
-    for (int q = tid; q < total * (NB1 + NB2); q += 1024) {
-        int lo = 0, hi = 2 * W - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (qstart[mid] <= q) lo = mid; else hi = mid - 1;
-        }
-        const int swv = qkey[lo] >> 1, sph = qkey[lo] & 1;
+    // segments to waves in turn, a segment's entries to the wave's lanes
+    const int qw = tid >> 6, ln = tid & 63;
+    for (int sg = qw; sg < 2 * W; sg += 16) {
+        const int q0 = qstart[sg], len = qstart[sg + 1] - q0;
+        const int swv = qkey[sg] >> 1, sph = qkey[sg] & 1;
         const int NB = sph ? NB2 : NB1;
-        const int i = q - qstart[lo];
-        const int mt = base[swv * kWaveExperts] + i / NB;
-        queue[q] = ((uint32_t)sph << 31) | ((uint32_t)mt << 8) | (uint32_t)(i % NB);
+        const int mt0 = base[swv * kWaveExperts];
+        for (int i = ln; i < len; i += 64)
+            queue[q0 + i] = ((uint32_t)sph << 31) | ((uint32_t)(mt0 + i / NB) << 8) | (uint32_t)(i % NB);
     }
 }
 __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int NB2, int build_queue, int D,
@@ -891,6 +893,7 @@ __global__ __launch_bounds__(1024) void k_build_tiles(int E, int M, int NB1, int
 // run one after the other (the tile list reads the offsets after a block
 // barrier), so the results are identical; one dependent launch fewer on the
 // latency-bound path.
+template <int CH>
 __global__ __launch_bounds__(1024) void k_perm_tiles(int P, int E, const int32_t* __restrict__ ids,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
                                                      int32_t* __restrict__ pair_pos, int M, int NB1, int NB2,
@@ -900,7 +903,7 @@ __global__ __launch_bounds__(1024) void k_perm_tiles(int P, int E, const int32_t
 {
     extern __shared__ int32_t sh[];
     __shared__ int32_t off_lds[1025];
-    perm_small_block(P, E, ids, offsets, sorted_pair, pair_pos, sh, off_lds);
+    perm_small_block<CH>(P, E, ids, offsets, sorted_pair, pair_pos, sh, off_lds);
     __syncthreads();
     // the tile list reads the offsets from LDS, not back from global memory
     build_tiles_block(E, M, NB1, NB2, build_queue, D, off_lds, mt_expert, mt_row0, ctrl, done1, queue);
@@ -1798,8 +1801,13 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, int32_t* offs
     const int P = T * k;
     const int nblk = (P + kPermChunk - 1) / kPermChunk;
     if (nblk <= 16 && nblk * E <= 4096) {   // dynamic LDS <= 32 KiB
-        hipLaunchKernelGGL(k_perm_small, dim3(1), dim3(1024), (size_t)2 * nblk * E * 4, s, P, E, ids, offsets,
-                           sorted_pair, pair_pos);
+        const int n64 = (P + 63) / 64;
+        if (n64 <= 16 && n64 * E <= 4096)
+            hipLaunchKernelGGL(k_perm_small<64>, dim3(1), dim3(1024), (size_t)2 * n64 * E * 4, s, P, E, ids, offsets,
+                               sorted_pair, pair_pos);
+        else
+            hipLaunchKernelGGL(k_perm_small<kPermChunk>, dim3(1), dim3(1024), (size_t)2 * nblk * E * 4, s, P, E, ids,
+                               offsets, sorted_pair, pair_pos);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_perm_pass<true>, dim3(nblk), dim3(64), (size_t)E * 4, s, P, E, ids, hist,
@@ -1822,9 +1830,15 @@ hipError_t launch_perm_tiles(int T, int k, int E, const int32_t* ids, int32_t* o
 {
     const int P = T * k;
     const int nblk = (P + kPermChunk - 1) / kPermChunk;
-    hipLaunchKernelGGL(k_perm_tiles, dim3(1), dim3(1024), (size_t)2 * nblk * E * 4, s, P, E, ids, offsets,
-                       sorted_pair, pair_pos, 16 * MT, NB1, NB2, build_queue, lag, mt_expert, mt_row0, a.ctrl,
-                       a.done1, queue);
+    const int n64 = (P + 63) / 64;   // 64-pair chunks when they fit the same 16 waves and LDS
+    if (n64 <= 16 && n64 * E <= 4096)
+        hipLaunchKernelGGL(k_perm_tiles<64>, dim3(1), dim3(1024), (size_t)2 * n64 * E * 4, s, P, E, ids, offsets,
+                           sorted_pair, pair_pos, 16 * MT, NB1, NB2, build_queue, lag, mt_expert, mt_row0, a.ctrl,
+                           a.done1, queue);
+    else
+        hipLaunchKernelGGL(k_perm_tiles<kPermChunk>, dim3(1), dim3(1024), (size_t)2 * nblk * E * 4, s, P, E, ids,
+                           offsets, sorted_pair, pair_pos, 16 * MT, NB1, NB2, build_queue, lag, mt_expert, mt_row0,
+                           a.ctrl, a.done1, queue);
     return hipGetLastError();
 }
 
