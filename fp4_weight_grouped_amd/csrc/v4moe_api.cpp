@@ -623,15 +623,17 @@ __attribute__((visibility("default"))) int moe_layer_backward(
         BgemmArgs wg{};
         wg.offsets = offsets; wg.padoff = padoff;
         wg.lda = wg.ldb = B.ldd;
+        // weight gradients: with the same batch rule as the dgrads' tiles
+        // (about 64 rows per expert or more), the kernel that holds B in registers
         wg.M = H; wg.N = I; wg.A = dyT; wg.B = hT; wg.dW = dWd;
-        if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bgemm(BG_WGRAD, B.bm, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         wg.M = I; wg.N = H; wg.B = xT;
         if (gated(d)) {
             wg.A = dguT; wg.dW = dWg;
-            if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+            if (launch_bgemm(BG_WGRAD, B.bm, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         }
         wg.A = dguT + (gated(d) ? (size_t)I * B.ldd : 0); wg.dW = dWu;
-        if (launch_bgemm(BG_WGRAD, 64, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
+        if (launch_bgemm(BG_WGRAD, B.bm, wg, 0, E, s) != hipSuccess) return V4MOE_ELAUNCH;
     } else {
         // no tokens: every weight gradient is zero
         if (launch_fill_i32(offsets, 0, E + 1, s) != hipSuccess) return V4MOE_ELAUNCH;

@@ -446,6 +446,137 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 }
 
 // ---------------------------------------------------------------------------
+// Weight gradients for large batches, B held in registers: dW_e[m][n] = sum
+// over the expert's padded columns c of A[m][c] B[n][c] (both [channel][column]
+// bf16, fp32 accumulation, the master layout out).  An expert's padded column
+// count Kp (its rows rounded up to 32, ~2.9 x 10^2 at prefill) is short, so a
+// tile that loads both operands for every 64 x 128 output moves 3.4 bytes
+// through the texture path per byte of fp32 it writes.  Here a block owns 128
+// columns n0.. of one expert's dW: each of its four waves keeps the MFMA
+// operands of its 32 columns for all of Kp (up to KMAX) in registers, loaded
+// once, and the block walks down dW in 128-row tiles, A's rows staged in LDS
+// with the next tile's loaded into registers while the current one computes:
+// 1.1 bytes read per byte written, with 76 KB of LDS so that two blocks share
+// a CU and one's loads and stores overlap the other's products.  Experts with
+// more columns take them in KMAX chunks, the B operand reloaded per chunk.
+// ---------------------------------------------------------------------------
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // (a uint4 copy would keep arrays in scratch)
+template <int KMAX>
+struct WgTile {
+    static constexpr int PITCH = KMAX + 8;                  // bf16 per LDS row of A
+    static constexpr int NS = KMAX / 32;                    // K steps of 32
+    static constexpr int QA = 128 * (KMAX / 8) / 256;       // 16-byte A pieces per thread per tile
+    static constexpr int LDS = 128 * PITCH * 2;             // the A tile, reused for the fp32 staging
+    static_assert(128 * 132 * 4 <= LDS, "the fp32 tile is staged in the A buffer");
+    static_assert((128 * (KMAX / 8)) % 256 == 0 && KMAX % 32 == 0, "tile shape");
+};
+// piece q of a 128-row x klen tile: row (tid + 256 q) / (klen/8), 16-byte
+// segment (tid + 256 q) % (klen/8); pieces past the tile repeat its last one
+// (the same bytes to the same place)
+template <int Q>
+__device__ __forceinline__ void wg_fetch(v4u (&r)[Q], const uint16_t* base, int ld, int row0, int c0, int klen, int tid)
+{
+    const int sp = klen / 8;
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+        const int i = min(tid + 256 * q, 128 * sp - 1);
+        r[q] = *reinterpret_cast<const v4u*>(base + (size_t)(row0 + i / sp) * ld + c0 + (i % sp) * 8);
+    }
+}
+template <int PITCH, int Q>
+__device__ __forceinline__ void wg_put(uint16_t* dst, const v4u (&r)[Q], int klen, int tid)
+{
+    const int sp = klen / 8;
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+        const int i = min(tid + 256 * q, 128 * sp - 1);
+        *reinterpret_cast<v4u*>(&dst[(i / sp) * PITCH + (i % sp) * 8]) = r[q];
+    }
+}
+template <int KMAX>
+__global__ __launch_bounds__(256) void k_wgrad(BgemmArgs a)
+{
+    using TL = WgTile<KMAX>;
+    constexpr int PITCH = TL::PITCH, NS = TL::NS;
+    extern __shared__ __align__(16) uint16_t smem_wg[];
+    uint16_t* As = smem_wg;
+    float* cs = reinterpret_cast<float*>(smem_wg);           // [128][132] fp32 staging
+    const int e = blockIdx.y, n0 = blockIdx.x * 128;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cbeg = a.padoff[e];
+    const int Kp = (a.offsets[e + 1] - a.offsets[e] + 31) & ~31;
+    const int nkc = Kp > 0 ? (Kp + KMAX - 1) / KMAX : 1;      // an expert without rows runs one empty chunk: zeros
+    const int items = (a.M / 128) * nkc;                      // (128-row tile, K chunk), chunk fastest
+    const uint16_t* Bb = a.B + (size_t)e * a.b_expert;
+    // this wave's B operand: columns n0 + 32w + 16j + (lane % 16), 8 K values
+    // from 32s + 8 (lane / 16) of the chunk
+    const uint16_t* brow[2] = {Bb + (size_t)(n0 + 32 * w + (lane & 15)) * a.ldb + 8 * (lane >> 4),
+                               Bb + (size_t)(n0 + 32 * w + 16 + (lane & 15)) * a.ldb + 8 * (lane >> 4)};
+    bf8 bfr[NS][2];
+    auto load_b = [&](int c0, int klen) {
+#pragma unroll
+        for (int st = 0; st < NS; st++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                if (32 * st < klen) bfr[st][j] = *reinterpret_cast<const bf8*>(brow[j] + c0 + 32 * st);
+    };
+    v4u ra[TL::QA];
+    if (Kp > 0) {
+        load_b(cbeg, min(KMAX, Kp));
+        wg_fetch(ra, a.A, a.lda, 0, cbeg, min(KMAX, Kp), tid);
+    }
+    v4f acc[8][2];
+    for (int it = 0; it < items; it++) {
+        const int mt = it / nkc, kc = it % nkc;
+        const int klen = Kp > 0 ? min(KMAX, Kp - kc * KMAX) : 0;
+        if (kc == 0)
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();                                      // As free: the last item's reads and stores are done
+        if (klen > 0) {
+            wg_put<PITCH>(As, ra, klen, tid);
+            if (nkc > 1 && kc > 0) load_b(cbeg + kc * KMAX, klen);
+        }
+        __syncthreads();
+        if (it + 1 < items && Kp > 0) {
+            const int mt1 = (it + 1) / nkc, kc1 = (it + 1) % nkc;
+            wg_fetch(ra, a.A, a.lda, mt1 * 128, cbeg + kc1 * KMAX, min(KMAX, Kp - kc1 * KMAX), tid);
+        }
+#pragma unroll
+        for (int st = 0; st < NS; st++) {
+            if (32 * st >= klen) break;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const bf8 afr = *reinterpret_cast<const bf8*>(&As[(i * 16 + (lane & 15)) * PITCH + 32 * st + 8 * (lane >> 4)]);
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[st][j], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (kc + 1 < nkc) continue;                         // the next chunk's B is loaded at its start
+        // the 128 x 128 fp32 tile through LDS, then 16-byte row stores
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    cs[(i * 16 + 4 * (lane >> 4) + q) * 132 + 32 * w + j * 16 + (lane & 15)] = acc[i][j][q];
+        __syncthreads();
+        for (int idx = tid; idx < 128 * 32; idx += 256) {
+            const int r = idx >> 5, c4 = (idx & 31) * 4;
+            *reinterpret_cast<float4*>(a.dW + ((size_t)e * a.M + mt * 128 + r) * a.N + n0 + c4) =
+                *reinterpret_cast<const float4*>(&cs[r * 132 + c4]);
+        }
+        // a chunked expert's next tile starts again at chunk 0: its B operand
+        if (nkc > 1 && it + 1 < items) load_b(cbeg, min(KMAX, Kp));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_bwd_combine(int T, int H, int k, const uint16_t* dout, const float* w, const uint16_t* y,
@@ -513,13 +644,25 @@ static hipError_t launch_bgemm_t(const BgemmArgs& a, dim3 grid, int NB, hipStrea
     return hipGetLastError();
 }
 
-// DGRAD modes: bm (64 or 128) is the row count of the m-tiles in the list.
+// DGRAD modes: bm (64 or 128) is the row count of the m-tiles in the list;
+// WGRAD: bm = 128 selects k_wgrad.
 hipError_t launch_bgemm(int mode, int bm, const BgemmArgs& a, int n_mt_bound, int E, hipStream_t s)
 {
     const int NB = a.N / 128;
     if (mode == WGRAD) {
         if (E == 0) return hipSuccess;
-        return launch_bgemm_t<WGRAD, 64, 64>(a, dim3((unsigned)((a.M / 64) * NB), 1, (unsigned)E), NB, s);
+        if (bm != 128) return launch_bgemm_t<WGRAD, 64, 64>(a, dim3((unsigned)((a.M / 64) * NB), 1, (unsigned)E), NB, s);
+        constexpr int KMAX = 288;
+        constexpr int LDS = WgTile<KMAX>::LDS;
+        static bool lds_ok = false;
+        if (!lds_ok) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_wgrad<KMAX>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, LDS) != hipSuccess)
+                return hipErrorInvalidValue;
+            lds_ok = true;
+        }
+        hipLaunchKernelGGL(k_wgrad<KMAX>, dim3((unsigned)NB, (unsigned)E), dim3(256), LDS, s, a);
+        return hipGetLastError();
     }
     const dim3 grid((unsigned)(n_mt_bound * NB));
     if (bm == 128)

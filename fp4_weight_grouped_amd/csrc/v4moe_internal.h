@@ -117,7 +117,8 @@ hipError_t launch_bwd_transpose(int mode, int C, int E, int k, int max_cols, con
 hipError_t launch_bwd_unpermute(int T, int H, int k, const int32_t* pair_pos, const float* dxs, float* dx,
                                 hipStream_t s);
 // DGRAD modes: grid over n_mt_bound m-tiles of bm (64 or 128) rows x N/128;
-// WGRAD: E x (M/64) x (N/128).
+// WGRAD: bm = 128 (large batches, bwd_tile_rows) one block per expert and 128
+// columns of dW with B in registers (k_wgrad), otherwise E x (M/64) x (N/128).
 hipError_t launch_bgemm(int mode, int bm, const BgemmArgs& a, int n_mt_bound, int E, hipStream_t s);
 // Rows per dgrad m-tile of the backward: 128 once experts average 64 rows or more.
 inline int bwd_tile_rows(int T, int k, int E) { return (long long)T * k >= 64LL * E ? 128 : 64; }
