@@ -384,7 +384,7 @@ def run_backward(name, steps, warmup, layer_cache):
     """One backward step = moe_layer_backward (forward recompute, combine
     backward, dgrad, activation derivative, un-permute, weight gradients) on
     the workload's layer, inputs and dout resident in HBM.  Reported against
-    HBM (decode: forward weight bytes + bf16 transposed weights of the active
+    HBM (decode: forward weight bytes + E4M3 transposed weights of the active
     experts read, fp32 weight gradients of all experts written) or the dense
     bf16 matrix peak (prefill: 4 * T*k*mats*H*I FLOP of dgrad and wgrad)."""
     import torch
@@ -424,7 +424,7 @@ def run_backward(name, steps, warmup, layer_cache):
     n_active = int((off > 0).sum())
     mats = 3 if d.act == inputs.ACT_SWIGLU else 2
     hi = d.H * d.I
-    nbytes = n_active * (weight_bytes_per_expert(d.H, d.I, mats) + mats * hi * 2) + d.E * mats * hi * 4
+    nbytes = n_active * (weight_bytes_per_expert(d.H, d.I, mats) + mats * hi) + d.E * mats * hi * 4
     flops = 4 * d.T * d.topk * mats * hi
     rec = dict(workload=name, T=d.T, ms=ms, p10=pct(ms_all, 10), p90=pct(ms_all, 90), tokens_per_s=d.T / (ms / 1e3),
                algorithmic_bytes=nbytes, bf16_flops=flops)

@@ -509,7 +509,7 @@ __attribute__((visibility("default"))) size_t moe_backward_workspace_bytes(const
 }
 
 __attribute__((visibility("default"))) int moe_transpose_weights(const v4moe_dims* d, const v4moe_experts* w,
-                                                                 uint16_t* wt_gu, uint16_t* wt_d, void* stream)
+                                                                 uint8_t* wt_gu, uint8_t* wt_d, void* stream)
 {
     if (!dims_ok(d)) return V4MOE_EDIMS;
     if (!w || !wt_gu || !wt_d) return V4MOE_ENULL;
@@ -532,7 +532,7 @@ __attribute__((visibility("default"))) int moe_transpose_weights(const v4moe_dim
 
 __attribute__((visibility("default"))) int moe_layer_backward(
     const v4moe_dims* d, const uint16_t* x, const float* w_router, const float* bias, int32_t mode,
-    const int64_t* token_ids, const v4moe_experts* w, const uint16_t* wt_gu, const uint16_t* wt_d,
+    const int64_t* token_ids, const v4moe_experts* w, const uint8_t* wt_gu, const uint8_t* wt_d,
     const uint16_t* dout, float* dx, float* dw, float* dWg, float* dWu, float* dWd, void* workspace,
     size_t ws_bytes, void* stream)
 {
@@ -595,11 +595,11 @@ __attribute__((visibility("default"))) int moe_layer_backward(
         float* dxs = reinterpret_cast<float*>(at(B.dxs));
         g.dxs = dxs;
         // dh = Wd^T dY, activation derivative -> dG, dU
-        g.N = I; g.K = H; g.A = dys; g.lda = H; g.B = wt_d; g.ldb = H; g.b_expert = (size_t)I * H;
+        g.N = I; g.K = H; g.A = dys; g.lda = H; g.Bq = wt_d; g.ldb = H; g.b_expert = (size_t)I * H;
         g.blk0 = w->down.blk;
         if (launch_bgemm(BG_DGRAD2, B.bm, g, B.n_mt4, E, s) != hipSuccess) return V4MOE_ELAUNCH;
         // dx per row = [Wg Wu]^T [dG dU]
-        g.N = H; g.K = gI; g.A = dgu; g.lda = gI; g.B = wt_gu; g.ldb = gI; g.b_expert = (size_t)H * gI;
+        g.N = H; g.K = gI; g.A = dgu; g.lda = gI; g.Bq = wt_gu; g.ldb = gI; g.b_expert = (size_t)H * gI;
         g.blk0 = gated(d) ? w->gate.blk : w->up.blk;
         g.blk1 = w->up.blk;
         if (launch_bgemm(BG_DGRAD1, B.bm, g, B.n_mt4, E, s) != hipSuccess) return V4MOE_ELAUNCH;

@@ -90,16 +90,18 @@ __global__ __launch_bounds__(256) void k_bwd_combine(int H, int k, const uint16_
 }
 
 // ---------------------------------------------------------------------------
-// Transposed FP8 weight values in bf16: packed matrix (N rows, K inputs) ->
-// out[e][kk][nofs + n] = e2m1(code) * 2^b for kk < K, n < N, row pitch ldo
-// (so gate and up can share one [H][2I] buffer).  One block per (expert,
-// 64-row quad, 128-wide chunk); the quad is transposed through LDS.
+// Transposed FP8 weight values as E4M3 bytes: packed matrix (N rows, K
+// inputs) -> out[e][kk][nofs + n] = E4M3(e2m1(code) * 2^b) for kk < K, n < N,
+// row pitch ldo bytes (so gate and up can share one [H][2I] buffer).  Inside
+// the scale window every such value is an E4M3 value, so the bytes are exact;
+// a zero keeps its code's sign.  One block per (expert, 64-row quad,
+// 128-wide chunk); the quad is transposed through LDS.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_weights_t(int N, int K, const uint8_t* __restrict__ fp4,
-                                                   const uint8_t* __restrict__ e8, uint16_t* __restrict__ out,
+                                                   const uint8_t* __restrict__ e8, uint8_t* __restrict__ out,
                                                    int ldo, int nofs, size_t out_expert_stride)
 {
-    __shared__ uint16_t tr[128][64 + 8];
+    __shared__ uint8_t tr[128][64 + 16];
     const int C = K / 128;
     const int c = blockIdx.x % C;
     const int qd = (blockIdx.x / C) % (N / 64);
@@ -114,17 +116,33 @@ __global__ __launch_bounds__(256) void k_weights_t(int N, int K, const uint8_t* 
     for (int i = 0; i < 32; i++) {
         const uint32_t code = (cw[i >> 3] >> (4 * (i & 7))) & 15u;
         const uint32_t e2 = (code >> 1) & 3u, m = code & 1u;
-        // e2m1 magnitude as fp32 bits, times 2^b (exact), to bf16 bits (exact)
+        // e2m1 magnitude as fp32 bits, times 2^b (exact), to its E4M3 byte
+        // (exact inside the window), the code's sign bit on top
         const float mag = e2 ? __uint_as_float(((e2 + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
-        const float v = ldexpf(mag, b);
-        tr[kl + i][nl] = (uint16_t)((__float_as_uint(v) >> 16) | ((code & 8u) << 12));
+        tr[kl + i][nl] = (uint8_t)((e4m3x2(ldexpf(mag, b), 0.0f) & 0x7Fu) | ((code & 8u) << 4));
     }
     __syncthreads();
-    for (int idx = tid; idx < 128 * 8; idx += 256) {
-        const int kk = idx >> 3, seg = idx & 7;
+    for (int idx = tid; idx < 128 * 4; idx += 256) {
+        const int kk = idx >> 2, seg = idx & 3;
         *reinterpret_cast<uint4*>(out + e * out_expert_stride + (size_t)(c * 128 + kk) * ldo + nofs + qd * 64 +
-                                  seg * 8) = *reinterpret_cast<const uint4*>(&tr[kk][seg * 8]);
+                                  seg * 16) = *reinterpret_cast<const uint4*>(&tr[kk][seg * 16]);
     }
+}
+
+// Eight OCP E4M3 bytes -> eight bf16 (exact: every E4M3 value is a bf16
+// value), in order: the hardware decode to fp32 (verified here on all 256
+// codes), then the upper halves of the fp32 words.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 v)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
+    const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+    const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
+    const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+    auto hi2 = [](float lo, float hi) {
+        return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    };
+    return make_uint4(hi2(a.x, a.y), hi2(b.x, b.y), hi2(c.x, c.y), hi2(d.x, d.y));
 }
 
 // ---------------------------------------------------------------------------
@@ -300,7 +318,8 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
         kbeg = 0;
         kend = a.K;
     }
-    const uint16_t* Bb = a.B + (size_t)e * a.b_expert;
+    const uint16_t* Bb = a.B + (size_t)e * a.b_expert;       // WGRAD: bf16 activations
+    const uint8_t* Bq = a.Bq + (size_t)e * a.b_expert;       // DGRAD: E4M3 transposed weights
     v4f acc[4][NJ], part[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -314,6 +333,7 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
     // columns past the stage's end read as zero.
     constexpr int RSTEP = 256 / SEGS;
     uint4 ra[TL::QA], rb[TL::QB];
+    uint2 rq[TL::QB];   // DGRAD: the weight pieces as E4M3 bytes, converted when staged
     auto load = [&](int k0) {
         const int kn = min(KS, kend - k0);
         const int sg = tid % SEGS;
@@ -327,8 +347,12 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
 #pragma unroll
         for (int q = 0; q < TL::QB; q++) {
             const int r = tid / SEGS + RSTEP * q;
-            rb[q] = in ? *reinterpret_cast<const uint4*>(Bb + (size_t)(n0 + r) * a.ldb + k0 + sg * 8)
-                       : make_uint4(0, 0, 0, 0);
+            if (MODE == WGRAD)
+                rb[q] = in ? *reinterpret_cast<const uint4*>(Bb + (size_t)(n0 + r) * a.ldb + k0 + sg * 8)
+                           : make_uint4(0, 0, 0, 0);
+            else
+                rq[q] = in ? *reinterpret_cast<const uint2*>(Bq + (size_t)(n0 + r) * a.ldb + k0 + sg * 8)
+                           : make_uint2(0, 0);
         }
     };
     if (kbeg < kend) load(kbeg);
@@ -342,7 +366,8 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
                 *reinterpret_cast<uint4*>(&As[(tid / SEGS + RSTEP * q) * PITCH + sg * 8]) = ra[q];
 #pragma unroll
             for (int q = 0; q < TL::QB; q++)
-                *reinterpret_cast<uint4*>(&Bs[(tid / SEGS + RSTEP * q) * PITCH + sg * 8]) = rb[q];
+                *reinterpret_cast<uint4*>(&Bs[(tid / SEGS + RSTEP * q) * PITCH + sg * 8]) =
+                    MODE == WGRAD ? rb[q] : e4m3x8_to_bf16x8(rq[q]);
         }
         __syncthreads();
         if (k0 + KS < kend) load(k0 + KS);
@@ -587,7 +612,7 @@ hipError_t launch_bwd_combine(int T, int H, int k, const uint16_t* dout, const f
     return hipGetLastError();
 }
 
-hipError_t launch_weights_t(int E, int N, int K, const uint8_t* fp4, const uint8_t* e8, uint16_t* out, int ldo,
+hipError_t launch_weights_t(int E, int N, int K, const uint8_t* fp4, const uint8_t* e8, uint8_t* out, int ldo,
                             int nofs, size_t out_expert_stride, hipStream_t s)
 {
     const size_t blocks = (size_t)E * (N / 64) * (K / 128);

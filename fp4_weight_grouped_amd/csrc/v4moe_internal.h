@@ -98,7 +98,8 @@ struct BgemmArgs {
     int M, N, K;                 // WGRAD: rows, cols of dW; DGRAD: N outputs, K contraction
     int I, H, act;
     const uint16_t* A; int lda;
-    const uint16_t* B; int ldb; size_t b_expert;   // B element (e, n, k) at B + e*b_expert + n*ldb + k
+    const uint16_t* B; int ldb; size_t b_expert;   // B element (e, n, k) at B + e*b_expert + n*ldb + k (WGRAD)
+    const uint8_t* Bq;                              // DGRAD: the same indexing, E4M3 weight bytes
     const float* blk0; const float* blk1;           // block scales (DGRAD2: down; DGRAD1: gate, up)
     const int32_t* mt_expert; const int32_t* mt_row0; const int32_t* ctrl; const int32_t* offsets;
     const int32_t* padoff;
@@ -107,7 +108,7 @@ struct BgemmArgs {
 };
 hipError_t launch_bwd_combine(int T, int H, int k, const uint16_t* dout, const float* w, const uint16_t* y,
                               const int32_t* pair_pos, uint16_t* dys, float* dw, hipStream_t s);
-hipError_t launch_weights_t(int E, int N, int K, const uint8_t* fp4, const uint8_t* e8, uint16_t* out, int ldo,
+hipError_t launch_weights_t(int E, int N, int K, const uint8_t* fp4, const uint8_t* e8, uint8_t* out, int ldo,
                             int nofs, size_t out_expert_stride, hipStream_t s);
 hipError_t launch_pad_offsets(int E, const int32_t* off, int32_t* padoff, hipStream_t s);
 hipError_t launch_bwd_transpose(int mode, int C, int E, int k, int max_cols, const int32_t* off,

@@ -312,12 +312,12 @@ class MoELayer:
         return out, ids, w, off
 
     def transposed_weights(self):
-        """The bf16 transposed FP8 weight values the backward reads (made once)."""
+        """The transposed FP8 weight values (E4M3 bytes) the backward reads (made once)."""
         if getattr(self, "_wt", None) is None:
             d = self.dims(1)
             gI = 2 * self.I if self.act == ACT_SWIGLU else self.I
-            wt_gu = torch.empty((self.E, self.H, gI), dtype=torch.int16, device=self.device)
-            wt_d = torch.empty((self.E, self.I, self.H), dtype=torch.int16, device=self.device)
+            wt_gu = torch.empty((self.E, self.H, gI), dtype=torch.uint8, device=self.device)
+            wt_d = torch.empty((self.E, self.I, self.H), dtype=torch.uint8, device=self.device)
             moe_transpose_weights(d, self.experts, wt_gu, wt_d)
             self._wt = (wt_gu, wt_d)
         return self._wt

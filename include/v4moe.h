@@ -266,16 +266,19 @@ int moe_dequant_fp8(const v4moe_mat* m, int32_t N, int32_t K, int32_t expert,
  * Device memory owned by the caller, 16-byte aligned, no initialisation. */
 size_t moe_backward_workspace_bytes(const v4moe_dims* d);
 
-/* The PACKED expert weights as transposed FP8 values in bf16 (exact: every
- * E2M1 code times its power-of-two sub-block scale is a bf16 value; the fp32
- * 128x128 block scales are not applied and stay in w):
- *   wt_gu: [E][H][2I] with [e][h][i] = gate(e, i, h), [e][h][I + i] = up(e, i, h)
- *          (gate-less: [E][H][I] of up);
- *   wt_d:  [E][I][H] with [e][i][h] = down(e, h, i).
- * Computed once per weight version and passed to moe_layer_backward.
+/* The PACKED expert weights as transposed FP8 values, one OCP E4M3 byte each
+ * (exact: inside the scale window every E2M1 code times its power-of-two
+ * sub-block scale is an E4M3 value, the byte moe_dequant_fp8 gives; a zero
+ * keeps its code's sign; the fp32 128x128 block scales are not applied and
+ * stay in w):
+ *   wt_gu: [E][H][2I] bytes with [e][h][i] = gate(e, i, h), [e][h][I + i] =
+ *          up(e, i, h) (gate-less: [E][H][I] of up);
+ *   wt_d:  [E][I][H] bytes with [e][i][h] = down(e, h, i).
+ * Computed once per weight version and passed to moe_layer_backward (whose
+ * matrix products read them as bf16, converted exactly when staged).
  * Asynchronous on `stream`; 16-byte aligned outputs. */
-int moe_transpose_weights(const v4moe_dims* d, const v4moe_experts* w, uint16_t* wt_gu,
-                          uint16_t* wt_d, void* stream);
+int moe_transpose_weights(const v4moe_dims* d, const v4moe_experts* w, uint8_t* wt_gu,
+                          uint8_t* wt_d, void* stream);
 
 /* Gradients of L = sum(dout * out) for the layer forward moe_layer_forward
  * computes on the same inputs (routing, quantisation and the FFN are
@@ -296,7 +299,7 @@ int moe_transpose_weights(const v4moe_dims* d, const v4moe_experts* w, uint16_t*
  * Pointers 16-byte aligned. */
 int moe_layer_backward(const v4moe_dims* d, const uint16_t* x, const float* w_router,
                        const float* bias, int32_t mode, const int64_t* token_ids,
-                       const v4moe_experts* w, const uint16_t* wt_gu, const uint16_t* wt_d,
+                       const v4moe_experts* w, const uint8_t* wt_gu, const uint8_t* wt_d,
                        const uint16_t* dout, float* dx, float* dw, float* dWg, float* dWu,
                        float* dWd, void* workspace, size_t ws_bytes, void* stream);
 
