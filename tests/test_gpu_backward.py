@@ -92,6 +92,8 @@ def test_backward_small(act):
     (200, 512, 384, 8, 3, 0, True),     # 3 chunks of I, skewed load, partial 64-row tiles
     (300, 256, 256, 16, 1, 1, False),   # hash routing, k = 1
     (64, 256, 128, 64, 4, 0, True),     # many experts, some empty (zero weight gradients)
+    (1200, 256, 384, 4, 2, 0, True),    # large-batch weight gradients: experts of 1199 / 1046 rows in
+                                        # 288-column chunks (ragged last chunk) next to experts of 29 / 126
 ])
 def test_backward_shapes(T, H, I, E, k, mode, bias):
     g, _, _ = full_check(make(T, H, I, E, k, mode=mode, bias=bias), f"T{T}H{H}I{I}E{E}k{k}")
