@@ -114,6 +114,27 @@ def test_backward_dx_batch_invariant():
         assert np.array_equal(alone["dw"], full["dw"][lo:hi])
 
 
+@pytest.mark.parametrize("act", [inputs.ACT_SWIGLU, inputs.ACT_RELU2])
+def test_transposed_weights_are_the_fp8_bytes(act):
+    """moe_transpose_weights writes each weight's E4M3 byte, the byte the
+    oracle's dequantisation gives (every sub-block exponent of the lossless
+    window, so E4M3 subnormals and both zero signs occur), transposed:
+    wt_gu[e][h] = [gate(e, :, h) | up(e, :, h)], wt_d[e][i] = down(e, :, i)."""
+    E, H, I = 3, 256, 256
+    gated = act == inputs.ACT_SWIGLU
+    ex = inputs.gen_experts(47, E, H, I, b_range=(-8, 6), gated=gated)
+    inp = inputs.Inputs(dims=inputs.Dims(8, H, I, E, 2, act), mode=0, x=inputs.gen_x(47, 8, H),
+                        w_router=inputs.gen_router(47, H, E), bias=None, token_ids=None, experts=ex)
+    wt_gu, wt_d = gpu_layer(inp).transposed_weights()
+    torch.cuda.synchronize()
+    wt_gu, wt_d = wt_gu.cpu().numpy(), wt_d.cpu().numpy()
+    for e in range(E):
+        cols = ([oracle.dequant_matrix(ex.gate.fp4[e], ex.gate.e8m0[e]).T] if gated else []) + \
+               [oracle.dequant_matrix(ex.up.fp4[e], ex.up.e8m0[e]).T]
+        assert np.array_equal(wt_gu[e], np.concatenate(cols, axis=1)), e
+        assert np.array_equal(wt_d[e], oracle.dequant_matrix(ex.down.fp4[e], ex.down.e8m0[e]).T), e
+
+
 def test_backward_zero_tokens():
     inp = make(0, 256, 128, 4, 2)
     layer = gpu_layer(inp)
