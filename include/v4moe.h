@@ -122,10 +122,9 @@ size_t moe_workspace_bytes(const v4moe_dims* d);
  *   x         bf16 [T][H]
  *   w_router  fp32 [H][E]
  *   bias      fp32 [E] or NULL: added to the logits (selection and weights)
- *   mode      V4MOE_ROUTE_LEARNED: logits z[t][e] = fp32 sum, in increasing
- *             order from +0, of one fp32 fused multiply-add chain per 512-h
- *             chunk (h ascending from +0; the last chunk shorter when 512
- *             does not divide H), + bias as one fp32 add; the
+ *   mode      V4MOE_ROUTE_LEARNED: logits z[t][e] = one fp32 fused
+ *             multiply-add chain over h = 0 .. H-1 ascending, starting from
+ *             +0 (x exact as fp32), + bias as one fp32 add afterwards; the
  *             topk largest z are taken, ties to the lower expert id, slot j
  *             = j-th pick; a = sqrt(softplus(z)); topk_w = a / sum(a) over
  *             the picks.
