@@ -495,27 +495,42 @@ struct WgTile {
     static_assert(128 * 132 * 4 <= LDS, "the fp32 tile is staged in the A buffer");
     static_assert((128 * (KMAX / 8)) % 256 == 0 && KMAX % 32 == 0, "tile shape");
 };
-// piece q of a 128-row x klen tile: row (tid + 256 q) / (klen/8), 16-byte
-// segment (tid + 256 q) % (klen/8); pieces past the tile repeat its last one
-// (the same bytes to the same place)
-template <int Q>
+// Piece q of a 128-row tile of KMAX columns (KMAX/8 16-byte segments per
+// row): i = tid + 256 q, row i / (KMAX/8), segment i % (KMAX/8), the quotient
+// by a 24-bit multiply and shift (exact for i < 2^20 / (KMAX/8)).  Segments
+// at or past klen are clamped to the last one inside it: the copy then moves
+// the same 16 bytes to the same place twice.  Indices are recomputed at each
+// use (cheap full-rate integer ops) rather than held in registers.
+template <int KMAX>
+__device__ __forceinline__ void wg_piece(int tid, int q, int klen, uint32_t& row, uint32_t& seg)
+{
+    constexpr uint32_t SPR = KMAX / 8, MUL = ((1u << 20) + SPR - 1) / SPR;
+    static_assert((uint64_t)128 * SPR * (MUL * SPR - (1u << 20)) < (1u << 20), "exact quotient for i < 128 SPR");
+    const uint32_t i = (uint32_t)tid + 256u * q;
+    row = __umul24(i, MUL) >> 20;
+    seg = min(i - row * SPR, (uint32_t)klen / 8u - 1u);
+}
+template <int KMAX, int Q>
 __device__ __forceinline__ void wg_fetch(v4u (&r)[Q], const uint16_t* base, int ld, int row0, int c0, int klen, int tid)
 {
-    const int sp = klen / 8;
+    asm volatile("" : "+v"(tid));                          // piece indices recomputed here, not held
+    const uint16_t* b = base + (size_t)row0 * ld + c0;     // uniform
 #pragma unroll
     for (int q = 0; q < Q; q++) {
-        const int i = min(tid + 256 * q, 128 * sp - 1);
-        r[q] = *reinterpret_cast<const v4u*>(base + (size_t)(row0 + i / sp) * ld + c0 + (i % sp) * 8);
+        uint32_t row, seg;
+        wg_piece<KMAX>(tid, q, klen, row, seg);
+        r[q] = *reinterpret_cast<const v4u*>(b + (row * (uint32_t)ld + seg * 8u));
     }
 }
-template <int PITCH, int Q>
+template <int KMAX, int PITCH, int Q>
 __device__ __forceinline__ void wg_put(uint16_t* dst, const v4u (&r)[Q], int klen, int tid)
 {
-    const int sp = klen / 8;
+    asm volatile("" : "+v"(tid));
 #pragma unroll
     for (int q = 0; q < Q; q++) {
-        const int i = min(tid + 256 * q, 128 * sp - 1);
-        *reinterpret_cast<v4u*>(&dst[(i / sp) * PITCH + (i % sp) * 8]) = r[q];
+        uint32_t row, seg;
+        wg_piece<KMAX>(tid, q, klen, row, seg);
+        *reinterpret_cast<v4u*>(&dst[row * PITCH + seg * 8u]) = r[q];
     }
 }
 template <int KMAX>
@@ -544,11 +559,14 @@ __global__ __launch_bounds__(256) void k_wgrad(BgemmArgs a)
 #pragma unroll
             for (int j = 0; j < 2; j++)
                 if (32 * st < klen) bfr[st][j] = *reinterpret_cast<const bf8*>(brow[j] + c0 + 32 * st);
+        // waited for here: a B reload is conditional, and a wait left to the
+        // compiler at the first product would also wait for the A prefetch
+        __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0)
     };
     v4u ra[TL::QA];
     if (Kp > 0) {
         load_b(cbeg, min(KMAX, Kp));
-        wg_fetch(ra, a.A, a.lda, 0, cbeg, min(KMAX, Kp), tid);
+        wg_fetch<KMAX>(ra, a.A, a.lda, 0, cbeg, min(KMAX, Kp), tid);
     }
     v4f acc[8][2];
     for (int it = 0; it < items; it++) {
@@ -561,13 +579,13 @@ __global__ __launch_bounds__(256) void k_wgrad(BgemmArgs a)
                 for (int j = 0; j < 2; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
         __syncthreads();                                      // As free: the last item's reads and stores are done
         if (klen > 0) {
-            wg_put<PITCH>(As, ra, klen, tid);
+            wg_put<KMAX, PITCH>(As, ra, klen, tid);
             if (nkc > 1 && kc > 0) load_b(cbeg + kc * KMAX, klen);
         }
         __syncthreads();
         if (it + 1 < items && Kp > 0) {
             const int mt1 = (it + 1) / nkc, kc1 = (it + 1) % nkc;
-            wg_fetch(ra, a.A, a.lda, mt1 * 128, cbeg + kc1 * KMAX, min(KMAX, Kp - kc1 * KMAX), tid);
+            wg_fetch<KMAX>(ra, a.A, a.lda, mt1 * 128, cbeg + kc1 * KMAX, min(KMAX, Kp - kc1 * KMAX), tid);
         }
 #pragma unroll
         for (int st = 0; st < NS; st++) {
@@ -591,10 +609,19 @@ __global__ __launch_bounds__(256) void k_wgrad(BgemmArgs a)
                 for (int q = 0; q < 4; q++)
                     cs[(i * 16 + 4 * (lane >> 4) + q) * 132 + 32 * w + j * 16 + (lane & 15)] = acc[i][j][q];
         __syncthreads();
-        for (int idx = tid; idx < 128 * 32; idx += 256) {
-            const int r = idx >> 5, c4 = (idx & 31) * 4;
-            *reinterpret_cast<float4*>(a.dW + ((size_t)e * a.M + mt * 128 + r) * a.N + n0 + c4) =
-                *reinterpret_cast<const float4*>(&cs[r * 132 + c4]);
+#pragma unroll 1
+        for (int q0 = 0; q0 < 16; q0 += 4) {
+            float4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int r = (tid >> 5) + 8 * (q0 + q);
+                v[q] = *reinterpret_cast<const float4*>(&cs[r * 132 + (tid & 31) * 4]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int r = (tid >> 5) + 8 * (q0 + q);
+                *reinterpret_cast<float4*>(a.dW + ((size_t)e * a.M + mt * 128 + r) * a.N + n0 + (tid & 31) * 4) = v[q];
+            }
         }
         // a chunked expert's next tile starts again at chunk 0: its B operand
         if (nkc > 1 && it + 1 < items) load_b(cbeg, min(KMAX, Kp));
