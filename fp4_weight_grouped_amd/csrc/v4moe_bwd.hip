@@ -497,7 +497,8 @@ struct WgTile {
 };
 // Piece q of a 128-row tile of KMAX columns (KMAX/8 16-byte segments per
 // row): i = tid + 256 q, row i / (KMAX/8), segment i % (KMAX/8), the quotient
-// by a 24-bit multiply and shift (exact for i < 2^20 / (KMAX/8)).  Segments
+// by a 24-bit multiply and shift (exact for every i of the tile, which the
+// static assertion checks; row * ld fits 32 bits as ld < 2^25).  Segments
 // at or past klen are clamped to the last one inside it: the copy then moves
 // the same 16 bytes to the same place twice.  Indices are recomputed at each
 // use (cheap full-rate integer ops) rather than held in registers.
