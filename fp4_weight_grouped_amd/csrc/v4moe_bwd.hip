@@ -342,7 +342,11 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
         for (int q = 0; q < TL::QA; q++) {
             const int r = tid / SEGS + RSTEP * q;
             const int ar = MODE == WGRAD ? m0 + r : row0 + min(r, rows - 1);
-            ra[q] = in ? *reinterpret_cast<const uint4*>(a.A + (size_t)ar * a.lda + k0 + sg * 8) : make_uint4(0, 0, 0, 0);
+            // DGRAD: rows past the m-tile's end are not loaded (zeros; their
+            // products are never stored)
+            ra[q] = in && (MODE == WGRAD || r < rows)
+                        ? *reinterpret_cast<const uint4*>(a.A + (size_t)ar * a.lda + k0 + sg * 8)
+                        : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < TL::QB; q++) {
