@@ -329,8 +329,8 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
     // Each thread moves QA A and QB B 16-byte pieces per stage: piece q is
     // row (tid / SEGS) + (256 / SEGS) q, columns 8 * (tid % SEGS)...; the next
     // stage's pieces are loaded into registers while this one computes.  Rows
-    // past the end of a DGRAD m-tile repeat its last row (never stored);
-    // columns past the stage's end read as zero.
+    // past the end of a DGRAD m-tile and columns past the stage's end are not
+    // loaded but read as zero (those rows' products are never stored).
     constexpr int RSTEP = 256 / SEGS;
     uint4 ra[TL::QA], rb[TL::QB];
     uint2 rq[TL::QB];   // DGRAD: the weight pieces as E4M3 bytes, converted when staged
@@ -342,8 +342,6 @@ __global__ __launch_bounds__(256) void k_bgemm(BgemmArgs a, int NB)
         for (int q = 0; q < TL::QA; q++) {
             const int r = tid / SEGS + RSTEP * q;
             const int ar = MODE == WGRAD ? m0 + r : row0 + min(r, rows - 1);
-            // DGRAD: rows past the m-tile's end are not loaded (zeros; their
-            // products are never stored)
             ra[q] = in && (MODE == WGRAD || r < rows)
                         ? *reinterpret_cast<const uint4*>(a.A + (size_t)ar * a.lda + k0 + sg * 8)
                         : make_uint4(0, 0, 0, 0);
