@@ -493,6 +493,17 @@ def test_routing_single_chain_order(T, H, E):
     (32, 256, 8, 3),        # few experts
     (50, 256, 6, 2),        # E % 4 != 0: one thread per logit
     (50, 768, 6, 2),
+    # every variant again at the layer's hidden size, H = 4096
+    (200, 4096, 100, 4),    # one chain per lane, partial last group of experts
+    (512, 4096, 256, 8),    # one token x one expert per lane
+    (64, 4096, 1024, 16),   # the same over 1024 experts
+    (2000, 4096, 256, 8),   # one token x four experts per lane
+    (4000, 4096, 40, 4),    # one token x two experts per lane
+    (8192, 4096, 256, 8),   # two tokens x eight experts per lane
+    (6100, 4096, 256, 8),   # two tokens x four experts per lane
+    (4096, 4096, 256, 8),   # the same at its smallest batch
+    (32, 4096, 8, 3),       # few experts
+    (50, 4096, 6, 2),       # E % 4 != 0: one thread per logit
 ])
 def test_routing_exact_ties(T, H, E, k):
     """Logits that collide exactly (x in {-1, 0, 1}, W_r columns drawn from
